@@ -1,0 +1,154 @@
+"""CPU oracle for the block-scaled FP4 mixture-of-experts layer (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY.  The oracle is plain single-threaded C++
+(``moe_oracle.cpp``) that shares no code with the HIP library.  Only the
+test suite, the smoke check and the benchmark's CPU-baseline leg may import
+this package; the library's product path never does.
+
+Numpy arrays in the logical layout that ``block_scaled_fp4_gather_amd.synth``
+produces go in; fp32 token sums and their bf16 bit patterns come out.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.cpp")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+FMT = {"mxfp4": 1, "nvfp4": 2}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with g++ (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["g++", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c++17",
+                               "-shared", "-fPIC", "-o", tmp, _SRC])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        L = ctypes.CDLL(_LIB)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        i = ctypes.c_int
+        L.oracle_e2m1.argtypes = [ctypes.c_uint32]
+        L.oracle_e2m1.restype = ctypes.c_float
+        L.oracle_ue8m0.argtypes = [ctypes.c_uint32]
+        L.oracle_ue8m0.restype = ctypes.c_float
+        L.oracle_e4m3.argtypes = [ctypes.c_uint32]
+        L.oracle_e4m3.restype = ctypes.c_float
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        L.oracle_dequant.argtypes = [i, u8p, u8p, ctypes.c_float, i, i, f32p]
+        L.oracle_dequant.restype = i
+        common = [i, i, i, i, i, i, u8p, u8p, u8p, u8p, f32p, f32p, u16p, i64p, f32p]
+        L.oracle_forward_f32.argtypes = common + [f32p, u16p]
+        L.oracle_forward_f32.restype = i
+        L.oracle_forward_f64.argtypes = common + [f64p]
+        L.oracle_forward_f64.restype = i
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray | None, ctype):
+    if a is None:
+        return ctypes.cast(None, ctypes.POINTER(ctype))
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def e2m1(nibble: int) -> float:
+    return lib().oracle_e2m1(nibble)
+
+
+def ue8m0(b: int) -> float:
+    return lib().oracle_ue8m0(b)
+
+
+def e4m3(b: int) -> float:
+    return lib().oracle_e4m3(b)
+
+
+def f32_to_bf16(f: float) -> int:
+    return lib().oracle_f32_to_bf16(f)
+
+
+def bf16_to_f32(h: int) -> float:
+    return lib().oracle_bf16_to_f32(h)
+
+
+def dequant(fmt: str, codes: np.ndarray, scales: np.ndarray, global_scale: float = 1.0) -> np.ndarray:
+    """Dequantise one [rows][cols/2] code matrix with its [rows][cols/G] scales."""
+    rows, half = codes.shape
+    cols = 2 * half
+    out = np.empty((rows, cols), dtype=np.float32)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rc = lib().oracle_dequant(FMT[fmt], _p(codes, ctypes.c_uint8), _p(scales, ctypes.c_uint8),
+                              float(global_scale), rows, cols, _p(out, ctypes.c_float))
+    if rc:
+        raise ValueError("oracle_dequant rejected its arguments")
+    return out
+
+
+def _args(fmt, d):
+    E, twoI, Hh = d["w13_codes"].shape
+    H, I = 2 * Hh, twoI // 2
+    M, k = d["ids"].shape
+    arr = {key: np.ascontiguousarray(d[key]) for key in
+           ("w13_codes", "w13_scales", "w2_codes", "w2_scales", "x", "w")}
+    ids = np.ascontiguousarray(d["ids"], dtype=np.int64)
+    g13 = None if d.get("g13") is None else np.ascontiguousarray(d["g13"], dtype=np.float32)
+    g2 = None if d.get("g2") is None else np.ascontiguousarray(d["g2"], dtype=np.float32)
+    keep = (arr, ids, g13, g2)
+    args = [FMT[fmt], E, H, I, M, k,
+            _p(arr["w13_codes"], ctypes.c_uint8), _p(arr["w13_scales"], ctypes.c_uint8),
+            _p(arr["w2_codes"], ctypes.c_uint8), _p(arr["w2_scales"], ctypes.c_uint8),
+            _p(g13, ctypes.c_float), _p(g2, ctypes.c_float),
+            _p(arr["x"], ctypes.c_uint16), _p(ids, ctypes.c_int64), _p(arr["w"], ctypes.c_float)]
+    return args, keep, M, H
+
+
+def forward_f32(fmt: str, d: dict) -> tuple[np.ndarray, np.ndarray]:
+    """Returns (fp32 token sums [M][H], bf16 bit patterns [M][H])."""
+    args, keep, M, H = _args(fmt, d)
+    acc = np.empty((M, H), dtype=np.float32)
+    out = np.empty((M, H), dtype=np.uint16)
+    rc = lib().oracle_forward_f32(*args, _p(acc, ctypes.c_float), _p(out, ctypes.c_uint16))
+    if rc:
+        raise ValueError("oracle_forward_f32 rejected its arguments")
+    del keep
+    return acc, out
+
+
+def forward_f64(fmt: str, d: dict) -> np.ndarray:
+    args, keep, M, H = _args(fmt, d)
+    acc = np.empty((M, H), dtype=np.float64)
+    rc = lib().oracle_forward_f64(*args, _p(acc, ctypes.c_double))
+    if rc:
+        raise ValueError("oracle_forward_f64 rejected its arguments")
+    del keep
+    return acc
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 (a bit shift, no rounding)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
