@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP4 MoE layer on one MI355X.
+
+Metric: microseconds per MoE layer at M=1 with cold caches, plus the fraction
+of HBM peak achieved on the unique routed FP4 weight + scale bytes.
+
+A step is one layer call (both kernels) on one batch of synthetic inputs
+already resident in HBM.  Steps rotate through groups of disjoint experts
+(each group has the workload's top-k size and weights from the workload's own
+softmax routing), so that between two uses of an expert every other group
+has streamed through: with the 512-expert NVFP4 workload that is ~700 MB of
+other weights, more than L2 plus the 256 MB Infinity Cache, so every step
+reads its experts from HBM.  The timed region is K back-to-back steps between
+two HIP events on the launch stream (one event pair per region, since a pair
+around a single launch adds ~4 us of its own).  FC1-only and FC2-only runs
+over the same rotation give each kernel's average duration for the roofline.
+Correctness against the CPU oracle gates the timing.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="nvfp4_decode_e512")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-check", action="store_true", help="skip the oracle check (profiling runs)")
+    ap.add_argument("--slab", type=int, default=None, help="FC1 K-slab chunks (4, 8, 16)")
+    ap.add_argument("--extra", action="store_true", help="also time warm-cache calls and a copy probe")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def routed_bytes(wl, ids):
+    """Unique valid experts and their algorithmic weight bytes (codes + scales)."""
+    import numpy as np
+    flat = ids.reshape(-1).astype(np.int64)
+    uniq = np.unique(flat[(flat >= 0) & (flat < wl.E)])
+    G = wl.G
+    w13 = 2 * wl.I * (wl.H // 2 + wl.H // G)
+    w2 = wl.H * (wl.I // 2 + wl.I // G)
+    glob = 4 if wl.fmt == "nvfp4" else 0
+    U = len(uniq)
+    return U, U * (w13 + glob), U * (w2 + glob)
+
+
+def cold_groups(wl, d, dev):
+    """Route tables for the rotation: the workload's own table first, then
+    tables whose valid ids are disjoint groups of experts not used by it."""
+    import numpy as np
+    import torch
+
+    ids0, w0 = d["ids"], d["w"]
+    flat = ids0.reshape(-1)
+    valid = flat[(flat >= 0) & (flat < wl.E)]
+    per = len(np.unique(valid))
+    rest = np.setdiff1d(np.arange(wl.E), valid)
+    rng = np.random.default_rng(wl.seed & 0xFFFF)
+    rest = rng.permutation(rest)
+    tables = [(ids0, w0)]
+    if per:
+        first_slot = {}
+        for pos, e in enumerate(flat):
+            if 0 <= e < wl.E and e not in first_slot:
+                first_slot[e] = pos
+        for g in range(len(rest) // per):
+            repl = dict(zip(first_slot.keys(), rest[g * per:(g + 1) * per]))
+            ids = np.array([repl.get(int(e), e) if 0 <= e < wl.E else e for e in flat],
+                           dtype=ids0.dtype).reshape(ids0.shape)
+            tables.append((ids, w0))
+    return [(torch.from_numpy(np.ascontiguousarray(i)).to(dev), torch.from_numpy(np.ascontiguousarray(w)).to(dev))
+            for i, w in tables]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "the layer would shard by experts or by I with one exchange of the [M, H] output.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_scaled_fp4_gather_amd import moe, synth
+
+    wl = synth.WORKLOADS[args.workload]
+    log(f"[bench] workload {wl.name}: {wl.description}")
+    d = synth.generate(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    desc = moe.Desc(wl.fmt, wl.E, wl.H, wl.I, wl.k, max(wl.M, 1))
+
+    def dt(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    layer = moe.Fp4MoE(desc, dt(d["w13_codes"]), dt(d["w13_scales"]), dt(d["w2_codes"]),
+                       dt(d["w2_scales"]), dt(d["g13"]) if d["g13"] is not None else None,
+                       dt(d["g2"]) if d["g2"] is not None else None, device=dev)
+    x = dt(d["x"]).view(torch.bfloat16)
+    ids = dt(d["ids"])
+    w = dt(d["w"])
+    out = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log("[bench] prepared")
+
+    check = None
+    if not args.no_check:
+        import oracle
+        acc, _ = oracle.forward_f32(wl.fmt, d)
+        layer(x, ids, w, out=out, slab_chunks=args.slab)
+        torch.cuda.synchronize()
+        g = oracle.bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64).ravel()
+        r = acc.astype(np.float64).ravel()
+        rms = float(np.sqrt(np.mean(r * r)))
+        cos = float(g @ r / (np.linalg.norm(g) * np.linalg.norm(r)))
+        err = np.abs(g - r)
+        _, ex = np.frexp(np.abs(r))
+        half_ulp = np.where(r == 0, 0.0, np.ldexp(1.0, ex - 9))
+        mx = float(err.max() / rms)
+        beyond = float(np.max(err - half_ulp) / rms)
+        check = {"cos": round(cos, 8), "maxabs_over_rms": round(mx, 6),
+                 "beyond_bf16_rounding_over_rms": round(beyond, 6),
+                 "pass": bool(cos >= 0.99995 and beyond <= 2e-2)}
+        log(f"[bench] oracle check {check}")
+        if not check["pass"]:
+            print(json.dumps({"error": "correctness check failed", "check": check}))
+            sys.exit(1)
+
+    K, W = args.steps, args.warmup
+    groups = cold_groups(wl, d, dev)
+    log(f"[bench] {len(groups)} disjoint expert groups in rotation")
+
+    def call(g, phases=None):
+        layer(x, g[0], g[1], out=out, slab_chunks=args.slab, phases=phases)
+
+    def region(phases=None, rotate=True):
+        """One graph holds a pass over the rotation; it is replayed until K
+        steps have run.  Returns (us per step from events, wall s per step)."""
+        n = len(groups)
+        reps = max(1, -(-K // n))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                call(groups[i] if rotate else groups[0], phases)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        steps = reps * n
+        return a.elapsed_time(b) * 1e3 / steps, (time.perf_counter() - t0) / steps, steps
+
+    for i in range(W):
+        call(groups[i % len(groups)])
+    torch.cuda.synchronize()
+    log("[bench] warm-up done")
+    value, wall_step, K = region()
+    log(f"[bench] layer, cold rotation: {value:.3f} us/step")
+    fc1_us, _, _ = region(phases=1)
+    fc2_us, _, _ = region(phases=2)
+    log(f"[bench] fc1 only {fc1_us:.3f} us/launch, fc2 only {fc2_us:.3f} us/launch")
+
+    U, b13, b2 = routed_bytes(wl, groups[0][0].cpu().numpy())
+    layer_bytes = b13 + b2
+    if wl.fmt == "nvfp4" or wl.fmt == "mxfp4":
+        dom, dom_bytes, dom_us = ("fc1_kernel", b13, fc1_us) if b13 >= b2 else ("fc2_kernel", b2, fc2_us)
+    dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
+    extra = {}
+    if args.extra:
+        warm_us, _, _ = region(rotate=False)
+        extra["warm_us_per_step"] = round(warm_us, 3)
+        scrub = torch.zeros(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        ev = []
+        for i in range(50):
+            scrub.add_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            call(groups[0])
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        extra["scrub_single_event_pair_us_median"] = round(statistics.median(a.elapsed_time(b) * 1e3 for a, b in ev), 3)
+        dst = torch.empty_like(scrub)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        dst.copy_(scrub)
+        c0.record()
+        for _ in range(10):
+            dst.copy_(scrub)
+        c1.record()
+        torch.cuda.synchronize()
+        extra["copy_probe_GBps"] = round(2 * scrub.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1)
+        del scrub, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and n < 1000:
+            s0 = time.perf_counter()
+            oracle.forward_f32(wl.fmt, d)
+            t_cpu += time.perf_counter() - s0
+            n += 1
+        cpu = {"value": round(t_cpu / n * 1e6, 1), "unit": "us", "cores": 1, "kind": "oracle",
+               "sample": f"{n} full layer calls of {wl.name} (M={wl.M}), single-threaded C++ oracle"}
+        log(f"[bench] cpu oracle {cpu['value']} us/layer over {n} calls")
+
+    line = {
+        "metric": "us per MoE layer @M=1 cold-L2 + % HBM peak on routed FP4 weight bytes",
+        "value": round(value, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(wall_step * 1e3, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e2m1 weights x bf16 activations, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "format": wl.fmt, "E": wl.E, "H": wl.H, "I": wl.I,
+                   "M": wl.M, "top_k": wl.k, "unique_experts": U},
+        "hbm_frac_layer": round(layer_bytes / (value * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+        "routed_bytes": {"fc1": b13, "fc2": b2},
+        "kernel_us": {"fc1": round(fc1_us, 3), "fc2": round(fc2_us, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": dom},
+        "cpu_baseline": cpu,
+        "check": check,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

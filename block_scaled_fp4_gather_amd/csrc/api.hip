@@ -1,0 +1,173 @@
+// C-ABI of libmoe_fp4.so (declared in include/moe_fp4.h): argument checks,
+// sizing, and the launches.  Every check runs before any HIP call, so a
+// rejected call touches neither the device nor the stream.
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe_fp4.h"
+#include "decode_path.h"
+#include "layout.h"
+
+using moe::Layout;
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_fp4_status desc_layout(const moe_fp4_desc* d, Layout* L) {
+  if (!d) return MOE_FP4_EINVAL;
+  if (d->format != MOE_FP4_MXFP4 && d->format != MOE_FP4_NVFP4) return MOE_FP4_EINVAL;
+  if (d->num_experts <= 0 || d->hidden <= 0 || d->inter <= 0 || d->top_k <= 0 || d->max_tokens < 0)
+    return MOE_FP4_EINVAL;
+  const int G = d->format == MOE_FP4_MXFP4 ? 32 : 16;
+  if (d->hidden % G || d->inter % G) return MOE_FP4_EINVAL;  // not whole scale blocks
+  if (d->hidden % 32 || d->inter % 32) return MOE_FP4_EUNSUPPORTED;
+  if ((int64_t)d->hidden * d->inter > (int64_t)1 << 30) return MOE_FP4_EUNSUPPORTED;
+  if (!moe::make_layout(d->format, d->num_experts, d->hidden, d->inter, L)) return MOE_FP4_EINVAL;
+  return MOE_FP4_OK;
+}
+
+// Route slots the workspace is sized for; it depends only on the descriptor.
+int decode_slots(const moe_fp4_desc* d) {
+  const int cap = moe::decode_max_tokens(d->top_k);
+  const int m = d->max_tokens < 1 ? 1 : (d->max_tokens > cap ? cap : d->max_tokens);
+  return m * d->top_k;
+}
+
+moe_fp4_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_FP4_OK : MOE_FP4_EHIP; }
+
+template <typename IdT>
+moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, const uint16_t* x,
+                            int32_t M, const IdT* ids, const float* w, uint16_t* out,
+                            void* workspace, size_t ws_bytes, int32_t cs, int32_t phases,
+                            void* stream) {
+  Layout L;
+  moe_fp4_status st = desc_layout(desc, &L);
+  if (st != MOE_FP4_OK) return st;
+  if (M < 0 || M > desc->max_tokens) return MOE_FP4_EINVAL;
+  if (M == 0) return MOE_FP4_OK;
+  if (!prepared || !x || !ids || !w || !out || !workspace) return MOE_FP4_EINVAL;
+  if (!aligned(prepared, 256) || !aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
+      !aligned(ids, sizeof(IdT)) || !aligned(w, 4))
+    return MOE_FP4_EINVAL;
+  if (cs != 0 && cs != 4 && cs != 8 && cs != 16) return MOE_FP4_EINVAL;
+  if (phases < 1 || phases > 3) return MOE_FP4_EINVAL;
+  const int k = desc->top_k;
+  if (k > moe::kDecodeMaxSlots || M > moe::decode_max_tokens(k)) return MOE_FP4_EUNSUPPORTED;
+  const moe::DecodeWs W = moe::decode_ws(L, decode_slots(desc));
+  if ((int64_t)ws_bytes < W.total) return MOE_FP4_EWORKSPACE;
+  if (cs == 0) cs = moe::choose_slab(L);
+  return from_hip(moe::launch_decode<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
+                                          (uint8_t*)workspace, W, cs, phases, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_fp4_status_string(moe_fp4_status s) {
+  switch (s) {
+    case MOE_FP4_OK: return "ok";
+    case MOE_FP4_EINVAL: return "invalid argument";
+    case MOE_FP4_EUNSUPPORTED: return "unsupported shape or size";
+    case MOE_FP4_EWORKSPACE: return "buffer too small";
+    case MOE_FP4_EHIP: return "HIP launch or runtime error";
+  }
+  return "unknown status";
+}
+
+moe_fp4_status moe_fp4_prepared_bytes(const moe_fp4_desc* desc, size_t* bytes) {
+  Layout L;
+  moe_fp4_status st = desc_layout(desc, &L);
+  if (st != MOE_FP4_OK) return st;
+  if (!bytes) return MOE_FP4_EINVAL;
+  *bytes = (size_t)L.total;
+  return MOE_FP4_OK;
+}
+
+moe_fp4_status moe_fp4_prepare(const moe_fp4_desc* desc, const uint8_t* w13_codes,
+                               const uint8_t* w13_scales, const uint8_t* w2_codes,
+                               const uint8_t* w2_scales, const float* g13, const float* g2,
+                               void* prepared, size_t prepared_bytes, void* stream) {
+  Layout L;
+  moe_fp4_status st = desc_layout(desc, &L);
+  if (st != MOE_FP4_OK) return st;
+  if (!w13_codes || !w13_scales || !w2_codes || !w2_scales || !prepared) return MOE_FP4_EINVAL;
+  const bool nv = desc->format == MOE_FP4_NVFP4;
+  if (nv != (g13 != nullptr) || nv != (g2 != nullptr)) return MOE_FP4_EINVAL;
+  if (!aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(prepared, 256)) return MOE_FP4_EINVAL;
+  if ((nv && (!aligned(g13, 4) || !aligned(g2, 4)))) return MOE_FP4_EINVAL;
+  if ((int64_t)prepared_bytes < L.total) return MOE_FP4_EWORKSPACE;
+  return from_hip(moe::launch_repack(L, 0, (uint8_t*)w13_codes, (uint8_t*)w13_scales,
+                                     (uint8_t*)w2_codes, (uint8_t*)w2_scales, (float*)g13,
+                                     (float*)g2, (uint8_t*)prepared, (hipStream_t)stream));
+}
+
+moe_fp4_status moe_fp4_unprepare(const moe_fp4_desc* desc, const void* prepared,
+                                 uint8_t* w13_codes, uint8_t* w13_scales, uint8_t* w2_codes,
+                                 uint8_t* w2_scales, float* g13, float* g2, void* stream) {
+  Layout L;
+  moe_fp4_status st = desc_layout(desc, &L);
+  if (st != MOE_FP4_OK) return st;
+  if (!w13_codes || !w13_scales || !w2_codes || !w2_scales || !prepared) return MOE_FP4_EINVAL;
+  const bool nv = desc->format == MOE_FP4_NVFP4;
+  if (nv != (g13 != nullptr) || nv != (g2 != nullptr)) return MOE_FP4_EINVAL;
+  if (!aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(prepared, 256)) return MOE_FP4_EINVAL;
+  return from_hip(moe::launch_repack(L, 1, w13_codes, w13_scales, w2_codes, w2_scales, g13, g2,
+                                     (uint8_t*)prepared, (hipStream_t)stream));
+}
+
+moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size_t* bytes) {
+  Layout L;
+  moe_fp4_status st = desc_layout(desc, &L);
+  if (st != MOE_FP4_OK) return st;
+  if (!bytes || M < 0 || M > desc->max_tokens) return MOE_FP4_EINVAL;
+  *bytes = (size_t)moe::decode_ws(L, decode_slots(desc)).total;
+  return MOE_FP4_OK;
+}
+
+moe_fp4_status moe_fp4_forward(const moe_fp4_desc* desc, const void* prepared, const uint16_t* x,
+                               int32_t M, const int32_t* topk_ids, const float* topk_w,
+                               uint16_t* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return forward_impl<int32_t>(desc, prepared, x, M, topk_ids, topk_w, out, workspace,
+                               workspace_bytes, 0, 3, stream);
+}
+
+moe_fp4_status moe_fp4_forward_i64(const moe_fp4_desc* desc, const void* prepared,
+                                   const uint16_t* x, int32_t M, const int64_t* topk_ids,
+                                   const float* topk_w, uint16_t* out, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return forward_impl<int64_t>(desc, prepared, x, M, topk_ids, topk_w, out, workspace,
+                               workspace_bytes, 0, 3, stream);
+}
+
+moe_fp4_status moe_fp4_forward_tuned(const moe_fp4_desc* desc, const void* prepared,
+                                     const uint16_t* x, int32_t M, const int32_t* topk_ids,
+                                     const float* topk_w, uint16_t* out, void* workspace,
+                                     size_t workspace_bytes, int32_t fc1_slab_chunks,
+                                     void* stream) {
+  return forward_impl<int32_t>(desc, prepared, x, M, topk_ids, topk_w, out, workspace,
+                               workspace_bytes, fc1_slab_chunks, 3, stream);
+}
+
+moe_fp4_status moe_fp4_forward_phase(const moe_fp4_desc* desc, const void* prepared,
+                                     const uint16_t* x, int32_t M, const int32_t* topk_ids,
+                                     const float* topk_w, uint16_t* out, void* workspace,
+                                     size_t workspace_bytes, int32_t phases, void* stream) {
+  return forward_impl<int32_t>(desc, prepared, x, M, topk_ids, topk_w, out, workspace,
+                               workspace_bytes, 0, phases, stream);
+}
+
+moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prepared,
+                                      int32_t expert, int32_t which, float* out, void* stream) {
+  Layout L;
+  moe_fp4_status st = desc_layout(desc, &L);
+  if (st != MOE_FP4_OK) return st;
+  if (!prepared || !out || expert < 0 || expert >= L.E || (which != 0 && which != 1))
+    return MOE_FP4_EINVAL;
+  if (!aligned(prepared, 256) || !aligned(out, 4)) return MOE_FP4_EINVAL;
+  return from_hip(moe::launch_export(L, expert, which, (const uint8_t*)prepared, out,
+                                     (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+/*
+ * moe_fp4 — block-scaled FP4 mixture-of-experts layer for AMD MI355X (gfx950).
+ *
+ * The layer (b12x PR #22, "rp-native tiny-decode kernel for w4a8_mx (M=1)",
+ * What section, FC1 and FC2 bullets): for every token t and every route j of
+ * its top-k, with expert e = ids[t][j],
+ *     gate_n = sum_h x[t][h] * W13[e][n][h],        n in [0, I)
+ *     up_n   = sum_h x[t][h] * W13[e][I + n][h]
+ *     a_n    = gate_n / (1 + exp(-gate_n)) * up_n     (SiLU(gate) * up)
+ *     y_h    = sum_n a_n * W2[e][h][n]
+ *     out[t][h] = bf16( sum_j w[t][j] * y_h )         (fp32 sum, one rounding)
+ * Weights are E2M1 nibbles with block scales:
+ *   MXFP4: one UE8M0 scale byte (2^(b-127)) per 32 consecutive K elements;
+ *   NVFP4: one E4M3 scale byte per 16 consecutive K elements, times an fp32
+ *          global multiplier per expert per matrix (g13[e] for W13, g2[e]
+ *          for W2).
+ * A route whose id is negative or >= E reads no weights and contributes
+ * nothing (b12x PR #311, commit message on the FC2-only endpoint, and its
+ * review of tiny_decode.py); a token with no valid route yields +0.
+ *
+ * Logical weight layout (the input of moe_fp4_prepare), row-major, G = 32
+ * (MXFP4) or 16 (NVFP4):
+ *   w13_codes  u8[E][2I][H/2]  rows [0, I) gate, [I, 2I) up; element 2b of a
+ *                              row in the low nibble of byte b, 2b+1 in the high
+ *   w13_scales u8[E][2I][H/G]
+ *   w2_codes   u8[E][H][I/2]
+ *   w2_scales  u8[E][H][I/G]
+ *   g13, g2    f32[E]          NVFP4 only (NULL for MXFP4)
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned device memory; the library allocates
+ *     nothing, keeps no global state and never synchronises.  Work is queued
+ *     on `stream` (a hipStream_t; NULL is the default stream).
+ *   - Inputs are never written.  Arguments are checked before any launch; a
+ *     rejected call launches nothing.  A failed launch returns MOE_FP4_EHIP.
+ *   - Data conditions are not errors: invalid ids contribute zero; NaN or Inf
+ *     in scales, globals or activations of valid routes propagate.
+ */
+#ifndef MOE_FP4_H
+#define MOE_FP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_FP4_OK = 0,
+  MOE_FP4_EINVAL = 1,      /* null/misaligned pointer, bad size or count */
+  MOE_FP4_EUNSUPPORTED = 2,/* valid request outside what this build handles */
+  MOE_FP4_EWORKSPACE = 3,  /* workspace or prepared buffer too small */
+  MOE_FP4_EHIP = 4         /* a HIP launch or runtime call failed */
+} moe_fp4_status;
+
+typedef enum {
+  MOE_FP4_MXFP4 = 1, /* E2M1 + UE8M0 scale per 32 */
+  MOE_FP4_NVFP4 = 2  /* E2M1 + E4M3 scale per 16, times an fp32 global */
+} moe_fp4_format;
+
+/* Shape of one MoE layer.  H and I must be multiples of 32 for both formats
+ * (the kernels work in 32-element units); max_tokens is the largest M that
+ * later forward calls will pass, used only to size the workspace. */
+typedef struct {
+  int32_t format;      /* moe_fp4_format */
+  int32_t num_experts; /* E, resident experts; ids outside [0, E) are invalid */
+  int32_t hidden;      /* H: K of FC1, N of FC2 */
+  int32_t inter;       /* I: intermediate size */
+  int32_t top_k;       /* k: routes per token */
+  int32_t max_tokens;  /* capacity for workspace sizing */
+} moe_fp4_desc;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_fp4_status_string(moe_fp4_status s);
+
+/* Bytes of the prepared (resident) weight buffer for `desc`.  It holds the
+ * same codes, scale bytes and fp32 globals as the logical tensors, reordered,
+ * plus zero padding to whole tiles. */
+moe_fp4_status moe_fp4_prepared_bytes(const moe_fp4_desc* desc, size_t* bytes);
+
+/* Weight preparation, once per layer at load time (b12x PR #459, "Reduce
+ * NVFP4-CSF scale reconstruction overhead", commit messages: keep the exact
+ * FP4 nibbles and scale bytes, no requantisation, reorder resident offsets
+ * for contiguous decoding).  A pure byte permutation of the logical tensors
+ * above into `prepared` (device, 256-byte aligned, `prepared_bytes` >=
+ * moe_fp4_prepared_bytes).  Logical inputs must be 16-byte aligned device
+ * buffers; g13/g2 are required for NVFP4 and must be NULL for MXFP4. */
+moe_fp4_status moe_fp4_prepare(const moe_fp4_desc* desc, const uint8_t* w13_codes,
+                               const uint8_t* w13_scales, const uint8_t* w2_codes,
+                               const uint8_t* w2_scales, const float* g13, const float* g2,
+                               void* prepared, size_t prepared_bytes, void* stream);
+
+/* Inverse of moe_fp4_prepare: writes the logical tensors back from a
+ * prepared buffer (used to check that preparation is a bijection). */
+moe_fp4_status moe_fp4_unprepare(const moe_fp4_desc* desc, const void* prepared,
+                                 uint8_t* w13_codes, uint8_t* w13_scales, uint8_t* w2_codes,
+                                 uint8_t* w2_scales, float* g13, float* g2, void* stream);
+
+/* Workspace bytes for forward calls on `desc` (device scratch, 256-byte
+ * aligned, caller-owned).  The size depends only on the descriptor, so one
+ * workspace serves every M <= max_tokens; `M` is checked against max_tokens.
+ * Its contents on entry do not matter and are overwritten. */
+moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size_t* bytes);
+
+/* The layer.  x: bf16 [M][H]; topk_ids: int32 [M][k]; topk_w: fp32 [M][k]
+ * (used as given, no renormalisation); out: bf16 [M][H], overwritten.  All
+ * device pointers, 16-byte aligned except topk_ids (element size) and topk_w
+ * (4-byte).  M may be 0 (nothing is launched).  Returns MOE_FP4_EUNSUPPORTED
+ * when M * k > 64 or M > 16 until the grouped (prefill) path is present.
+ * Calls that share a workspace must be ordered on one stream. */
+moe_fp4_status moe_fp4_forward(const moe_fp4_desc* desc, const void* prepared,
+                               const uint16_t* x, int32_t M, const int32_t* topk_ids,
+                               const float* topk_w, uint16_t* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Same, with int64 route ids (any int64 value outside [0, E) is invalid). */
+moe_fp4_status moe_fp4_forward_i64(const moe_fp4_desc* desc, const void* prepared,
+                                   const uint16_t* x, int32_t M, const int64_t* topk_ids,
+                                   const float* topk_w, uint16_t* out, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* Test hook: dequantise one expert matrix from the prepared buffer with the
+ * same decode instructions the forward kernels use, into fp32 row-major
+ * `out` ([2I][H] for which = 0 (W13), [H][I] for which = 1 (W2)).  Each value
+ * is (E2M1 code * block scale) rounded to fp32, times the global (NVFP4). */
+moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prepared,
+                                      int32_t expert, int32_t which, float* out,
+                                      void* stream);
+
+/* Tuning hook for measurements: forward with an explicit FC1 K-slab width
+ * per wave in 32-element chunks (4, 8 or 16; 0 = the built-in choice). */
+moe_fp4_status moe_fp4_forward_tuned(const moe_fp4_desc* desc, const void* prepared,
+                                     const uint16_t* x, int32_t M, const int32_t* topk_ids,
+                                     const float* topk_w, uint16_t* out, void* workspace,
+                                     size_t workspace_bytes, int32_t fc1_slab_chunks,
+                                     void* stream);
+
+/* Measurement hook: queue only part of moe_fp4_forward, so a caller can put
+ * events between the FC1 and FC2 launches.  phases = 1 queues FC1 (fills the
+ * workspace's activation), 2 queues FC2 (reads it and writes `out`; it must
+ * follow a phase-1 call with the same arguments on the same stream), 3 queues
+ * both and equals moe_fp4_forward. */
+moe_fp4_status moe_fp4_forward_phase(const moe_fp4_desc* desc, const void* prepared,
+                                     const uint16_t* x, int32_t M, const int32_t* topk_ids,
+                                     const float* topk_w, uint16_t* out, void* workspace,
+                                     size_t workspace_bytes, int32_t phases, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP4_H */

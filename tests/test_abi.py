@@ -1,0 +1,120 @@
+"""The C-ABI library on the host: it loads, exports every entry point the
+header declares, and rejects bad arguments before any HIP call (so these run
+without a GPU)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from block_scaled_fp4_gather_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_fp4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_fp4_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(moe.LIB_PATH):
+        from block_scaled_fp4_gather_amd import build
+        build.build()
+    return moe.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) >= set(moe._SIGS)
+
+
+def test_status_strings(L):
+    for s, text in moe.STATUS.items():
+        assert moe.status_string(s) == text
+    assert moe.status_string(99) == "unknown status"
+
+
+def test_prepared_bytes_counts_every_byte_once(L):
+    """The resident buffer holds the logical bytes plus tile padding only."""
+    for fmt, G in (("mxfp4", 32), ("nvfp4", 16)):
+        for E, H, I in ((8, 256, 128), (512, 2560, 320), (3, 96, 64)):
+            d = moe.Desc(fmt, E, H, I, 2, 1)
+            n = moe.prepared_bytes(d)
+            logical = E * (2 * I * (H // 2 + H // G) + H * (I // 2 + I // G))
+            if fmt == "nvfp4":
+                logical += 8 * E
+            assert n >= logical
+            # padding is bounded: whole 64-row FC2 tiles, 4-byte scale words,
+            # 256-byte expert alignment and the globals header
+            slack = E * (64 * (I // 2 + I // G + 4) + 2 * I * 4 + 64 * 4 + 256) + 256
+            assert n - logical <= slack
+
+
+def test_descriptor_validation(L):
+    def status(desc):
+        n = ctypes.c_size_t()
+        return L.moe_fp4_prepared_bytes(ctypes.byref(desc.c()), ctypes.byref(n))
+
+    assert status(moe.Desc("mxfp4", 8, 256, 128, 2, 1)) == 0
+    assert status(moe.Desc(3, 8, 256, 128, 2, 1)) == 1          # unknown format
+    assert status(moe.Desc("mxfp4", 0, 256, 128, 2, 1)) == 1    # no experts
+    assert status(moe.Desc("mxfp4", 8, 240, 128, 2, 1)) == 1    # H not whole MX blocks
+    assert status(moe.Desc("nvfp4", 8, 240, 128, 2, 1)) == 2    # whole NV blocks, not whole units
+    assert status(moe.Desc("mxfp4", 8, 256, 128, 0, 1)) == 1    # k = 0
+    assert L.moe_fp4_prepared_bytes(None, None) == 1
+
+
+def _forward_status(L, desc, M=1, prepared=256, x=16, ids=4, w=4, out=16, ws=256, ws_bytes=1 << 30):
+    # fake device addresses: validation must reject before any dereference
+    return L.moe_fp4_forward(ctypes.byref(desc.c()), prepared, x, M, ids, w, out, ws, ws_bytes, None)
+
+
+def test_forward_rejects_before_launch(L):
+    d = moe.Desc("nvfp4", 512, 2560, 320, 10, 4)
+    assert _forward_status(L, d, M=5) == 1                     # M > max_tokens
+    assert _forward_status(L, d, M=-1) == 1
+    assert _forward_status(L, d, prepared=None) == 1
+    assert _forward_status(L, d, x=None) == 1
+    assert _forward_status(L, d, prepared=256 + 16) == 1       # misaligned prepared buffer
+    assert _forward_status(L, d, x=18) == 1                    # misaligned activations
+    assert _forward_status(L, d, ws_bytes=1024) == 3           # workspace too small
+    assert _forward_status(L, d, M=0, prepared=None) == 0      # nothing to do
+    big = moe.Desc("mxfp4", 8, 256, 128, 2, 4096)
+    assert _forward_status(L, big, M=4096) == 2                # grouped path not present
+    wide = moe.Desc("nvfp4", 512, 2560, 320, 10, 8)
+    assert _forward_status(L, wide, M=7) == 2                  # 70 route slots > 64
+
+
+def test_prepare_rejects_mismatched_globals(L):
+    d = moe.Desc("mxfp4", 8, 256, 128, 2, 1).c()
+    n = moe.prepared_bytes(moe.Desc("mxfp4", 8, 256, 128, 2, 1))
+    # MXFP4 with a global pointer, and NVFP4 without one
+    assert L.moe_fp4_prepare(ctypes.byref(d), 16, 16, 16, 16, 16, 16, 256, n, None) == 1
+    dn = moe.Desc("nvfp4", 8, 256, 128, 2, 1).c()
+    assert L.moe_fp4_prepare(ctypes.byref(dn), 16, 16, 16, 16, None, None, 256, n, None) == 1
+    assert L.moe_fp4_prepare(ctypes.byref(d), 16, 16, 16, 16, None, None, 256, 10, None) == 3
+
+
+def test_workspace_sizes_do_not_depend_on_m(L):
+    d = moe.Desc("nvfp4", 288, 4096, 512, 8, 8)
+    sizes = {moe.workspace_bytes(d, m) for m in (1, 2, 5, 8)}
+    assert len(sizes) == 1
+    # two bf16 activation planes for every route slot the descriptor allows
+    assert sizes.pop() == 2 * 2 * 8 * 8 * 512
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(moe, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        moe.lib()

@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path, called through the C-ABI, against the CPU oracle
+on the same seeded inputs.  Bit-exact for preparation and dequantisation;
+cosine >= 0.99995 and max-abs <= 2e-2 * RMS for the layer output."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_fp4_gather_amd import moe, synth
+from gpu_util import compare, make_layer, run_layer, say, to_dev
+from pins_util import e4m3_value, pack_nibbles, random_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"\n[gpu] {request.node.nodeid}")
+    yield
+
+
+def _logical(d):
+    return [to_dev(d[k]) for k in ("w13_codes", "w13_scales", "w2_codes", "w2_scales")]
+
+
+# ---- preparation -------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,E,H,I", [("mxfp4", 3, 96, 64), ("nvfp4", 5, 256, 96),
+                                       ("nvfp4", 2, 2560, 320), ("mxfp4", 2, 7168, 256)])
+def test_prepare_is_a_bijection(fmt, E, H, I):
+    rng = np.random.default_rng(E * H + I)
+    G = 32 if fmt == "mxfp4" else 16
+    d = dict(w13_codes=rng.integers(0, 256, (E, 2 * I, H // 2), dtype=np.uint8),
+             w13_scales=rng.integers(0, 256, (E, 2 * I, H // G), dtype=np.uint8),
+             w2_codes=rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8),
+             w2_scales=rng.integers(0, 256, (E, H, I // G), dtype=np.uint8))
+    g = (rng.random(E).astype(np.float32), rng.random(E).astype(np.float32)) if fmt == "nvfp4" else (None, None)
+    desc = moe.Desc(fmt, E, H, I, 2, 1)
+    src = _logical(d)
+    g13, g2 = to_dev(g[0]), to_dev(g[1])
+    prep = torch.full((moe.prepared_bytes(desc),), 0xAB, dtype=torch.uint8, device="cuda")
+    moe.prepare(desc, *src, g13, g2, prep)
+    back = [torch.full_like(t, 0x5C) for t in src]
+    gb = [torch.full_like(t, -1.0) if t is not None else None for t in (g13, g2)]
+    moe.unprepare(desc, prep, *back, *gb)
+    torch.cuda.synchronize()
+    for a, b in zip(src, back):
+        assert torch.equal(a, b)
+    if fmt == "nvfp4":
+        assert torch.equal(g13, gb[0]) and torch.equal(g2, gb[1])
+    # same bytes, reordered: the byte histogram of the buffer is the logical
+    # bytes' histogram plus zero padding
+    hist = torch.bincount(prep.long(), minlength=256).cpu().numpy()
+    want = sum(np.bincount(a.ravel(), minlength=256) for a in d.values())
+    assert np.array_equal(hist[1:], want[1:]) or fmt == "nvfp4"  # fp32 globals add bytes
+    # preparation is deterministic
+    prep2 = torch.zeros_like(prep)
+    moe.prepare(desc, *src, g13, g2, prep2)
+    torch.cuda.synchronize()
+    assert torch.equal(prep, prep2)
+
+
+def _all_codes_all_scales(fmt, E, H, I, rng):
+    """Weights whose W13 and W2 together hold every nibble next to every scale byte."""
+    G = 32 if fmt == "mxfp4" else 16
+    nib13 = rng.integers(0, 16, (E, 2 * I, H), dtype=np.uint8)
+    nib13[..., :16] = np.arange(16, dtype=np.uint8)
+    nib2 = rng.integers(0, 16, (E, H, I), dtype=np.uint8)
+    nib2[..., :16] = np.arange(16, dtype=np.uint8)
+    s13 = (np.arange(E * 2 * I * (H // G)) % 256).astype(np.uint8).reshape(E, 2 * I, H // G)
+    s2 = ((np.arange(E * H * (I // G)) * 7 + 3) % 256).astype(np.uint8).reshape(E, H, I // G)
+    return dict(w13_codes=pack_nibbles(nib13), w13_scales=s13, w2_codes=pack_nibbles(nib2), w2_scales=s2)
+
+
+@pytest.mark.parametrize("fmt,g", [("mxfp4", None), ("nvfp4", 1.0 / 512), ("nvfp4", 0.3)])
+def test_dequant_export_bit_exact(fmt, g):
+    E, H, I = 2, 256, 64
+    rng = np.random.default_rng(5)
+    d = _all_codes_all_scales(fmt, E, H, I, rng)
+    g13 = np.full(E, g, np.float32) if g else None
+    g2 = np.full(E, g * 3, np.float32) if g else None
+    desc = moe.Desc(fmt, E, H, I, 2, 1)
+    prep = torch.empty(moe.prepared_bytes(desc), dtype=torch.uint8, device="cuda")
+    moe.prepare(desc, *_logical(d), to_dev(g13), to_dev(g2), prep)
+    for e in range(E):
+        for which, rows, cols, c, s, gl in ((0, 2 * I, H, "w13_codes", "w13_scales", g13),
+                                            (1, H, I, "w2_codes", "w2_scales", g2)):
+            out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+            moe.dequant_export(desc, prep, e, which, out)
+            got = out.cpu().numpy()
+            want = oracle.dequant(fmt, d[c][e], d[s][e], 1.0 if gl is None else float(gl[e]))
+            nan = np.isnan(want)
+            assert np.array_equal(np.isnan(got), nan), f"expert {e} which {which}: NaN positions"
+            assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32)), \
+                f"expert {e} which {which}: {np.count_nonzero(got[~nan] != want[~nan])} values differ"
+
+
+# ---- the layer -----------------------------------------------------------------
+
+SMALL = [
+    # fmt, E, H, I, M, k, seed
+    ("mxfp4", 4, 64, 32, 1, 1, 1),
+    ("mxfp4", 6, 96, 64, 3, 3, 2),      # ragged FC2 tile (96 rows = 64 + 32)
+    ("nvfp4", 5, 256, 96, 2, 4, 3),
+    ("nvfp4", 8, 512, 128, 5, 2, 4),
+    ("mxfp4", 16, 1024, 256, 8, 4, 5),
+    ("nvfp4", 12, 2560, 64, 16, 2, 6),
+    ("mxfp4", 3, 1536, 544, 2, 2, 7),   # I = 17 chunks: two FC2 batches
+]
+
+
+@pytest.mark.parametrize("fmt,E,H,I,M,k,seed", SMALL)
+def test_forward_small_shapes(fmt, E, H, I, M, k, seed):
+    rng = np.random.default_rng(seed)
+    d, _, _ = random_case(rng, fmt, E, H, I, M, k)
+    flat = d["ids"].reshape(-1)
+    if flat.size > 2:
+        flat[1] = -1                 # an invalid route
+        flat[-1] = E + seed          # another, past the last expert
+    if M > 1 and k > 1:
+        d["ids"][1, 1] = d["ids"][1, 0]  # a duplicate within a token
+    acc, _ = oracle.forward_f32(fmt, d)
+    layer = make_layer(fmt, d, k, M)
+    for cs in (None, 4, 8, 16):
+        label = f"{fmt} E{E} H{H} I{I} M{M} k{k} slab={cs}"
+        say(f"  run {label}")
+        compare(run_layer(layer, d, slab_chunks=cs), acc, label)
+    compare(run_layer(layer, d, ids_dtype=torch.int64), acc, "int64 ids")
+
+
+@pytest.mark.parametrize("name", ["tiny_mxfp4", "nvfp4_decode_e512", "nvfp4_multi_e288",
+                                  "mxfp4_shard_e256_m1", "mxfp4_shard_e256_m2", "mxfp4_shard_e256_m4"])
+def test_forward_workloads_full_size(name):
+    wl = synth.WORKLOADS[name]
+    say(f"  generate {name}")
+    d = synth.generate(wl)
+    acc, _ = oracle.forward_f32(wl.fmt, d)
+    layer = make_layer(wl.fmt, d, wl.k, max(wl.M, 16))
+    compare(run_layer(layer, d), acc, name)
+    if wl.n_invalid:
+        assert (d["ids"] < 0).any() and (d["ids"] >= wl.E).any()
+
+
+def test_invalid_ids_with_nan_poisoned_expert_zero():
+    for fmt, poison in (("mxfp4", 0xFF), ("nvfp4", 0x7F)):
+        rng = np.random.default_rng(21)
+        d, _, _ = random_case(rng, fmt, 6, 512, 64, 4, 4)
+        d["ids"][:] = rng.integers(1, 6, size=(4, 4))
+        d["w13_scales"][0] = poison
+        d["w2_scales"][0] = poison
+        d["ids"][:, 2] = [-1, 6, 2**31 - 1, -(2**31)]
+        acc, _ = oracle.forward_f32(fmt, d)
+        assert np.isfinite(acc).all()
+        layer = make_layer(fmt, d, 4, 4)
+        compare(run_layer(layer, d), acc, f"{fmt} poisoned expert 0")
+        # int64 ids beyond the int32 range are invalid too
+        d64 = dict(d)
+        d64["ids"] = d["ids"].astype(np.int64)
+        d64["ids"][:, 2] = [-(2**40), 2**40, 2**62, 6]
+        compare(run_layer(layer, d64, ids_dtype=torch.int64), acc, f"{fmt} int64 out-of-range ids")
+
+
+def test_all_invalid_routes_give_positive_zero():
+    rng = np.random.default_rng(22)
+    d, _, _ = random_case(rng, "nvfp4", 4, 256, 64, 3, 2)
+    d["ids"][:] = np.array([[-1, 4], [7, -3], [4, 4]], np.int32)
+    layer = make_layer("nvfp4", d, 2, 3)
+    x = to_dev(d["x"]).view(torch.bfloat16)
+    out = torch.full((3, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    layer(x, to_dev(d["ids"]), to_dev(d["w"]), out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), torch.zeros_like(out.view(torch.int16)))
+
+
+def test_zero_router_weights_give_zero():
+    rng = np.random.default_rng(23)
+    d, _, _ = random_case(rng, "mxfp4", 4, 256, 64, 2, 3)
+    d["w"][:] = 0
+    layer = make_layer("mxfp4", d, 3, 2)
+    bits = run_layer(layer, d)
+    assert not np.any(bits & 0x7FFF)
+
+
+def test_poisoned_scratch_and_output_deterministic_and_inputs_unchanged():
+    wl = synth.WORKLOADS["nvfp4_decode_e512"].replace(E=64)
+    d = synth.generate(wl)
+    d["ids"] %= 64
+    acc, _ = oracle.forward_f32(wl.fmt, d)
+    layer = make_layer(wl.fmt, d, wl.k, 4)
+    x = to_dev(d["x"]).view(torch.bfloat16)
+    ids = to_dev(d["ids"])
+    w = to_dev(d["w"])
+    snap = [t.clone() for t in (x, ids, w, layer.prepared)]
+    results = []
+    for rep in range(3):
+        layer.workspace.fill_(0xFF)  # NaN in every scratch word
+        out = torch.full((1, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        layer(x, ids, w, out=out)
+        torch.cuda.synchronize()
+        results.append(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    compare(results[0], acc, "poisoned scratch")
+    assert all(np.array_equal(results[0], r) for r in results[1:]), "not bit-reproducible"
+    for a, b in zip(snap, (x, ids, w, layer.prepared)):
+        assert torch.equal(a, b), "an input was modified"
+
+
+def test_graph_capture_and_replay_with_changing_routes():
+    wl = synth.WORKLOADS["mxfp4_shard_e256_m2"].replace(E=32, H=1024)
+    d = synth.generate(wl)
+    d["ids"] %= 32
+    layer = make_layer(wl.fmt, d, wl.k, 2)
+    x = to_dev(d["x"]).view(torch.bfloat16)
+    ids = to_dev(d["ids"])
+    w = to_dev(d["w"])
+    out = torch.empty((2, wl.H), dtype=torch.bfloat16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer(x, ids, w, out=out, stream=s)  # warm up outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(x, ids, w, out=out)
+    rng = np.random.default_rng(99)
+    for rep in range(4):
+        new_ids = rng.integers(-2, 34, size=(2, wl.k)).astype(np.int32)
+        new_w = rng.random((2, wl.k)).astype(np.float32)
+        ids.copy_(torch.from_numpy(new_ids))
+        w.copy_(torch.from_numpy(new_w))
+        g.replay()
+        torch.cuda.synchronize()
+        eager = torch.empty_like(out)
+        layer(x, ids, w, out=eager)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {rep}"
+        dd = dict(d)
+        dd["ids"], dd["w"] = new_ids, new_w
+        acc, _ = oracle.forward_f32(wl.fmt, dd)
+        compare(out.view(torch.int16).cpu().numpy().view(np.uint16), acc, f"replay {rep}")
+
+
+def test_forward_m0_is_a_no_op():
+    rng = np.random.default_rng(24)
+    d, _, _ = random_case(rng, "mxfp4", 4, 64, 32, 1, 1)
+    layer = make_layer("mxfp4", d, 1, 1)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((0, 1), dtype=torch.int32, device="cuda")
+    w = torch.empty((0, 1), dtype=torch.float32, device="cuda")
+    layer(x, ids, w)
+    torch.cuda.synchronize()
