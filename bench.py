@@ -39,9 +39,25 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-check", action="store_true", help="skip the oracle check (profiling runs)")
-    ap.add_argument("--slab", type=int, default=None, help="FC1 K-slab chunks (4, 8, 16)")
+    ap.add_argument("--shape", default=None,
+                    help="launch shape kl1,r1,r2 (FC1 chunks per wave, FC1 rows, FC2 rows; 0 = built-in)")
     ap.add_argument("--extra", action="store_true", help="also time warm-cache calls and a copy probe")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run 5 copies of a 256 MiB buffer (reference for profiler byte counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain device copy of known size: 256 MiB read + 256 MiB written per
+    dispatch.  Profiler byte counters of this run calibrate the ones of the
+    layer's kernels."""
+    import torch
+    src = torch.ones(1 << 26, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_dispatch": {"read": src.numel() * 4, "write": dst.numel() * 4}}))
 
 
 def log(*a):
@@ -91,6 +107,9 @@ def cold_groups(wl, d, dev):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
               "the layer would shard by experts or by I with one exchange of the [M, H] output.",
@@ -124,12 +143,13 @@ def main():
     out = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     log("[bench] prepared")
+    tuning = moe.Tuning(*[int(v) for v in args.shape.split(",")], 0) if args.shape else None
 
     check = None
     if not args.no_check:
         import oracle
         acc, _ = oracle.forward_f32(wl.fmt, d)
-        layer(x, ids, w, out=out, slab_chunks=args.slab)
+        layer(x, ids, w, out=out, tuning=tuning)
         torch.cuda.synchronize()
         g = oracle.bf16_bits_to_f32(out.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64).ravel()
         r = acc.astype(np.float64).ravel()
@@ -153,17 +173,18 @@ def main():
     log(f"[bench] {len(groups)} disjoint expert groups in rotation")
 
     def call(g, phases=None):
-        layer(x, g[0], g[1], out=out, slab_chunks=args.slab, phases=phases)
+        layer(x, g[0], g[1], out=out, tuning=tuning, phases=phases)
 
     def region(phases=None, rotate=True):
         """One graph holds a pass over the rotation; it is replayed until K
         steps have run.  Returns (us per step from events, wall s per step)."""
-        n = len(groups)
+        # at least 64 steps per graph, so the graph launch itself is amortised
+        n = len(groups) * max(1, -(-64 // len(groups)))
         reps = max(1, -(-K // n))
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(n):
-                call(groups[i] if rotate else groups[0], phases)
+                call(groups[i % len(groups)] if rotate else groups[0], phases)
         g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

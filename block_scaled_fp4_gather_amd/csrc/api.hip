@@ -38,8 +38,8 @@ moe_fp4_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_FP4_OK : MO
 template <typename IdT>
 moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, const uint16_t* x,
                             int32_t M, const IdT* ids, const float* w, uint16_t* out,
-                            void* workspace, size_t ws_bytes, int32_t cs, int32_t phases,
-                            void* stream) {
+                            void* workspace, size_t ws_bytes, const moe_fp4_tuning* tuning,
+                            int32_t phases, void* stream) {
   Layout L;
   moe_fp4_status st = desc_layout(desc, &L);
   if (st != MOE_FP4_OK) return st;
@@ -49,15 +49,19 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
   if (!aligned(prepared, 256) || !aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
       !aligned(ids, sizeof(IdT)) || !aligned(w, 4))
     return MOE_FP4_EINVAL;
-  if (cs != 0 && cs != 4 && cs != 8 && cs != 16) return MOE_FP4_EINVAL;
+  moe::DecodeShape shape{0, 0, 0};
+  if (tuning) {
+    shape = moe::DecodeShape{tuning->fc1_chunks_per_wave, tuning->fc1_rows, tuning->fc2_rows};
+    if (tuning->reserved != 0 || !moe::valid_shape(L, shape)) return MOE_FP4_EINVAL;
+  }
   if (phases < 1 || phases > 3) return MOE_FP4_EINVAL;
   const int k = desc->top_k;
   if (k > moe::kDecodeMaxSlots || M > moe::decode_max_tokens(k)) return MOE_FP4_EUNSUPPORTED;
   const moe::DecodeWs W = moe::decode_ws(L, decode_slots(desc));
   if ((int64_t)ws_bytes < W.total) return MOE_FP4_EWORKSPACE;
-  if (cs == 0) cs = moe::choose_slab(L);
+  shape = moe::resolve_shape(L, M * k, shape);
   return from_hip(moe::launch_decode<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
-                                          (uint8_t*)workspace, W, cs, phases, (hipStream_t)stream));
+                                          (uint8_t*)workspace, W, shape, phases, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -130,7 +134,7 @@ moe_fp4_status moe_fp4_forward(const moe_fp4_desc* desc, const void* prepared, c
                                uint16_t* out, void* workspace, size_t workspace_bytes,
                                void* stream) {
   return forward_impl<int32_t>(desc, prepared, x, M, topk_ids, topk_w, out, workspace,
-                               workspace_bytes, 0, 3, stream);
+                               workspace_bytes, nullptr, 3, stream);
 }
 
 moe_fp4_status moe_fp4_forward_i64(const moe_fp4_desc* desc, const void* prepared,
@@ -138,24 +142,16 @@ moe_fp4_status moe_fp4_forward_i64(const moe_fp4_desc* desc, const void* prepare
                                    const float* topk_w, uint16_t* out, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   return forward_impl<int64_t>(desc, prepared, x, M, topk_ids, topk_w, out, workspace,
-                               workspace_bytes, 0, 3, stream);
+                               workspace_bytes, nullptr, 3, stream);
 }
 
-moe_fp4_status moe_fp4_forward_tuned(const moe_fp4_desc* desc, const void* prepared,
-                                     const uint16_t* x, int32_t M, const int32_t* topk_ids,
-                                     const float* topk_w, uint16_t* out, void* workspace,
-                                     size_t workspace_bytes, int32_t fc1_slab_chunks,
-                                     void* stream) {
+moe_fp4_status moe_fp4_forward_ex(const moe_fp4_desc* desc, const void* prepared,
+                                  const uint16_t* x, int32_t M, const int32_t* topk_ids,
+                                  const float* topk_w, uint16_t* out, void* workspace,
+                                  size_t workspace_bytes, const moe_fp4_tuning* tuning,
+                                  int32_t phases, void* stream) {
   return forward_impl<int32_t>(desc, prepared, x, M, topk_ids, topk_w, out, workspace,
-                               workspace_bytes, fc1_slab_chunks, 3, stream);
-}
-
-moe_fp4_status moe_fp4_forward_phase(const moe_fp4_desc* desc, const void* prepared,
-                                     const uint16_t* x, int32_t M, const int32_t* topk_ids,
-                                     const float* topk_w, uint16_t* out, void* workspace,
-                                     size_t workspace_bytes, int32_t phases, void* stream) {
-  return forward_impl<int32_t>(desc, prepared, x, M, topk_ids, topk_w, out, workspace,
-                               workspace_bytes, 0, phases, stream);
+                               workspace_bytes, tuning, phases, stream);
 }
 
 moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prepared,

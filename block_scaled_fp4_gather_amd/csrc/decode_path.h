@@ -12,7 +12,14 @@ namespace moe {
 constexpr int kDecodeMaxSlots = 64;
 constexpr int kDecodeMaxTokens = 16;
 constexpr int kMaxWaves = 16;   // waves per FC1 workgroup
-constexpr int kMaxWaves2 = 12;  // waves per FC2 workgroup (register budget)
+// Activations of all route slots are staged in FC2's LDS up to this size,
+// within the 64 KiB a workgroup may allocate without opting in to more.
+constexpr int64_t kStageActBytes = 40 * 1024;
+constexpr int64_t kMaxLdsBytes = 64 * 1024;
+
+// Waves per FC2 workgroup: 16-chunk lanes need more than the 128 VGPRs a
+// 16-wave workgroup leaves each wave.
+constexpr int fc2_max_waves(int kl) { return kl >= 16 ? 12 : 16; }
 
 // Workspace of the decode band: the activation a[r][n] of every route slot r
 // that carries an (expert, token) pair, as two bf16 planes (hi, lo).
@@ -34,18 +41,41 @@ inline int decode_max_tokens(int k) {
   return m < kDecodeMaxTokens ? m : kDecodeMaxTokens;
 }
 
-// FC1 K-slab width (chunks per wave): the smallest of 4, 8, 16 whose slabs
-// fit in one workgroup of at most 16 waves (wider K loops over slabs).
-inline int choose_slab(const Layout& L) {
-  for (int cs : {4, 8})
-    if ((L.nC1 + cs - 1) / cs <= kMaxWaves) return cs;
-  return 16;
+// Launch shape of the decode kernels (see moe_fp4_tuning).
+struct DecodeShape {
+  int kl1;  // FC1 chunks per wave: 4, 8, 16
+  int r1;   // FC1 rows per workgroup: 16, 32
+  int r2;   // FC2 rows per workgroup: 8, 16, 32
+};
+
+// FC2 chunk lanes: the smallest of 4, 8, 16 that covers I (longer I loops).
+inline int fc2_chunk_lanes(const Layout& L) { return L.nC2 <= 4 ? 4 : (L.nC2 <= 8 ? 8 : 16); }
+
+inline bool valid_shape(const Layout& L, const DecodeShape& s) {
+  if (s.kl1 != 0 && s.kl1 != 4 && s.kl1 != 8 && s.kl1 != 16) return false;
+  if (s.r1 != 0 && s.r1 != 16 && s.r1 != 32) return false;
+  if (s.r2 != 0 && s.r2 != 8 && s.r2 != 16 && s.r2 != 32) return false;
+  if (s.r2 != 0 && s.r2 * fc2_chunk_lanes(L) < 64) return false;  // a lane needs a row
+  return true;
+}
+
+// Built-in choices for fields left at 0 (from sweeps on MI355X over the
+// E512/H2560/I320 NVFP4 and E256/H7168/I256 MXFP4 decode shapes).
+inline DecodeShape resolve_shape(const Layout& L, int slots, DecodeShape s) {
+  if (s.kl1 == 0) {
+    // 8 chunks per wave while K fits one workgroup of 16 waves, else 16
+    s.kl1 = (L.nC1 + 7) / 8 <= kMaxWaves ? 8 : 16;
+    if (L.nC1 <= 8) s.kl1 = 4;
+  }
+  if (s.r1 == 0) s.r1 = (int64_t)slots * L.nB1 * 2 >= 160 ? 32 : 16;
+  if (s.r2 == 0) s.r2 = fc2_chunk_lanes(L) == 4 ? 32 : 16;
+  return s;
 }
 
 template <typename IdT>
 hipError_t launch_decode(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                          const IdT* ids, const float* tw, uint16_t* out, uint8_t* ws,
-                         const DecodeWs& W, int cs, int phases, hipStream_t st);
+                         const DecodeWs& W, const DecodeShape& shape, int phases, hipStream_t st);
 
 hipError_t launch_repack(const Layout& L, int dir, uint8_t* w13c, uint8_t* w13s, uint8_t* w2c,
                          uint8_t* w2s, float* g13, float* g2, uint8_t* prep, hipStream_t st);

@@ -69,94 +69,211 @@ __device__ __forceinline__ uint64_t token_routes(uint64_t mask, int t, int k) {
   return (mask >> (t * k)) & kmask;
 }
 
-// SiLU(gate)*up across the lane pair (l, l+32) of an FC1 tile.  The fp32
-// activation a is stored as two bf16 planes, a = hi + lo (hi = bf16(a),
-// lo = bf16(a - hi)), which keeps 16 significant bits for FC2's bf16 dot
-// products.
-__device__ __forceinline__ void fc1_finish(float v, float g13, int lane, int b, int r,
-                                           const Layout& L, uint16_t* __restrict__ act_hi,
-                                           uint16_t* __restrict__ act_lo) {
-  v *= g13;
-  const float up = __shfl(v, (lane + 32) & 63);
-  if (lane < 32) {
-    const float a = v / (1.0f + __expf(-v)) * up;
-    const uint16_t hi = f32_to_bf16_rne(a);
-    const float rest = a - __uint_as_float((uint32_t)hi << 16);
-    const int64_t at = (int64_t)r * L.I + 32 * b + lane;
-    act_hi[at] = hi;
-    act_lo[at] = f32_to_bf16_rne(rest);
+// DPP lane exchange inside a 16-lane row: partner = lane ^ X for X in
+// {1, 3, 7, 15} (quad_perm [1,0,3,2], quad_perm [3,2,1,0], row_half_mirror,
+// row_mirror).
+template <int X>
+__device__ __forceinline__ float dpp_xor(float v) {
+  constexpr int ctrl = X == 1 ? 0xB1 : X == 3 ? 0x1B : X == 7 ? 0x141 : 0x140;
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+
+template <int M>
+__device__ __forceinline__ void fold_stage(float* v, bool upper) {
+  // v[0, 2M) -> v[0, M): keep the half selected by this lane's bit, add the
+  // partner's copy of the same half (the partner selected the other one).
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const float keep = upper ? v[i + M] : v[i];
+    const float send = upper ? v[i] : v[i + M];
+    v[i] = keep + dpp_xor<2 * M - 1>(send);
   }
 }
 
-template <int FMT, int CS, typename IdT>
+template <int X, int T>
+__device__ __forceinline__ void fold_plain(float* v) {
+#pragma unroll
+  for (int j = 0; j < T; ++j) v[j] += dpp_xor<X>(v[j]);
+}
+
+// Reduction over the KL lanes of a group (KL in {4, 8, 16}, the group
+// aligned inside a 16-lane row) of T partial sums per lane (T a power of two,
+// T <= KL): on entry lane p holds v[j] for rows j = 0..T-1; on exit lane p
+// returns the full sum of row p % T.  Lane bits at or above log2(T) are
+// folded plainly (every value adds lane p ^ (2^(b+1) - 1), which differs from
+// p in bit b); the lower bits are folded by transposition: stage m pairs lane
+// p with lane p ^ (2m - 1), and each lane keeps the half of its rows whose
+// bit m matches its own.
+template <int KL, int T>
+__device__ __forceinline__ float fold_rows(float* v, int p) {
+  if (KL >= 16 && T <= 8) fold_plain<15, T>(v);
+  if (KL >= 8 && T <= 4) fold_plain<7, T>(v);
+  if (KL >= 4 && T <= 2) fold_plain<3, T>(v);
+  if (T <= 1) fold_plain<1, T>(v);
+  if (T >= 8) fold_stage<4>(v, (p & 4) != 0);
+  if (T >= 4) fold_stage<2>(v, (p & 2) != 0);
+  if (T >= 2) fold_stage<1>(v, (p & 1) != 0);
+  return v[0];
+}
+
+// Block scale(s) of chunk c from the lane's scale dword of that row.
+template <int FMT>
+__device__ __forceinline__ f32x2_t chunk_scale(uint32_t dword, int c) {
+  if (FMT == kMXFP4) {
+    const float s = mx_scale(dword, c);
+    return f32x2_t{s, s};
+  }
+  return e4m3x2_to_f32(dword, (c & 1) != 0);
+}
+
+// Dot product of one 32-element unit with 32 bf16 activations (16 dwords),
+// with the block scale(s) applied to the partial sums.
+template <int FMT>
+__device__ __forceinline__ float unit_dot(const u32x4 q, const uint32_t* a, f32x2_t sc) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    bf16x2_t wv[4];
+    fp4x8_to_bf16(w[d], wv);  // elements 8d .. 8d+7
+    float acc = d < 2 ? pa : pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(wv[i], as_bf16x2(a[4 * d + i]), acc, false);
+    if (d < 2)
+      pa = acc;
+    else
+      pb = acc;
+  }
+  if (FMT == kMXFP4) return (pa + pb) * sc.x;
+  return fmaf(pa, sc.x, pb * sc.y);
+}
+
+// Same against an activation held as two bf16 planes (a = hi + lo); the
+// unit is decoded once for both.
+template <int FMT>
+__device__ __forceinline__ float unit_dot2(const u32x4 q, const uint32_t* hi, const uint32_t* lo,
+                                           f32x2_t sc) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float pa = 0.0f, pb = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    bf16x2_t wv[4];
+    fp4x8_to_bf16(w[d], wv);
+    float acc = d < 2 ? pa : pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = __builtin_amdgcn_fdot2_f32_bf16(wv[i], as_bf16x2(hi[4 * d + i]), acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(wv[i], as_bf16x2(lo[4 * d + i]), acc, false);
+    }
+    if (d < 2)
+      pa = acc;
+    else
+      pb = acc;
+  }
+  if (FMT == kMXFP4) return (pa + pb) * sc.x;
+  return fmaf(pa, sc.x, pb * sc.y);
+}
+
+__device__ __forceinline__ void load_chunk16(const uint16_t* p, uint32_t* d) {
+  const u32x4* q = (const u32x4*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = q[i];
+    d[4 * i] = v.x;
+    d[4 * i + 1] = v.y;
+    d[4 * i + 2] = v.z;
+    d[4 * i + 3] = v.w;
+  }
+}
+
+// Copies n16 16-byte words from global to LDS with all threads of the
+// workgroup (no barrier; the caller synchronises before reading).
+__device__ __forceinline__ void stage_lds(const void* src, void* dst, int n16) {
+  const u32x4* s = (const u32x4*)src;
+  u32x4* d = (u32x4*)dst;
+  for (int i = threadIdx.x; i < n16; i += blockDim.x) d[i] = s[i];
+}
+
+__device__ __forceinline__ void lds_chunk16(const uint16_t* p, uint32_t* d) {
+  const u32x4* q = (const u32x4*)p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = q[i];
+    d[4 * i] = v.x;
+    d[4 * i + 1] = v.y;
+    d[4 * i + 2] = v.z;
+    d[4 * i + 3] = v.w;
+  }
+}
+
+// FC1: one workgroup per (route slot, 64-row tile, block of R rows): R/2 gate
+// rows and their R/2 up rows.  Wave w covers chunks [w*KL, w*KL + KL) (and
+// further groups of W*KL chunks if K is longer); lane (g, p) = (lane / KL,
+// lane % KL) owns chunk w*KL + p of the block rows q = g + RG*j, j < T, so
+// its activation chunk is read once and reused for T rows.  The activations
+// of the slot's own token are staged in LDS while the route lookup is in
+// flight.
+template <int FMT, int KL, int R, typename IdT>
 __global__ void __launch_bounds__(1024)
     fc1_kernel(const uint8_t* __restrict__ prep, const Layout L, const uint16_t* __restrict__ x,
                const IdT* __restrict__ ids, const int M, const int k,
                uint16_t* __restrict__ act_hi, uint16_t* __restrict__ act_lo) {
   constexpr int SPD = FMT == kMXFP4 ? 4 : 2;  // chunks per scale dword
-  constexpr int ND = CS / SPD;
-  extern __shared__ float part[];  // [token index][wave][lane]
+  constexpr int RG = 64 / KL;                 // row groups of a wave
+  constexpr int T = R / RG;                   // rows per lane
+  constexpr int NB = 64 / R;                  // blocks per tile
+  extern __shared__ u32x4 lds_raw[];
+  uint16_t* xs = (uint16_t*)lds_raw;                // [H] activations of token t0
+  float* part = (float*)(xs + align_up(L.H, 64));  // [token index][16 waves][R rows]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
-  const int b = blockIdx.x % L.nB1;
-  const int s = blockIdx.x / L.nB1;
-  const Routes R = load_routes(ids, (const float*)nullptr, M * k, L.E);
+  const int p = lane % KL, g = lane / KL;
+  const int blk = blockIdx.x % NB;
+  const int b = (blockIdx.x / NB) % L.nB1;
+  const int s = (blockIdx.x / NB) / L.nB1;
+  const int t0 = s / k;  // the slot's own token routes to the slot's expert
+  const int ngroups = (L.nC1 + W * KL - 1) / (W * KL);
+
+  stage_lds(x + (int64_t)t0 * L.H, xs, L.H / 8);
+  const Routes R_ = load_routes(ids, (const float*)nullptr, M * k, L.E);
   uint64_t mask = 0;
-  const int e = slot_expert(R, s, &mask);
+  const int e = slot_expert(R_, s, &mask);
   if (e < 0) return;  // same decision in every wave of the workgroup
   const uint8_t* tile = prep + fc1_tile_offset(L, e, b);
-  const uint32_t* sw = (const uint32_t*)(tile + (int64_t)L.nC1 * 1024) + lane;
-  const int S = (L.nC1 + CS - 1) / CS;
+  const uint8_t* sbase = tile + (int64_t)L.nC1 * 1024;
+
   int m = 0;
   for (int t = 0; t < M; ++t) m += token_routes(mask, t, k) != 0;
-  for (int i = 0; i < m; ++i) part[(i * W + wave) * 64 + lane] = 0.0f;
+  for (int i = threadIdx.x; i < m * 16 * R; i += blockDim.x) part[i] = 0.0f;
+  __syncthreads();
 
-  for (int slab = wave; slab < S; slab += W) {
-    const int c0 = slab * CS;
-    const int n = min(CS, L.nC1 - c0);
-    // Unconditional loads (a tail slab re-reads its last chunk, a cache hit):
-    // guarded loads become branches, and the compiler then waits for each
-    // load to land before issuing the next one.
-    u32x4 q[CS];
+  for (int grp = 0; grp < ngroups; ++grp) {
+    const int c = (grp * W + wave) * KL + p;
+    const bool cv = c < L.nC1;
+    const int cc = min(c, L.nC1 - 1);
+    u32x4 q[T];
+    uint32_t sd[T];
 #pragma unroll
-    for (int i = 0; i < CS; ++i)
-      q[i] = __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)min(c0 + i, L.nC1 - 1) * 1024) + lane);
-    uint32_t sd[ND];
-#pragma unroll
-    for (int i = 0; i < ND; ++i) sd[i] = __builtin_nontemporal_load(sw + 64 * min(c0 / SPD + i, L.nQ1 - 1));
+    for (int j = 0; j < T; ++j) {
+      const int qr = g + RG * j;  // block row: R/2 gate rows, then R/2 up rows
+      const int row = (qr < R / 2 ? 0 : 32 - R / 2) + blk * (R / 2) + qr;
+      q[j] = __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)cc * 1024 + row * 16));
+      sd[j] = __builtin_nontemporal_load((const uint32_t*)(sbase + (cc / SPD) * 256 + row * 4));
+    }
     int ti = 0;
     for (int t = 0; t < M; ++t) {
       if (!token_routes(mask, t, k)) continue;
-      const uint32_t* xr = (const uint32_t*)(x + (int64_t)t * L.H) + c0 * 16;
-      float acc = 0.0f;
+      uint32_t xc[16];
+      if (t == t0)
+        lds_chunk16(xs + 32 * cc, xc);
+      else
+        load_chunk16(x + (int64_t)t * L.H + 32 * cc, xc);
+      float v[T];
 #pragma unroll
-      for (int i = 0; i < CS; ++i) {
-        if (i < n) {
-          bf16x2_t wv[16];
-          fp4x8_to_bf16(q[i].x, wv);
-          fp4x8_to_bf16(q[i].y, wv + 4);
-          fp4x8_to_bf16(q[i].z, wv + 8);
-          fp4x8_to_bf16(q[i].w, wv + 12);
-          const uint32_t* xc = xr + i * 16;
-          if (FMT == kMXFP4) {
-            float p = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) p = __builtin_amdgcn_fdot2_f32_bf16(wv[j], as_bf16x2(xc[j]), p, false);
-            acc = fmaf(p, mx_scale(sd[i / 4], i), acc);
-          } else {
-            float pa = 0.0f, pb = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) pa = __builtin_amdgcn_fdot2_f32_bf16(wv[j], as_bf16x2(xc[j]), pa, false);
-#pragma unroll
-            for (int j = 8; j < 16; ++j) pb = __builtin_amdgcn_fdot2_f32_bf16(wv[j], as_bf16x2(xc[j]), pb, false);
-            const f32x2_t sc = e4m3x2_to_f32(sd[i / 2], (i & 1) != 0);
-            acc = fmaf(pa, sc.x, acc);
-            acc = fmaf(pb, sc.y, acc);
-          }
-        }
-      }
-      part[(ti * W + wave) * 64 + lane] += acc;
+      for (int j = 0; j < T; ++j) v[j] = cv ? unit_dot<FMT>(q[j], xc, chunk_scale<FMT>(sd[j], cc)) : 0.0f;
+      const float r = fold_rows<KL, T>(v, p);
+      if (p < T) part[(ti * 16 + wave) * R + g + RG * p] += r;
       ++ti;
     }
   }
@@ -166,49 +283,81 @@ __global__ void __launch_bounds__(1024)
   for (int t = 0; t < M; ++t) {
     const uint64_t tm = token_routes(mask, t, k);
     if (!tm) continue;
-    if (ti % W == wave) {
-      float v = 0.0f;
-      for (int w = 0; w < W; ++w) v += part[(ti * W + w) * 64 + lane];
-      fc1_finish(v, g13, lane, b, t * k + __builtin_ctzll(tm), L, act_hi, act_lo);
+    if (ti % W == wave && lane < R / 2) {
+      float gate = 0.0f, up = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        gate += part[(ti * 16 + w) * R + lane];
+        up += part[(ti * 16 + w) * R + R / 2 + lane];
+      }
+      gate *= g13;
+      up *= g13;
+      const float a = gate / (1.0f + __expf(-gate)) * up;
+      // a = hi + lo in two bf16 planes: 16 significant bits for FC2's bf16
+      // dot products.
+      const uint16_t hi = f32_to_bf16_rne(a);
+      const int64_t at = (int64_t)(t * k + __builtin_ctzll(tm)) * L.I + 32 * b + blk * (R / 2) + lane;
+      act_hi[at] = hi;
+      act_lo[at] = f32_to_bf16_rne(a - __uint_as_float((uint32_t)hi << 16));
     }
     ++ti;
   }
 }
 
-template <int FMT, int NB, typename IdT>
-__global__ void __launch_bounds__(64 * kMaxWaves2)
+// FC2: one workgroup per block of R rows of H; its waves split the route
+// slots.  Lane (g, p) owns chunk c0 + p of the expert's block rows
+// q = g + RG*j, j < T.  With STAGE, the activations of every route slot are
+// staged in LDS while the route lookup is in flight.
+template <int FMT, int KL, int R, bool STAGE, typename IdT>
+__global__ void __launch_bounds__(64 * fc2_max_waves(KL))
     fc2_kernel(const uint8_t* __restrict__ prep, const Layout L, const IdT* __restrict__ ids,
                const float* __restrict__ tw, const int M, const int k,
                const uint16_t* __restrict__ act_hi, const uint16_t* __restrict__ act_lo,
                uint16_t* __restrict__ out) {
   constexpr int SPD = FMT == kMXFP4 ? 4 : 2;
-  constexpr int ND = NB / SPD;
-  extern __shared__ float part[];  // [token][wave][lane]
+  constexpr int RG = 64 / KL;
+  constexpr int T = R / RG;
+  extern __shared__ u32x4 lds_raw[];
+  const int slots = M * k;
+  float* part = (float*)lds_raw;                           // [token][16 waves][R rows]
+  uint16_t* as = (uint16_t*)(part + M * 16 * R);           // [slot][hi | lo][I]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
-  const int hb = blockIdx.x;
-  const int h = hb * 64 + lane;
-  const int slots = M * k;
-  const Routes R = load_routes(ids, tw, slots, L.E);
-  for (int t = 0; t < M; ++t) part[(t * W + wave) * 64 + lane] = 0.0f;
+  const int p = lane % KL, g = lane / KL;
+  const int row0 = blockIdx.x * R;  // first row of H
+  const int hb = row0 / 64;
+  if (STAGE) {
+    // hi and lo planes are separate buffers of slots x I bf16 each
+    for (int i = threadIdx.x; i < slots * L.I / 8; i += blockDim.x) {
+      const int r = i / (L.I / 8), c = i % (L.I / 8);
+      ((u32x4*)(as + (int64_t)r * 2 * L.I))[c] = ((const u32x4*)(act_hi + (int64_t)r * L.I))[c];
+      ((u32x4*)(as + (int64_t)r * 2 * L.I + L.I))[c] = ((const u32x4*)(act_lo + (int64_t)r * L.I))[c];
+    }
+  }
+  const Routes R_ = load_routes(ids, tw, slots, L.E);
+  for (int i = threadIdx.x; i < M * 16 * R; i += blockDim.x) part[i] = 0.0f;
+  __syncthreads();
 
   for (int s = wave; s < slots; s += W) {
     uint64_t mask = 0;
-    const int e = slot_expert(R, s, &mask);
+    const int e = slot_expert(R_, s, &mask);
     if (e < 0) continue;
     const uint8_t* tile = prep + fc2_tile_offset(L, e, hb);
-    const uint32_t* sw = (const uint32_t*)(tile + (int64_t)L.nC2 * 1024) + lane;
+    const uint8_t* sbase = tile + (int64_t)L.nC2 * 1024;
     const float g2 = FMT == kNVFP4 ? ((const float*)prep)[L.E + e] : 1.0f;
-    for (int c0 = 0; c0 < L.nC2; c0 += NB) {
-      const int n = min(NB, L.nC2 - c0);
-      u32x4 q[NB];  // unconditional loads, as in fc1_kernel
+    for (int c0 = 0; c0 < L.nC2; c0 += KL) {
+      const int c = c0 + p;
+      const bool cv = c < L.nC2;
+      const int cc = min(c, L.nC2 - 1);
+      u32x4 q[T];
+      uint32_t sd[T];
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        q[i] = __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)min(c0 + i, L.nC2 - 1) * 1024) + lane);
-      uint32_t sd[ND];
-#pragma unroll
-      for (int i = 0; i < ND; ++i) sd[i] = __builtin_nontemporal_load(sw + 64 * min(c0 / SPD + i, L.nQ2 - 1));
+      for (int j = 0; j < T; ++j) {
+        const int row = row0 % 64 + g + RG * j;  // tile rows past H are zero padding
+        q[j] = __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)cc * 1024 + row * 16));
+        sd[j] = __builtin_nontemporal_load((const uint32_t*)(sbase + (cc / SPD) * 256 + row * 4));
+      }
       for (int t = 0; t < M; ++t) {
         uint64_t tm = token_routes(mask, t, k);
         if (!tm) continue;
@@ -217,97 +366,106 @@ __global__ void __launch_bounds__(64 * kMaxWaves2)
         while (tm) {
           const int j = __builtin_ctzll(tm);
           tm &= tm - 1;
-          wsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(R.w), t * k + j));
+          wsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(R_.w), t * k + j));
         }
-        const uint32_t* ah = (const uint32_t*)(act_hi + (int64_t)r * L.I) + 16 * c0;
-        const uint32_t* al = (const uint32_t*)(act_lo + (int64_t)r * L.I) + 16 * c0;
-        float y = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          if (i < n) {
-            bf16x2_t wv[16];
-            fp4x8_to_bf16(q[i].x, wv);
-            fp4x8_to_bf16(q[i].y, wv + 4);
-            fp4x8_to_bf16(q[i].z, wv + 8);
-            fp4x8_to_bf16(q[i].w, wv + 12);
-            const uint32_t* hc = ah + 16 * i;
-            const uint32_t* lc = al + 16 * i;
-            if (FMT == kMXFP4) {
-              float p = 0.0f;
-#pragma unroll
-              for (int j = 0; j < 16; ++j) {
-                p = __builtin_amdgcn_fdot2_f32_bf16(wv[j], as_bf16x2(hc[j]), p, false);
-                p = __builtin_amdgcn_fdot2_f32_bf16(wv[j], as_bf16x2(lc[j]), p, false);
-              }
-              y = fmaf(p, mx_scale(sd[i / 4], i), y);
-            } else {
-              float pa = 0.0f, pb = 0.0f;
-#pragma unroll
-              for (int j = 0; j < 8; ++j) {
-                pa = __builtin_amdgcn_fdot2_f32_bf16(wv[j], as_bf16x2(hc[j]), pa, false);
-                pa = __builtin_amdgcn_fdot2_f32_bf16(wv[j], as_bf16x2(lc[j]), pa, false);
-              }
-#pragma unroll
-              for (int j = 8; j < 16; ++j) {
-                pb = __builtin_amdgcn_fdot2_f32_bf16(wv[j], as_bf16x2(hc[j]), pb, false);
-                pb = __builtin_amdgcn_fdot2_f32_bf16(wv[j], as_bf16x2(lc[j]), pb, false);
-              }
-              const f32x2_t sc = e4m3x2_to_f32(sd[i / 2], (i & 1) != 0);
-              y = fmaf(pa, sc.x, y);
-              y = fmaf(pb, sc.y, y);
-            }
-          }
+        uint32_t ah[16], al[16];
+        if (STAGE) {
+          lds_chunk16(as + (int64_t)r * 2 * L.I + 32 * cc, ah);
+          lds_chunk16(as + (int64_t)r * 2 * L.I + L.I + 32 * cc, al);
+        } else {
+          load_chunk16(act_hi + (int64_t)r * L.I + 32 * cc, ah);
+          load_chunk16(act_lo + (int64_t)r * L.I + 32 * cc, al);
         }
-        part[(t * W + wave) * 64 + lane] += (y * g2) * wsum;
+        float v[T];
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+          const f32x2_t sc = chunk_scale<FMT>(sd[j], cc);
+          v[j] = cv ? unit_dot2<FMT>(q[j], ah, al, sc) : 0.0f;
+        }
+        const float y = fold_rows<KL, T>(v, p);
+        if (p < T) part[(t * 16 + wave) * R + g + RG * p] += (y * g2) * wsum;
       }
     }
   }
   __syncthreads();
-  if (h >= L.H) return;
+  const int h = row0 + lane;
+  if (lane >= R || h >= L.H) return;
   for (int t = wave; t < M; t += W) {
     float v = 0.0f;
-    for (int w = 0; w < W; ++w) v += part[(t * W + w) * 64 + lane];
+#pragma unroll
+    for (int w = 0; w < 16; ++w) v += part[(t * 16 + w) * R + lane];
     out[(int64_t)t * L.H + h] = f32_to_bf16_rne(v);
+  }
+}
+
+template <int FMT, int KL, typename IdT>
+hipError_t launch_fc1(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
+                      const IdT* ids, uint16_t* act_hi, uint16_t* act_lo, int R, hipStream_t st) {
+  const int slots = M * k;
+  const int groups = (L.nC1 + KL - 1) / KL;
+  const int waves = groups < kMaxWaves ? groups : kMaxWaves;
+  const bool big = R == 32;
+  const size_t lds = 2 * (size_t)align_up(L.H, 64) + (size_t)M * 16 * R * sizeof(float);
+  const dim3 grid((unsigned)((int64_t)slots * L.nB1 * (64 / R))), block(64 * waves);
+  if (big)
+    hipLaunchKernelGGL((fc1_kernel<FMT, KL, 32, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, act_hi, act_lo);
+  else
+    hipLaunchKernelGGL((fc1_kernel<FMT, KL, 16, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, act_hi, act_lo);
+  return hipGetLastError();
+}
+
+template <int FMT, int KL, int R, typename IdT>
+hipError_t launch_fc2_r(const Layout& L, const uint8_t* prep, int M, int k, const IdT* ids,
+                        const float* tw, const uint16_t* ah, const uint16_t* al, uint16_t* out,
+                        hipStream_t st) {
+  const int slots = M * k;
+  const int waves = slots < fc2_max_waves(KL) ? slots : fc2_max_waves(KL);
+  const size_t act_bytes = (size_t)slots * L.I * 4;
+  const size_t part_bytes = (size_t)M * 16 * R * sizeof(float);
+  const bool stage = act_bytes <= kStageActBytes && part_bytes + act_bytes <= kMaxLdsBytes;
+  const size_t lds = part_bytes + (stage ? act_bytes : 0);
+  const dim3 grid((unsigned)((L.H + R - 1) / R)), block(64 * waves);
+  if (stage)
+    hipLaunchKernelGGL((fc2_kernel<FMT, KL, R, true, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, ah, al, out);
+  else
+    hipLaunchKernelGGL((fc2_kernel<FMT, KL, R, false, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, ah, al, out);
+  return hipGetLastError();
+}
+
+template <int FMT, int KL, typename IdT>
+hipError_t launch_fc2(const Layout& L, const uint8_t* prep, int M, int k, const IdT* ids,
+                      const float* tw, const uint16_t* ah, const uint16_t* al, uint16_t* out,
+                      int R, hipStream_t st) {
+  if (R == 32) return launch_fc2_r<FMT, KL, 32, IdT>(L, prep, M, k, ids, tw, ah, al, out, st);
+  if constexpr (KL == 4) {
+    return launch_fc2_r<FMT, KL, 16, IdT>(L, prep, M, k, ids, tw, ah, al, out, st);
+  } else {
+    if (R == 16) return launch_fc2_r<FMT, KL, 16, IdT>(L, prep, M, k, ids, tw, ah, al, out, st);
+    return launch_fc2_r<FMT, KL, 8, IdT>(L, prep, M, k, ids, tw, ah, al, out, st);
   }
 }
 
 template <int FMT, typename IdT>
 hipError_t launch_decode_fmt(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                              const IdT* ids, const float* tw, uint16_t* out, uint8_t* ws,
-                             const DecodeWs& W, int cs, int phases, hipStream_t st) {
-  const int slots = M * k;
+                             const DecodeWs& W, const DecodeShape& sh, int phases, hipStream_t st) {
   uint16_t* act_hi = (uint16_t*)(ws + W.act_hi);
   uint16_t* act_lo = (uint16_t*)(ws + W.act_lo);
   if (phases & 1) {
-    const int S = (L.nC1 + cs - 1) / cs;
-    const int waves = S < kMaxWaves ? S : kMaxWaves;
-    const size_t lds = (size_t)M * waves * 64 * sizeof(float);
-    const dim3 grid((unsigned)((int64_t)slots * L.nB1)), block(64 * waves);
-    if (cs == 4)
-      hipLaunchKernelGGL((fc1_kernel<FMT, 4, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, act_hi, act_lo);
-    else if (cs == 8)
-      hipLaunchKernelGGL((fc1_kernel<FMT, 8, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, act_hi, act_lo);
+    hipError_t err;
+    if (sh.kl1 == 4)
+      err = launch_fc1<FMT, 4, IdT>(L, prep, x, M, k, ids, act_hi, act_lo, sh.r1, st);
+    else if (sh.kl1 == 8)
+      err = launch_fc1<FMT, 8, IdT>(L, prep, x, M, k, ids, act_hi, act_lo, sh.r1, st);
     else
-      hipLaunchKernelGGL((fc1_kernel<FMT, 16, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, act_hi, act_lo);
-    const hipError_t err = hipGetLastError();
+      err = launch_fc1<FMT, 16, IdT>(L, prep, x, M, k, ids, act_hi, act_lo, sh.r1, st);
     if (err != hipSuccess) return err;
   }
   if (phases & 2) {
-    const int waves = slots < kMaxWaves2 ? slots : kMaxWaves2;
-    const size_t lds = (size_t)M * waves * 64 * sizeof(float);
-    const dim3 grid(L.nB2), block(64 * waves);
-    const uint16_t* ah = act_hi;
-    const uint16_t* al = act_lo;
-    // chunk batch: the smallest of 4, 8, 12, 16 that covers I (or 16)
-    if (L.nC2 <= 4)
-      hipLaunchKernelGGL((fc2_kernel<FMT, 4, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, ah, al, out);
-    else if (L.nC2 <= 8)
-      hipLaunchKernelGGL((fc2_kernel<FMT, 8, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, ah, al, out);
-    else if (L.nC2 <= 12)
-      hipLaunchKernelGGL((fc2_kernel<FMT, 12, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, ah, al, out);
-    else
-      hipLaunchKernelGGL((fc2_kernel<FMT, 16, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, ah, al, out);
-    return hipGetLastError();
+    const int kl2 = fc2_chunk_lanes(L);
+    if (kl2 == 4) return launch_fc2<FMT, 4, IdT>(L, prep, M, k, ids, tw, act_hi, act_lo, out, sh.r2, st);
+    if (kl2 == 8) return launch_fc2<FMT, 8, IdT>(L, prep, M, k, ids, tw, act_hi, act_lo, out, sh.r2, st);
+    return launch_fc2<FMT, 16, IdT>(L, prep, M, k, ids, tw, act_hi, act_lo, out, sh.r2, st);
   }
   return hipSuccess;
 }
@@ -315,17 +473,17 @@ hipError_t launch_decode_fmt(const Layout& L, const uint8_t* prep, const uint16_
 template <typename IdT>
 hipError_t launch_decode(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                          const IdT* ids, const float* tw, uint16_t* out, uint8_t* ws,
-                         const DecodeWs& W, int cs, int phases, hipStream_t st) {
+                         const DecodeWs& W, const DecodeShape& sh, int phases, hipStream_t st) {
   if (L.fmt == kMXFP4)
-    return launch_decode_fmt<kMXFP4, IdT>(L, prep, x, M, k, ids, tw, out, ws, W, cs, phases, st);
-  return launch_decode_fmt<kNVFP4, IdT>(L, prep, x, M, k, ids, tw, out, ws, W, cs, phases, st);
+    return launch_decode_fmt<kMXFP4, IdT>(L, prep, x, M, k, ids, tw, out, ws, W, sh, phases, st);
+  return launch_decode_fmt<kNVFP4, IdT>(L, prep, x, M, k, ids, tw, out, ws, W, sh, phases, st);
 }
 
 template hipError_t launch_decode<int32_t>(const Layout&, const uint8_t*, const uint16_t*, int, int,
                                            const int32_t*, const float*, uint16_t*, uint8_t*,
-                                           const DecodeWs&, int, int, hipStream_t);
+                                           const DecodeWs&, const DecodeShape&, int, hipStream_t);
 template hipError_t launch_decode<int64_t>(const Layout&, const uint8_t*, const uint16_t*, int, int,
                                            const int64_t*, const float*, uint16_t*, uint8_t*,
-                                           const DecodeWs&, int, int, hipStream_t);
+                                           const DecodeWs&, const DecodeShape&, int, hipStream_t);
 
 }  // namespace moe

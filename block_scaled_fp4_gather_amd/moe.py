@@ -29,6 +29,12 @@ class MoeFp4Error(RuntimeError):
         self.status = status
 
 
+class Tuning(ctypes.Structure):
+    """Launch shape of the decode kernels (0 keeps the built-in choice)."""
+    _fields_ = [("fc1_chunks_per_wave", ctypes.c_int32), ("fc1_rows", ctypes.c_int32),
+                ("fc2_rows", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class _Desc(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
@@ -62,8 +68,8 @@ _SIGS = {
     "moe_fp4_workspace_bytes": ([ctypes.POINTER(_Desc), _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
     "moe_fp4_forward": ([ctypes.POINTER(_Desc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
     "moe_fp4_forward_i64": ([ctypes.POINTER(_Desc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
-    "moe_fp4_forward_tuned": ([ctypes.POINTER(_Desc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _I32, _VP], ctypes.c_int),
-    "moe_fp4_forward_phase": ([ctypes.POINTER(_Desc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _I32, _VP], ctypes.c_int),
+    "moe_fp4_forward_ex": ([ctypes.POINTER(_Desc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ,
+                            ctypes.POINTER(Tuning), _I32, _VP], ctypes.c_int),
     "moe_fp4_dequant_export": ([ctypes.POINTER(_Desc), _VP, _I32, _I32, _VP, _VP], ctypes.c_int),
 }
 
@@ -130,19 +136,19 @@ def unprepare(desc: Desc, prepared, w13_codes, w13_scales, w2_codes, w2_scales, 
         _ptr(w2_scales), _ptr(g13), _ptr(g2), _stream(stream)))
 
 
-def forward(desc: Desc, prepared, x, ids, w, out, workspace, stream=None, slab_chunks: int | None = None,
+def forward(desc: Desc, prepared, x, ids, w, out, workspace, stream=None, tuning: Tuning | None = None,
             phases: int | None = None):
-    """x bf16 [M][H], ids int32 or int64 [M][k], w fp32 [M][k], out bf16 [M][H]."""
+    """x bf16 [M][H], ids int32 or int64 [M][k], w fp32 [M][k], out bf16 [M][H].
+    `tuning` and `phases` select the measurement hook (int32 ids only)."""
     M = x.shape[0]
     ws_n = workspace.numel() * workspace.element_size()
     args = (ctypes.byref(desc.c()), _ptr(prepared), _ptr(x), M, _ptr(ids), _ptr(w), _ptr(out),
             _ptr(workspace), ws_n)
-    if phases is not None:
-        assert ids.dtype == torch.int32 and slab_chunks is None
-        _check("moe_fp4_forward_phase", lib().moe_fp4_forward_phase(*args, phases, _stream(stream)))
-    elif slab_chunks is not None:
+    if tuning is not None or phases is not None:
         assert ids.dtype == torch.int32
-        _check("moe_fp4_forward_tuned", lib().moe_fp4_forward_tuned(*args, slab_chunks, _stream(stream)))
+        tp = ctypes.byref(tuning) if tuning is not None else None
+        _check("moe_fp4_forward_ex", lib().moe_fp4_forward_ex(*args, tp, 3 if phases is None else phases,
+                                                               _stream(stream)))
     elif ids.dtype == torch.int64:
         _check("moe_fp4_forward_i64", lib().moe_fp4_forward_i64(*args, _stream(stream)))
     else:
@@ -177,8 +183,8 @@ class Fp4MoE:
         del tensors
         self.workspace = torch.empty(workspace_bytes(desc, desc.max_tokens), dtype=torch.uint8, device=dev)
 
-    def __call__(self, x, ids, w, out=None, stream=None, slab_chunks=None, phases=None):
+    def __call__(self, x, ids, w, out=None, stream=None, tuning=None, phases=None):
         if out is None:
             out = torch.empty_like(x)
-        forward(self.desc, self.prepared, x, ids, w, out, self.workspace, stream, slab_chunks, phases)
+        forward(self.desc, self.prepared, x, ids, w, out, self.workspace, stream, tuning, phases)
         return out

@@ -128,23 +128,30 @@ moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prep
                                       int32_t expert, int32_t which, float* out,
                                       void* stream);
 
-/* Tuning hook for measurements: forward with an explicit FC1 K-slab width
- * per wave in 32-element chunks (4, 8 or 16; 0 = the built-in choice). */
-moe_fp4_status moe_fp4_forward_tuned(const moe_fp4_desc* desc, const void* prepared,
-                                     const uint16_t* x, int32_t M, const int32_t* topk_ids,
-                                     const float* topk_w, uint16_t* out, void* workspace,
-                                     size_t workspace_bytes, int32_t fc1_slab_chunks,
-                                     void* stream);
+/* Launch shape of the decode kernels; 0 in a field keeps the built-in choice.
+ *   fc1_chunks_per_wave: 32-element K chunks per FC1 wave (4, 8 or 16)
+ *   fc1_rows: FC1 rows per workgroup, half gate and half up (16 or 32)
+ *   fc2_rows: FC2 rows of H per workgroup (8, 16 or 32; at least 64 divided
+ *             by FC2's chunk lanes, which is 4, 8 or 16 for I up to 128, 256
+ *             or beyond) */
+typedef struct {
+  int32_t fc1_chunks_per_wave;
+  int32_t fc1_rows;
+  int32_t fc2_rows;
+  int32_t reserved; /* must be 0 */
+} moe_fp4_tuning;
 
-/* Measurement hook: queue only part of moe_fp4_forward, so a caller can put
- * events between the FC1 and FC2 launches.  phases = 1 queues FC1 (fills the
- * workspace's activation), 2 queues FC2 (reads it and writes `out`; it must
- * follow a phase-1 call with the same arguments on the same stream), 3 queues
- * both and equals moe_fp4_forward. */
-moe_fp4_status moe_fp4_forward_phase(const moe_fp4_desc* desc, const void* prepared,
-                                     const uint16_t* x, int32_t M, const int32_t* topk_ids,
-                                     const float* topk_w, uint16_t* out, void* workspace,
-                                     size_t workspace_bytes, int32_t phases, void* stream);
+/* Measurement hook: moe_fp4_forward (int32 ids) with an explicit launch
+ * shape (`tuning` may be NULL) and only part of the call queued, so a caller
+ * can put events between the FC1 and FC2 launches: phases = 1 queues FC1
+ * (fills the workspace's activation), 2 queues FC2 (reads it and writes
+ * `out`; it must follow a phase-1 call with the same arguments on the same
+ * stream), 3 queues both. */
+moe_fp4_status moe_fp4_forward_ex(const moe_fp4_desc* desc, const void* prepared,
+                                  const uint16_t* x, int32_t M, const int32_t* topk_ids,
+                                  const float* topk_w, uint16_t* out, void* workspace,
+                                  size_t workspace_bytes, const moe_fp4_tuning* tuning,
+                                  int32_t phases, void* stream);
 
 #ifdef __cplusplus
 }

@@ -32,7 +32,7 @@ def L():
 
 def test_every_declared_symbol_is_exported(L):
     names = declared_functions()
-    assert len(names) >= 10
+    assert len(names) >= 9
     for n in names:
         assert hasattr(L, n), n
     assert set(names) >= set(moe._SIGS)
@@ -103,6 +103,19 @@ def test_prepare_rejects_mismatched_globals(L):
     dn = moe.Desc("nvfp4", 8, 256, 128, 2, 1).c()
     assert L.moe_fp4_prepare(ctypes.byref(dn), 16, 16, 16, 16, None, None, 256, n, None) == 1
     assert L.moe_fp4_prepare(ctypes.byref(d), 16, 16, 16, 16, None, None, 256, 10, None) == 3
+
+
+def test_tuning_hook_rejects_bad_shapes(L):
+    d = moe.Desc("mxfp4", 8, 256, 128, 2, 1)   # I = 128: FC2 uses 4 chunk lanes
+    def status(t, phases=3):
+        return L.moe_fp4_forward_ex(ctypes.byref(d.c()), 256, 16, 1, 4, 4, 16, 256, 1 << 30,
+                                    ctypes.byref(t) if t is not None else None, phases, None)
+    assert status(moe.Tuning(3, 0, 0, 0)) == 1      # chunks per wave not 4/8/16
+    assert status(moe.Tuning(0, 24, 0, 0)) == 1     # FC1 rows not 16/32
+    assert status(moe.Tuning(0, 0, 8, 0)) == 1      # 8 FC2 rows x 4 lanes < 64
+    assert status(moe.Tuning(0, 0, 0, 1)) == 1      # reserved must be 0
+    assert status(None, phases=0) == 1
+    assert status(None, phases=4) == 1
 
 
 def test_workspace_sizes_do_not_depend_on_m(L):

@@ -123,11 +123,17 @@ def test_forward_small_shapes(fmt, E, H, I, M, k, seed):
         d["ids"][1, 1] = d["ids"][1, 0]  # a duplicate within a token
     acc, _ = oracle.forward_f32(fmt, d)
     layer = make_layer(fmt, d, k, M)
-    for cs in (None, 4, 8, 16):
-        label = f"{fmt} E{E} H{H} I{I} M{M} k{k} slab={cs}"
-        say(f"  run {label}")
-        compare(run_layer(layer, d, slab_chunks=cs), acc, label)
+    compare(run_layer(layer, d), acc, f"{fmt} E{E} H{H} I{I} M{M} k{k}")
     compare(run_layer(layer, d, ids_dtype=torch.int64), acc, "int64 ids")
+    # every launch shape the tuning hook accepts gives a valid result
+    kl2 = 4 if I <= 128 else (8 if I <= 256 else 16)
+    for kl1 in (4, 8, 16):
+        for r1 in (16, 32):
+            for r2 in (8, 16, 32):
+                if r2 * kl2 < 64:
+                    continue
+                t = moe.Tuning(kl1, r1, r2, 0)
+                compare(run_layer(layer, d, tuning=t), acc, f"  shape kl1={kl1} r1={r1} r2={r2}")
 
 
 @pytest.mark.parametrize("name", ["tiny_mxfp4", "nvfp4_decode_e512", "nvfp4_multi_e288",
