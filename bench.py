@@ -212,6 +212,9 @@ def main():
     if wl.fmt == "nvfp4" or wl.fmt == "mxfp4":
         dom, dom_bytes, dom_us = ("fc1_kernel", b13, fc1_us) if b13 >= b2 else ("fc2_kernel", b2, fc2_us)
     dom_gbps = dom_bytes / (dom_us * 1e-6) / 1e9
+    from block_scaled_fp4_gather_amd import profsum
+    prof = profsum.lookup(dom, wl.name) if args.shape is None else None
+    traffic = prof["hbm_bytes_per_dispatch"] if prof else None
     extra = {}
     if args.extra:
         warm_us, _, _ = region(rotate=False)
@@ -270,8 +273,9 @@ def main():
         "routed_bytes": {"fc1": b13, "fc2": b2},
         "kernel_us": {"fc1": round(fc1_us, 3), "fc2": round(fc2_us, 3)},
         "roofline": {"bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": dom},
+                     "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": dom, "algorithmic_bytes": dom_bytes,
+                     "rocprof_mean_us": prof["duration_us"]["mean_us"] if prof else None},
         "cpu_baseline": cpu,
         "check": check,
     }

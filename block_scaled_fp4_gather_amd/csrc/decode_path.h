@@ -62,11 +62,7 @@ inline bool valid_shape(const Layout& L, const DecodeShape& s) {
 // Built-in choices for fields left at 0 (from sweeps on MI355X over the
 // E512/H2560/I320 NVFP4 and E256/H7168/I256 MXFP4 decode shapes).
 inline DecodeShape resolve_shape(const Layout& L, int slots, DecodeShape s) {
-  if (s.kl1 == 0) {
-    // 8 chunks per wave while K fits one workgroup of 16 waves, else 16
-    s.kl1 = (L.nC1 + 7) / 8 <= kMaxWaves ? 8 : 16;
-    if (L.nC1 <= 8) s.kl1 = 4;
-  }
+  if (s.kl1 == 0) s.kl1 = L.nC1 <= 8 ? 4 : 8;  // longer K: waves loop over chunk groups
   if (s.r1 == 0) s.r1 = (int64_t)slots * L.nB1 * 2 >= 160 ? 32 : 16;
   if (s.r2 == 0) s.r2 = fc2_chunk_lanes(L) == 4 ? 32 : 16;
   return s;
