@@ -6,6 +6,7 @@
 #include "../../include/moe_fp4.h"
 #include "decode_path.h"
 #include "layout.h"
+#include "prefill.h"
 
 using moe::Layout;
 
@@ -33,6 +34,18 @@ int decode_slots(const moe_fp4_desc* d) {
   return m * d->top_k;
 }
 
+// Routes the grouped path's workspace is sized for (desc capacity).
+int64_t prefill_routes(const moe_fp4_desc* d) {
+  return (int64_t)(d->max_tokens < 1 ? 1 : d->max_tokens) * d->top_k;
+}
+
+// Workspace layout: both paths start at offset 0 and never run in one call.
+int64_t workspace_total(const Layout& L, const moe_fp4_desc* d) {
+  const int64_t a = moe::decode_ws(L, decode_slots(d)).total;
+  const int64_t b = moe::prefill_ws(L, prefill_routes(d)).total;
+  return a > b ? a : b;
+}
+
 moe_fp4_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_FP4_OK : MOE_FP4_EHIP; }
 
 template <typename IdT>
@@ -50,15 +63,25 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
       !aligned(ids, sizeof(IdT)) || !aligned(w, 4))
     return MOE_FP4_EINVAL;
   moe::DecodeShape shape{0, 0, 0};
+  int path = MOE_FP4_PATH_AUTO;
   if (tuning) {
     shape = moe::DecodeShape{tuning->fc1_chunks_per_wave, tuning->fc1_rows, tuning->fc2_rows};
-    if (tuning->reserved != 0 || !moe::valid_shape(L, shape)) return MOE_FP4_EINVAL;
+    path = tuning->path;
+    if (path < MOE_FP4_PATH_AUTO || path > MOE_FP4_PATH_GROUPED || !moe::valid_shape(L, shape))
+      return MOE_FP4_EINVAL;
   }
   if (phases < 1 || phases > 3) return MOE_FP4_EINVAL;
+  if (prefill_routes(desc) > moe::kPrefillMaxRoutes) return MOE_FP4_EUNSUPPORTED;
   const int k = desc->top_k;
-  if (k > moe::kDecodeMaxSlots || M > moe::decode_max_tokens(k)) return MOE_FP4_EUNSUPPORTED;
+  const bool decode_ok = k <= moe::kDecodeMaxSlots && M <= moe::decode_max_tokens(k);
+  if (path == MOE_FP4_PATH_AUTO) path = decode_ok ? MOE_FP4_PATH_DECODE : MOE_FP4_PATH_GROUPED;
+  if (path == MOE_FP4_PATH_DECODE && !decode_ok) return MOE_FP4_EUNSUPPORTED;
+  if ((int64_t)ws_bytes < workspace_total(L, desc)) return MOE_FP4_EWORKSPACE;
+  if (path == MOE_FP4_PATH_GROUPED)
+    return from_hip(moe::launch_prefill<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
+                                             (uint8_t*)workspace, moe::prefill_ws(L, prefill_routes(desc)),
+                                             phases, (hipStream_t)stream));
   const moe::DecodeWs W = moe::decode_ws(L, decode_slots(desc));
-  if ((int64_t)ws_bytes < W.total) return MOE_FP4_EWORKSPACE;
   shape = moe::resolve_shape(L, M * k, shape);
   return from_hip(moe::launch_decode<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
                                           (uint8_t*)workspace, W, shape, phases, (hipStream_t)stream));
@@ -125,7 +148,8 @@ moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size
   moe_fp4_status st = desc_layout(desc, &L);
   if (st != MOE_FP4_OK) return st;
   if (!bytes || M < 0 || M > desc->max_tokens) return MOE_FP4_EINVAL;
-  *bytes = (size_t)moe::decode_ws(L, decode_slots(desc)).total;
+  if (prefill_routes(desc) > moe::kPrefillMaxRoutes) return MOE_FP4_EUNSUPPORTED;
+  *bytes = (size_t)workspace_total(L, desc);
   return MOE_FP4_OK;
 }
 

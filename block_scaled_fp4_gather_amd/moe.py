@@ -29,10 +29,14 @@ class MoeFp4Error(RuntimeError):
         self.status = status
 
 
+PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
+
+
 class Tuning(ctypes.Structure):
-    """Launch shape of the decode kernels (0 keeps the built-in choice)."""
+    """Launch shape of the decode kernels and the execution path (0 keeps the
+    built-in choice; path is PATH_AUTO, PATH_DECODE or PATH_GROUPED)."""
     _fields_ = [("fc1_chunks_per_wave", ctypes.c_int32), ("fc1_rows", ctypes.c_int32),
-                ("fc2_rows", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("fc2_rows", ctypes.c_int32), ("path", ctypes.c_int32)]
 
 
 class _Desc(ctypes.Structure):

@@ -7,7 +7,8 @@ reads one kernel-trace database (``--kernel-trace --stats``), two counter
 runs of the benchmark (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``) and the
 same two counters for the benchmark's copy probe (a device copy of 256 MiB
 each way), and writes ``profiles/<kernel>.<workload>.md`` for each layer
-kernel.  Each summary ends with a JSON block that bench.py reads back; the
+kernel (decode: fc1_kernel, fc2_kernel; grouped: fc1_gemm, fc2_gemm and the
+routing and combine kernels).  Each summary ends with a JSON block that bench.py reads back; the
 counters there are tied to a hash of the HIP sources so that a summary taken
 before a kernel change is not used after it.
 """
@@ -25,7 +26,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 256 * 1024 * 1024  # bench.py --copy-probe: bytes read and written per dispatch
-KERNELS = ("fc1_kernel", "fc2_kernel")
+KERNELS = ("fc1_kernel", "fc2_kernel", "fc1_gemm", "fc2_gemm", "route_count", "route_scatter", "combine")
 
 
 def source_hash() -> str:

@@ -100,15 +100,31 @@ moe_fp4_status moe_fp4_unprepare(const moe_fp4_desc* desc, const void* prepared,
 /* Workspace bytes for forward calls on `desc` (device scratch, 256-byte
  * aligned, caller-owned).  The size depends only on the descriptor, so one
  * workspace serves every M <= max_tokens; `M` is checked against max_tokens.
- * Its contents on entry do not matter and are overwritten. */
+ * The grouped path needs about 4I + 4H bytes per route (max_tokens * k
+ * routes).  Its contents on entry do not matter and are
+ * overwritten. */
 moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size_t* bytes);
 
 /* The layer.  x: bf16 [M][H]; topk_ids: int32 [M][k]; topk_w: fp32 [M][k]
  * (used as given, no renormalisation); out: bf16 [M][H], overwritten.  All
  * device pointers, 16-byte aligned except topk_ids (element size) and topk_w
- * (4-byte).  M may be 0 (nothing is launched).  Returns MOE_FP4_EUNSUPPORTED
- * when M * k > 64 or M > 16 until the grouped (prefill) path is present.
- * Calls that share a workspace must be ordered on one stream. */
+ * (4-byte).  M may be 0 (nothing is launched).  Calls that share a workspace
+ * must be ordered on one stream.
+ *
+ * Two execution paths, chosen by M (both compute the layer above):
+ *   decode  (M <= min(16, 64 / k)): FC1 and FC2 as streamed FP4 GEMVs, each
+ *           routed expert's weights read once per call (b12x PR #22, What);
+ *           results are bit-reproducible.
+ *   grouped (any other M): routes grouped by expert in route order, FC1 and
+ *           FC2 as grouped GEMMs on the matrix cores over bf16 operands (FP4
+ *           dequantised exactly) with fp32 accumulation, per-route fp32 rows
+ *           summed per token in route order and cast once (flashinfer #4285,
+ *           description: the prefill kernel's per-expert tiles; b12x PR #311,
+ *           commit message on the prefill fused-sum epilogue).  The SiLU
+ *           product enters FC2 as a pair of bf16 values (hi + lo, 16
+ *           significant bits), as in the decode path.  Results are
+ *           bit-reproducible.
+ * Returns MOE_FP4_EUNSUPPORTED when max_tokens * k > 2^22. */
 moe_fp4_status moe_fp4_forward(const moe_fp4_desc* desc, const void* prepared,
                                const uint16_t* x, int32_t M, const int32_t* topk_ids,
                                const float* topk_w, uint16_t* out, void* workspace,
@@ -128,25 +144,35 @@ moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prep
                                       int32_t expert, int32_t which, float* out,
                                       void* stream);
 
-/* Launch shape of the decode kernels; 0 in a field keeps the built-in choice.
+/* Execution path selector for moe_fp4_forward_ex. */
+typedef enum {
+  MOE_FP4_PATH_AUTO = 0,    /* by M, as moe_fp4_forward */
+  MOE_FP4_PATH_DECODE = 1,  /* decode path; MOE_FP4_EUNSUPPORTED when M is past its band */
+  MOE_FP4_PATH_GROUPED = 2  /* grouped path at any M */
+} moe_fp4_path;
+
+/* Launch shape of the decode kernels and the path; 0 in a field keeps the
+ * built-in choice.
  *   fc1_chunks_per_wave: 32-element K chunks per FC1 wave (4, 8 or 16)
  *   fc1_rows: FC1 rows per workgroup, half gate and half up (16 or 32)
  *   fc2_rows: FC2 rows of H per workgroup (8, 16 or 32; at least 64 divided
  *             by FC2's chunk lanes, which is 4, 8 or 16 for I up to 128, 256
- *             or beyond) */
+ *             or beyond)
+ *   path: a moe_fp4_path */
 typedef struct {
   int32_t fc1_chunks_per_wave;
   int32_t fc1_rows;
   int32_t fc2_rows;
-  int32_t reserved; /* must be 0 */
+  int32_t path;
 } moe_fp4_tuning;
 
-/* Measurement hook: moe_fp4_forward (int32 ids) with an explicit launch
- * shape (`tuning` may be NULL) and only part of the call queued, so a caller
- * can put events between the FC1 and FC2 launches: phases = 1 queues FC1
- * (fills the workspace's activation), 2 queues FC2 (reads it and writes
- * `out`; it must follow a phase-1 call with the same arguments on the same
- * stream), 3 queues both. */
+/* Measurement and test hook: moe_fp4_forward (int32 ids) with an explicit
+ * launch shape and path (`tuning` may be NULL) and only part of the call
+ * queued, so a caller can put events between the two halves: phases = 1
+ * queues the first half (decode: FC1; grouped: routing and FC1), which fills
+ * the workspace's activation; 2 queues the second half (FC2 and the combine
+ * into `out`; it must follow a phase-1 call with the same arguments on the
+ * same stream); 3 queues both. */
 moe_fp4_status moe_fp4_forward_ex(const moe_fp4_desc* desc, const void* prepared,
                                   const uint16_t* x, int32_t M, const int32_t* topk_ids,
                                   const float* topk_w, uint16_t* out, void* workspace,

@@ -89,10 +89,8 @@ def test_forward_rejects_before_launch(L):
     assert _forward_status(L, d, x=18) == 1                    # misaligned activations
     assert _forward_status(L, d, ws_bytes=1024) == 3           # workspace too small
     assert _forward_status(L, d, M=0, prepared=None) == 0      # nothing to do
-    big = moe.Desc("mxfp4", 8, 256, 128, 2, 4096)
-    assert _forward_status(L, big, M=4096) == 2                # grouped path not present
-    wide = moe.Desc("nvfp4", 512, 2560, 320, 10, 8)
-    assert _forward_status(L, wide, M=7) == 2                  # 70 route slots > 64
+    huge = moe.Desc("mxfp4", 8, 256, 128, 8, 1 << 20)
+    assert _forward_status(L, huge, M=1) == 2                  # 2^23 routes of capacity > 2^22
 
 
 def test_prepare_rejects_mismatched_globals(L):
@@ -113,17 +111,33 @@ def test_tuning_hook_rejects_bad_shapes(L):
     assert status(moe.Tuning(3, 0, 0, 0)) == 1      # chunks per wave not 4/8/16
     assert status(moe.Tuning(0, 24, 0, 0)) == 1     # FC1 rows not 16/32
     assert status(moe.Tuning(0, 0, 8, 0)) == 1      # 8 FC2 rows x 4 lanes < 64
-    assert status(moe.Tuning(0, 0, 0, 1)) == 1      # reserved must be 0
+    assert status(moe.Tuning(0, 0, 0, 3)) == 1      # no such path
+    assert status(moe.Tuning(0, 0, 0, -1)) == 1
     assert status(None, phases=0) == 1
     assert status(None, phases=4) == 1
+
+
+def test_decode_path_rejects_past_its_band(L):
+    # forcing the decode path where M * k > 64 or M > 16: unsupported, nothing launched
+    wide = moe.Desc("nvfp4", 512, 2560, 320, 10, 8)
+    t = moe.Tuning(0, 0, 0, moe.PATH_DECODE)
+    assert L.moe_fp4_forward_ex(ctypes.byref(wide.c()), 256, 16, 7, 4, 4, 16, 256, 1 << 30,
+                                ctypes.byref(t), 3, None) == 2   # 70 route slots > 64
+    many = moe.Desc("mxfp4", 8, 256, 128, 1, 32)
+    assert L.moe_fp4_forward_ex(ctypes.byref(many.c()), 256, 16, 17, 4, 4, 16, 256, 1 << 30,
+                                ctypes.byref(t), 3, None) == 2   # 17 tokens > 16
 
 
 def test_workspace_sizes_do_not_depend_on_m(L):
     d = moe.Desc("nvfp4", 288, 4096, 512, 8, 8)
     sizes = {moe.workspace_bytes(d, m) for m in (1, 2, 5, 8)}
     assert len(sizes) == 1
-    # two bf16 activation planes for every route slot the descriptor allows
-    assert sizes.pop() == 2 * 2 * 8 * 8 * 512
+    size = sizes.pop()
+    routes, H, I = 8 * 8, 4096, 512
+    # decode: two bf16 activation planes per route slot; grouped: two bf16
+    # activation rows and an fp32 output row per route, plus routing tables
+    assert size >= 2 * 2 * routes * I
+    assert routes * (4 * I + 4 * H) <= size <= routes * (4 * I + 4 * H) + 64 * 1024
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
