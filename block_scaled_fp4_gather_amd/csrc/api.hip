@@ -71,11 +71,14 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
       return MOE_FP4_EINVAL;
   }
   if (phases < 1 || phases > 3) return MOE_FP4_EINVAL;
-  if (prefill_routes(desc) > moe::kPrefillMaxRoutes) return MOE_FP4_EUNSUPPORTED;
+  if (prefill_routes(desc) > moe::kPrefillMaxRoutes ||
+      moe::prefill_max_workgroups(L, prefill_routes(desc)) >= ((int64_t)1 << 31))
+    return MOE_FP4_EUNSUPPORTED;
   const int k = desc->top_k;
   const bool decode_ok = k <= moe::kDecodeMaxSlots && M <= moe::decode_max_tokens(k);
   if (path == MOE_FP4_PATH_AUTO) path = decode_ok ? MOE_FP4_PATH_DECODE : MOE_FP4_PATH_GROUPED;
   if (path == MOE_FP4_PATH_DECODE && !decode_ok) return MOE_FP4_EUNSUPPORTED;
+  if (path == MOE_FP4_PATH_GROUPED && L.E > moe::kRouteMaxExperts) return MOE_FP4_EUNSUPPORTED;
   if ((int64_t)ws_bytes < workspace_total(L, desc)) return MOE_FP4_EWORKSPACE;
   if (path == MOE_FP4_PATH_GROUPED)
     return from_hip(moe::launch_prefill<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,

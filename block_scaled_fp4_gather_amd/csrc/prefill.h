@@ -8,7 +8,8 @@
 
 namespace moe {
 
-constexpr int kGemmBM = 128;  // routes per m-tile of the grouped GEMMs
+constexpr int kGemmBM = 128;             // routes per m-tile of the grouped GEMMs
+constexpr int kRouteMaxExperts = 8192;   // experts the grouping's LDS histogram holds
 
 // Workspace of the grouped path, byte offsets (256-byte aligned).
 struct PrefillWs {
@@ -39,6 +40,14 @@ inline PrefillWs prefill_ws(const Layout& L, int64_t routes) {
 // Largest routes (M * k) the grouped path takes: grouped-row indexes stay in
 // int32 and the workspace within 4 * (I + H) bytes per route.
 constexpr int64_t kPrefillMaxRoutes = int64_t(1) << 22;
+
+// Workgroups of the larger grouped GEMM grid for `routes` routes; the grid
+// must stay below 2^31 workgroups.
+inline int64_t prefill_max_workgroups(const Layout& L, int64_t routes) {
+  const int64_t mt = (routes + kGemmBM - 1) / kGemmBM + L.E;
+  const int64_t nb1 = (L.I + 63) / 64, nb2 = (L.H + 127) / 128;
+  return mt * (nb1 > nb2 ? nb1 : nb2) + 8;
+}
 
 // phases: bit 0 queues routing + FC1, bit 1 queues FC2 + combine (which read
 // what the first part left in the workspace).

@@ -6,9 +6,9 @@
 // large tile (flashinfer #4285, description: MoEDynamicKernel with tiles
 // smaller than 128 rows), and reduces the routed outputs into fp32 before one
 // cast (b12x #311, commit on the prefill fused-sum epilogue).  Here:
-//   route_count / route_scatter  group the valid routes by expert in route
-//                                order (deterministic), and number the
-//                                128-row m-tiles of every expert;
+//   route_build  groups the valid routes by expert in route order
+//                (deterministic) and numbers the 128-row m-tiles of every
+//                expert;
 //   fc1_gemm   x rows gathered into LDS, FP4 weight tiles dequantised to
 //              bf16 into LDS (exact: E2M1 times a UE8M0 or E4M3 block scale
 //              has at most 6 significant bits), v_mfma_f32_32x32x16_bf16 with
@@ -42,55 +42,76 @@ __device__ __forceinline__ int route_expert(const IdT* __restrict__ ids, int r, 
   return (v >= 0 && v < E) ? (int)v : -1;
 }
 
-// One wave per expert: number of valid routes holding it.
-template <typename IdT>
-__global__ void __launch_bounds__(256)
-    route_count(const IdT* __restrict__ ids, int R, int E, int* __restrict__ counts) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
-  int cnt = 0;
-  for (int base = 0; base < R; base += 64) cnt += __popcll(__ballot(route_expert(ids, base + lane, R, E) == e));
-  if (lane == 0) counts[e] = cnt;
-}
-
 __device__ __forceinline__ int wave_sum(int v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
   return v;
 }
 
-// One wave per expert: its group's start, its m-tiles' start, and the
-// grouped position of each of its routes (route order within the group).
+// One workgroup per expert e.  Every workgroup builds the histogram of
+// valid routes over all experts in LDS (so no workgroup waits for another),
+// derives e's group start and m-tile start from it, and places e's routes at
+// consecutive grouped rows in route order: each wave takes a contiguous
+// slice of the routes, counts its matches with ballots, and after a prefix
+// over the waves writes perm (grouped row -> route) and rpos (route ->
+// grouped row).  Workgroup e also writes counts[e], and the last one the
+// total m-tile count tile_start[E].
 template <typename IdT>
-__global__ void __launch_bounds__(256)
-    route_scatter(const IdT* __restrict__ ids, int R, int E, const int* __restrict__ counts,
-                  int* __restrict__ grp_start, int* __restrict__ tile_start, int* __restrict__ perm,
-                  int* __restrict__ rpos) {
-  const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (e >= E) return;
+__global__ void __launch_bounds__(1024)
+    route_build(const IdT* __restrict__ ids, int R, int E, int* __restrict__ counts,
+                int* __restrict__ grp_start, int* __restrict__ tile_start, int* __restrict__ perm,
+                int* __restrict__ rpos) {
+  __shared__ int hist[kRouteMaxExperts];
+  __shared__ int part[3][16];
+  const int e = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  for (int q = t; q < E; q += 1024) hist[q] = 0;
+  __syncthreads();
+  for (int r = t; r < R; r += 1024) {
+    const int x = route_expert(ids, r, R, E);
+    if (x >= 0) atomicAdd(&hist[x], 1);
+  }
+  __syncthreads();
   int off = 0, toff = 0;
-  for (int q = lane; q < e; q += 64) {
-    const int c = counts[q];
+  for (int q = t; q < e; q += 1024) {
+    const int c = hist[q];
     off += c;
     toff += (c + kGemmBM - 1) / kGemmBM;
   }
   off = wave_sum(off);
   toff = wave_sum(toff);
-  const int ce = counts[e];
+  // this wave's slice of the routes, in whole ballots
+  const int slice = ((R + 15) / 16 + 63) / 64 * 64;
+  const int r0 = wave * slice, r1 = min(R, r0 + slice);
+  int mine = 0;
+  for (int base = r0; base < r1; base += 64) mine += __popcll(__ballot(route_expert(ids, base + lane, r1, E) == e));
   if (lane == 0) {
-    grp_start[e] = off;
-    tile_start[e] = toff;
-    if (e == E - 1) tile_start[E] = toff + (ce + kGemmBM - 1) / kGemmBM;
+    part[0][wave] = off;
+    part[1][wave] = toff;
+    part[2][wave] = mine;
+  }
+  __syncthreads();
+  int goff = 0, gtoff = 0, pos = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    goff += part[0][w];
+    gtoff += part[1][w];
+    pos += w < wave ? part[2][w] : 0;
+  }
+  if (t == 0) {
+    const int ce = hist[e];
+    counts[e] = ce;
+    grp_start[e] = goff;
+    tile_start[e] = gtoff;
+    if (e == E - 1) tile_start[E] = gtoff + (ce + kGemmBM - 1) / kGemmBM;
   }
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  int pos = off;
-  for (int base = 0; base < R; base += 64) {
+  pos += goff;
+  for (int base = r0; base < r1; base += 64) {
     const int r = base + lane;
-    const bool mine = route_expert(ids, r, R, E) == e;
-    const uint64_t m = __ballot(mine);
-    if (mine) {
+    const bool hit = route_expert(ids, r, r1, E) == e;
+    const uint64_t m = __ballot(hit);
+    if (hit) {
       const int p = pos + __popcll(m & below);
       perm[p] = r;
       rpos[r] = p;
@@ -113,130 +134,153 @@ __device__ __forceinline__ int tile_expert(const int* __restrict__ tile_start, i
   return lo;
 }
 
-// 32 E2M1 values of one unit as bf16 with the block scale(s) applied
-// (exact), written as 4 x 16 B to LDS.
+// MFMA B fragment q (K values 8q..8q+7 of a 32-value unit) from dword q of
+// the unit's codes, with the block scale applied (exact: E2M1 times a UE8M0
+// or E4M3 scale has at most 6 significant bits).  MXFP4: v_cvt_scalef32_pk_
+// bf16_fp4 scales by the exponent of its fp32 operand, which is the UE8M0
+// byte placed in the exponent field.  NVFP4: fp32 widening, times the E4M3
+// scale of the 16-value half, rounded to bf16 (exact).
 template <int FMT>
-__device__ __forceinline__ void dequant_unit_to_lds(u32x4 q, uint32_t sword, int c, __bf16* dst) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  u32x4* d = (u32x4*)dst;
+__device__ __forceinline__ bf16x8_t b_frag(uint32_t w, float s) {
+  uint32_t o[4];
   if (FMT == kMXFP4) {
-    // v_cvt_scalef32_pk_bf16_fp4 scales by the exponent of its fp32 operand,
-    // which is the UE8M0 byte placed in the exponent field.
-    const float s = __uint_as_float(((sword >> (8 * (c & 3))) & 0xFFu) << 23);
-#pragma unroll
-    for (int dd = 0; dd < 4; ++dd) {
-      bf16x2_t p[4];
-      p[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[dd], s, 0);
-      p[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[dd], s, 1);
-      p[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[dd], s, 2);
-      p[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[dd], s, 3);
-      d[dd] = u32x4{__builtin_bit_cast(uint32_t, p[0]), __builtin_bit_cast(uint32_t, p[1]),
-                    __builtin_bit_cast(uint32_t, p[2]), __builtin_bit_cast(uint32_t, p[3])};
-    }
+    o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0));
+    o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1));
+    o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2));
+    o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3));
   } else {
-    const f32x2_t sc = e4m3x2_to_f32(sword, (c & 1) != 0);
+    f32x2_t f[4];
+    fp4x8_to_f32(w, f);
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd) {
-      const float s = dd < 2 ? sc.x : sc.y;
-      f32x2_t f[4];
-      fp4x8_to_f32(w[dd], f);
-      uint32_t o[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        bf16x2_t b;
-        b.x = (__bf16)(f[i].x * s);  // exact: at most 6 significant bits
-        b.y = (__bf16)(f[i].y * s);
-        o[i] = __builtin_bit_cast(uint32_t, b);
-      }
-      d[dd] = u32x4{o[0], o[1], o[2], o[3]};
+    for (int i = 0; i < 4; ++i) {
+      bf16x2_t b;
+      b.x = (__bf16)(f[i].x * s);
+      b.y = (__bf16)(f[i].y * s);
+      o[i] = __builtin_bit_cast(uint32_t, b);
     }
   }
+  return __builtin_bit_cast(bf16x8_t, u32x4{o[0], o[1], o[2], o[3]});
+}
+
+// Scale operand of b_frag for fragment q of unit c from the unit's scale
+// dword (MXFP4: byte c % 4 as an exponent; NVFP4: E4M3 byte 2 (c % 2) + q / 2).
+template <int FMT>
+__device__ __forceinline__ float b_scale(uint32_t sword, int c, int q) {
+  if (FMT == kMXFP4) return __uint_as_float(((sword >> (8 * (c & 3))) & 0xFFu) << 23);
+  const f32x2_t sc = e4m3x2_to_f32(sword, (c & 1) != 0);
+  return q < 2 ? sc.x : sc.y;
 }
 
 __device__ __forceinline__ bf16x8_t lds_frag(const __bf16* p) {
   return __builtin_bit_cast(bf16x8_t, *(const u32x4*)p);
 }
 
-// Grouped GEMM main loop for one 128 x 128 output tile, K in steps of 64.
-// Each thread's A row comes from `arow` (bf16, K contiguous) and, when
-// SPLIT, a second plane `arow_lo` whose products are added to the same
-// accumulators.  B rows are two 64-row prepared tiles (tile1 reads as zero
-// when !tile1_ok).  Waves form a 2 x 2 grid of 64 x 64 sub-tiles, each 2 x 2
-// MFMA 32x32x16 blocks; this wave's B rows start at bcol0.
-template <int FMT, bool SPLIT>
-__device__ __forceinline__ void gemm_main(const uint16_t* __restrict__ arow,
-                                          const uint16_t* __restrict__ arow_lo, int kmax,
-                                          const uint8_t* tile0, const uint8_t* tile1, bool tile1_ok,
-                                          int nC, __bf16 (*As)[kGemmBM][kLdsRow],
-                                          __bf16 (*Bs)[kLdsRow], f32x16_t (&acc)[2][2], int bcol0) {
+// Grouped GEMM main loop for one 128-row x 256-column output tile, K in
+// steps of 64.
+//
+// Wave w owns the 64 columns of one prepared weight tile (`btile`, read as
+// zero and skipped when !bok) and all 128 rows: 4 x 2 MFMA 32x32x16 blocks.
+// Within a step the K order of the MFMAs is permuted so that the lanes of
+// half h (lanes 32h..32h+31) take K values 32h + 8q + i in MFMA q: a lane's
+// B operand for the four MFMAs of a step is then one 16-byte unit of one
+// weight row, read straight from the prepared tile into registers two steps
+// ahead and widened there (no LDS for B; each widened fragment feeds four
+// MFMAs); its A operand for MFMA q is 16 bytes of the A row in LDS at K
+// offset 32h + 8q.
+//
+// A rows (bf16, K contiguous) come from `arow` per thread (two threads per
+// row, 32 K values each), and, for NP == 2, a second plane `plane` elements
+// further whose products are added to the same accumulators.  They are
+// double-buffered in LDS with one barrier per step.  `mact` masks the 32-row
+// MFMA blocks that hold rows of the tile.
+template <int FMT, int NP>
+__device__ __forceinline__ void gemm_main(const uint16_t* __restrict__ arow, int64_t plane, int kmax,
+                                          const uint8_t* __restrict__ btile, bool bok, int nC,
+                                          __bf16 (*As)[NP][kGemmBM][kLdsRow], f32x16_t (&acc)[4][2],
+                                          int mact) {
   constexpr int SPD = FMT == kMXFP4 ? 4 : 2;
-  constexpr int NP = SPLIT ? 2 : 1;
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int wr = wave >> 1;
-  // loader roles
-  const int ia = t >> 1, ha = t & 1;   // A: tile row, 32-element half of the step
-  const int ib = t & 127, hb = t >> 7; // B: tile row, unit of the step
-  const uint8_t* btile = ib < 64 ? tile0 : tile1;
-  const bool bok = ib < 64 || tile1_ok;
-  const int brow = ib & 63;
+  const int lane = t & 63;
+  const int ia = t >> 1, ha = t & 1;           // A loader: tile row, 32-value half of the step
+  const int n = lane & 31, h = lane >> 5;      // MFMA roles: row/column within a block, K half
   const int nsteps = (nC + 1) / 2;
+  if (!bok) mact = 0;
 
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
   u32x4 ra[NP][4];
-  u32x4 rb;
-  uint32_t rs;
-  auto load = [&](int ks) {
-    const int ka = ks * kBK + 32 * ha;
+  u32x4 rb[2][2];  // [stage][j]
+  uint32_t rs[2][2];
+  auto load_a = [&](int s) {
+    const int ka = s * kBK + 32 * ha;
     const bool aok = ka < kmax;
 #pragma unroll
     for (int pl = 0; pl < NP; ++pl) {
-      const u32x4* ap = (const u32x4*)((pl ? arow_lo : arow) + (aok ? ka : 0));
+      const u32x4* ap = (const u32x4*)(arow + pl * plane + (aok ? ka : 0));
 #pragma unroll
       for (int i = 0; i < 4; ++i) ra[pl][i] = aok ? ap[i] : u32x4{0u, 0u, 0u, 0u};
     }
-    const int c = ks * 2 + hb;
-    const bool cok = bok && c < nC;
-    const int cc = cok ? c : 0;
-    rb = cok ? __builtin_nontemporal_load((const u32x4*)(btile + (int64_t)cc * 1024 + brow * 16))
-             : u32x4{0u, 0u, 0u, 0u};
-    rs = cok ? __builtin_nontemporal_load((const uint32_t*)(btile + (int64_t)nC * 1024 + (cc / SPD) * 256 + brow * 4))
-             : 0u;
   };
-  load(0);
-  for (int ks = 0; ks < nsteps; ++ks) {
-    // stage the loaded step in LDS
+  auto load_b = [&](int s, u32x4 (&cb)[2], uint32_t (&cs)[2]) {
+    const int c = 2 * s + h;
+    const bool ok = mact != 0 && s < nsteps && c < nC;
+    const int cc = ok ? c : 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 32 * j + n;
+      cb[j] = ok ? __builtin_nontemporal_load((const u32x4*)(btile + (int64_t)cc * 1024 + row * 16))
+                 : u32x4{0u, 0u, 0u, 0u};
+      cs[j] = ok ? __builtin_nontemporal_load(
+                       (const uint32_t*)(btile + (int64_t)nC * 1024 + (cc / SPD) * 256 + row * 4))
+                 : 0u;
+    }
+  };
+  auto store_a = [&](int buf) {
 #pragma unroll
     for (int pl = 0; pl < NP; ++pl) {
-      u32x4* ad = (u32x4*)&As[pl][ia][32 * ha];
+      u32x4* ad = (u32x4*)&As[buf][pl][ia][32 * ha];
 #pragma unroll
       for (int i = 0; i < 4; ++i) ad[i] = ra[pl][i];
     }
-    dequant_unit_to_lds<FMT>(rb, rs, ks * 2 + hb, &Bs[ib][32 * hb]);
-    __syncthreads();
-    if (ks + 1 < nsteps) load(ks + 1);  // next step's loads overlap this step's MFMAs
+  };
+
+  load_a(0);
+  load_b(0, rb[0], rs[0]);
+  load_b(1, rb[1], rs[1]);
+  store_a(0);
+  __syncthreads();
+  for (int s = 0; s < nsteps; ++s) {
+    const int buf = s & 1;
+    const u32x4 cb[2] = {rb[0][0], rb[0][1]};
+    const uint32_t cs[2] = {rs[0][0], rs[0][1]};
+    rb[0][0] = rb[1][0];
+    rb[0][1] = rb[1][1];
+    rs[0][0] = rs[1][0];
+    rs[0][1] = rs[1][1];
+    load_b(s + 2, rb[1], rs[1]);        // weights two steps ahead
+    if (s + 1 < nsteps) load_a(s + 1);  // activations one step ahead
+    const int c = 2 * s + h;
 #pragma unroll
-    for (int k16 = 0; k16 < kBK / 16; ++k16) {
-      const int kk = k16 * 16 + 8 * (lane >> 5);
+    for (int q = 0; q < 4; ++q) {
       bf16x8_t bf[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = lds_frag(&Bs[bcol0 + j * 32 + (lane & 31)][kk]);
+      for (int j = 0; j < 2; ++j) bf[j] = b_frag<FMT>(cb[j][q], b_scale<FMT>(cs[j], c, q));
 #pragma unroll
       for (int pl = 0; pl < NP; ++pl) {
-        bf16x8_t af[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) af[i] = lds_frag(&As[pl][wr * 64 + i * 32 + (lane & 31)][kk]);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i) {
+          if (!((mact >> i) & 1)) continue;
+          const bf16x8_t af = lds_frag(&As[buf][pl][i * 32 + n][32 * h + 8 * q]);
 #pragma unroll
           for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
+    if (s + 1 < nsteps) store_a(buf ^ 1);
     __syncthreads();
   }
 }
@@ -244,40 +288,64 @@ __device__ __forceinline__ void gemm_main(const uint16_t* __restrict__ arow,
 // Row (within the 32x32 block) of accumulator register r of this lane.
 __device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
+// Workgroup -> (m-tile, column block).  Workgroups are dealt to the 8 XCDs
+// in turn, so consecutive ids are remapped to give each XCD a contiguous
+// range of tiles, column block fastest: the column blocks of one m-tile run
+// together on one XCD and share its A rows through that XCD's L2, and the
+// m-tiles of one expert follow each other there and share its weights.
+struct TileId {
+  int gm, nb;
+};
+__device__ __forceinline__ TileId tile_id(int nblocks) {
+  const int per = gridDim.x / 8;
+  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  return TileId{logical / nblocks, logical % nblocks};
+}
+
+// Bit i set when 32-row block i holds rows of the tile.
+__device__ __forceinline__ int active_blocks(int rows) {
+  int m = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) m |= (b * 32 < rows) << b;
+  return m;
+}
+
+// FC1 column blocks: 4 prepared tiles (128 gate + 128 up columns) each.
+__host__ __device__ inline int fc1_blocks(const Layout& L) { return (L.nB1 + 3) / 4; }
+// FC2 column blocks: 4 prepared tiles (256 output columns) each.
+__host__ __device__ inline int fc2_blocks(const Layout& L) { return (L.nB2 + 3) / 4; }
+
 template <int FMT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     fc1_gemm(const uint8_t* __restrict__ prep, const Layout L, const uint16_t* __restrict__ x, int k,
              const int* __restrict__ counts, const int* __restrict__ grp_start,
              const int* __restrict__ tile_start, const int* __restrict__ perm,
              uint16_t* __restrict__ act, int64_t plane) {
-  __shared__ __bf16 As[1][kGemmBM][kLdsRow];
-  __shared__ __bf16 Bs[128][kLdsRow];
-  const int gm = blockIdx.x;
-  if (gm >= tile_start[L.E]) return;
-  const int e = tile_expert(tile_start, L.E, gm);
-  const int m0 = (gm - tile_start[e]) * kGemmBM;
+  __shared__ __bf16 As[2][1][kGemmBM][kLdsRow];
+  const TileId id = tile_id(fc1_blocks(L));
+  if (id.gm >= tile_start[L.E]) return;
+  const int e = tile_expert(tile_start, L.E, id.gm);
+  const int m0 = (id.gm - tile_start[e]) * kGemmBM;
   const int rows = min(kGemmBM, counts[e] - m0);
   const int gs = grp_start[e] + m0;
-  const int n0 = blockIdx.y * 64;  // gate columns n0..n0+63 (prepared tiles n0/32, n0/32 + 1)
-  const int b0 = n0 / 32;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-  // A row of this thread's loader role: the token of grouped row gs + ia
-  const int ia = t >> 1;
-  const int token = perm[gs + min(ia, rows - 1)] / k;
-  f32x16_t acc[2][2];
-  // wave column wc uses prepared tile b0 + wc: its rows 0..31 are gate, 32..63 up
-  gemm_main<FMT, false>(x + (int64_t)token * L.H, nullptr, L.H, prep + fc1_tile_offset(L, e, b0),
-                 prep + fc1_tile_offset(L, e, min(b0 + 1, L.nB1 - 1)), b0 + 1 < L.nB1, L.nC1, As, Bs,
-                 acc, wc * 64);
+  // wave w computes prepared FC1 tile b: its rows 0..31 are gate columns
+  // 32b.., rows 32..63 the matching up columns
+  const int b = 4 * id.nb + wave;
+  const bool bok = b < L.nB1;
+  // A row of this thread's loader role: the token of grouped row gs + t / 2
+  const int token = perm[gs + min(t >> 1, rows - 1)] / k;
+  f32x16_t acc[4][2];
+  gemm_main<FMT, 1>(x + (int64_t)token * L.H, 0, L.H, prep + fc1_tile_offset(L, e, bok ? b : 0), bok,
+                    L.nC1, As, acc, active_blocks(rows));
+  if (!bok) return;
   const float g13 = FMT == kNVFP4 ? ((const float*)prep)[e] : 1.0f;
-  const int n = n0 + wc * 32 + (lane & 31);
-  if (n >= L.I) return;
+  const int n = 32 * b + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = wr * 64 + i * 32 + acc_row(r, lane);
+      const int row = i * 32 + acc_row(r, lane);
       if (row >= rows) continue;
       const float gate = acc[i][0][r] * g13;
       const float up = acc[i][1][r] * g13;
@@ -291,41 +359,38 @@ __global__ void __launch_bounds__(256)
 }
 
 template <int FMT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     fc2_gemm(const uint8_t* __restrict__ prep, const Layout L, const float* __restrict__ tw,
              const int* __restrict__ counts, const int* __restrict__ grp_start,
              const int* __restrict__ tile_start, const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, float* __restrict__ y) {
-  __shared__ __bf16 As[2][kGemmBM][kLdsRow];
-  __shared__ __bf16 Bs[128][kLdsRow];
+  __shared__ __bf16 As[2][2][kGemmBM][kLdsRow];
   __shared__ float wrow[kGemmBM];
-  const int gm = blockIdx.x;
-  if (gm >= tile_start[L.E]) return;
-  const int e = tile_expert(tile_start, L.E, gm);
-  const int m0 = (gm - tile_start[e]) * kGemmBM;
+  const TileId id = tile_id(fc2_blocks(L));
+  if (id.gm >= tile_start[L.E]) return;
+  const int e = tile_expert(tile_start, L.E, id.gm);
+  const int m0 = (id.gm - tile_start[e]) * kGemmBM;
   const int rows = min(kGemmBM, counts[e] - m0);
   const int gs = grp_start[e] + m0;
-  const int n0 = blockIdx.y * 128;  // output columns (rows of W2) n0..n0+127
-  const int hb0 = n0 / 64;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
+  // wave w computes prepared FC2 tile hb: output columns 64hb..64hb+63
+  const int hb = 4 * id.nb + wave;
+  const bool bok = hb < L.nB2;
   if (t < kGemmBM) wrow[t] = t < rows ? tw[perm[gs + t]] : 0.0f;
-  const int ia = t >> 1;
-  f32x16_t acc[2][2];
-  const uint16_t* arow = act + (int64_t)(gs + min(ia, rows - 1)) * L.I;
-  gemm_main<FMT, true>(arow, arow + plane, L.I, prep + fc2_tile_offset(L, e, hb0),
-                 prep + fc2_tile_offset(L, e, min(hb0 + 1, L.nB2 - 1)), hb0 + 1 < L.nB2, L.nC2, As, Bs,
-                 acc, wc * 64);
+  f32x16_t acc[4][2];
+  gemm_main<FMT, 2>(act + (int64_t)(gs + min(t >> 1, rows - 1)) * L.I, plane, L.I,
+                    prep + fc2_tile_offset(L, e, bok ? hb : 0), bok, L.nC2, As, acc, active_blocks(rows));
+  if (!bok) return;
   const float g2 = FMT == kNVFP4 ? ((const float*)prep)[L.E + e] : 1.0f;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wc * 64 + j * 32 + (lane & 31);
+    const int n = 64 * hb + j * 32 + (lane & 31);
     if (n >= L.H) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = wr * 64 + i * 32 + acc_row(r, lane);
+        const int row = i * 32 + acc_row(r, lane);
         if (row >= rows) continue;
         y[(int64_t)(gs + row) * L.H + n] = (acc[i][j][r] * g2) * wrow[row];
       }
@@ -334,24 +399,56 @@ __global__ void __launch_bounds__(256)
 }
 
 // out[t][h] = bf16(sum over valid routes j of token t, in route order, of
-// y[grouped row of (t, j)][h]); a token with no valid route gives +0.
+// y[grouped row of (t, j)][h]); a token with no valid route gives +0.  One
+// workgroup per (token, 1024 columns); the token's grouped rows go through
+// LDS, then each thread keeps 8 rows' loads in flight.  Absent or invalid
+// routes add +0, which leaves every partial sum (never -0, as the sum starts
+// at +0) unchanged, so the result equals skipping them.
 template <typename IdT>
 __global__ void __launch_bounds__(256)
     combine(const IdT* __restrict__ ids, int k, int E, int H, const int* __restrict__ rpos,
             const float* __restrict__ y, uint16_t* __restrict__ out) {
-  const int t = blockIdx.x;
-  const int h = (blockIdx.y * 256 + threadIdx.x) * 2;
-  if (h >= H) return;
-  float a0 = 0.0f, a1 = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int64_t id = (int64_t)ids[t * k + j];
-    if (id < 0 || id >= E) continue;
-    const f32x2_t v = *(const f32x2_t*)(y + (int64_t)rpos[t * k + j] * H + h);
-    a0 += v.x;
-    a1 += v.y;
+  __shared__ int rows[256];
+  const int tok = blockIdx.x;
+  const int t = threadIdx.x;
+  const int h = (blockIdx.y * 256 + t) * 4;
+  const bool on = h < H;
+  const int hh = on ? h : 0;
+  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j0 = 0; j0 < k; j0 += 256) {
+    __syncthreads();
+    if (j0 + t < k) {
+      const int64_t r = (int64_t)tok * k + j0 + t;
+      const int64_t id = (int64_t)ids[r];
+      rows[t] = (id >= 0 && id < E) ? rpos[r] : -1;
+    }
+    __syncthreads();
+    const int kc = min(256, k - j0);
+    for (int u0 = 0; u0 < kc; u0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int rr = u0 + u < kc ? rows[u0 + u] : -1;
+        v[u] = rr >= 0 ? *(const float4*)(y + (int64_t)rr * H + hh) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc.x += v[u].x;
+        acc.y += v[u].y;
+        acc.z += v[u].z;
+        acc.w += v[u].w;
+      }
+    }
   }
-  *(uint32_t*)(out + (int64_t)t * H + h) = (uint32_t)f32_to_bf16_rne(a0) | ((uint32_t)f32_to_bf16_rne(a1) << 16);
+  if (!on) return;
+  uint2 o;
+  o.x = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+  o.y = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+  *(uint2*)(out + (int64_t)tok * H + h) = o;
 }
+
+// Grid of n tiles rounded up to whole XCD rounds (tile_id needs a multiple of 8).
+inline unsigned grid8(int64_t n) { return (unsigned)((n + 7) / 8 * 8); }
 
 template <int FMT, typename IdT>
 hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
@@ -366,22 +463,20 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   uint16_t* act = (uint16_t*)(ws + W.act);
   const int64_t plane = (W.y - W.act) / 4;  // elements from the hi plane to the lo plane
   float* y = (float*)(ws + W.y);
-  const dim3 gE((L.E + 3) / 4);
   // m-tiles: at most one partial tile per expert beyond R / 128 full ones
   const unsigned mt = (unsigned)((R + kGemmBM - 1) / kGemmBM + L.E);
   if (phases & 1) {
-    hipLaunchKernelGGL((route_count<IdT>), gE, dim3(256), 0, st, ids, R, L.E, counts);
-    hipLaunchKernelGGL((route_scatter<IdT>), gE, dim3(256), 0, st, ids, R, L.E, (const int*)counts,
-                       grp_start, tile_start, perm, rpos);
-    hipLaunchKernelGGL((fc1_gemm<FMT>), dim3(mt, (L.I + 63) / 64), dim3(256), 0, st, prep, L, x, k,
+    hipLaunchKernelGGL((route_build<IdT>), dim3(L.E), dim3(1024), 0, st, ids, R, L.E, counts, grp_start,
+                       tile_start, perm, rpos);
+    hipLaunchKernelGGL((fc1_gemm<FMT>), dim3(grid8((int64_t)mt * fc1_blocks(L))), dim3(256), 0, st, prep, L, x, k,
                        (const int*)counts, (const int*)grp_start, (const int*)tile_start,
                        (const int*)perm, act, plane);
   }
   if (phases & 2) {
-    hipLaunchKernelGGL((fc2_gemm<FMT>), dim3(mt, (L.H + 127) / 128), dim3(256), 0, st, prep, L, tw,
+    hipLaunchKernelGGL((fc2_gemm<FMT>), dim3(grid8((int64_t)mt * fc2_blocks(L))), dim3(256), 0, st, prep, L, tw,
                        (const int*)counts, (const int*)grp_start, (const int*)tile_start,
                        (const int*)perm, (const uint16_t*)act, plane, y);
-    hipLaunchKernelGGL((combine<IdT>), dim3(M, (L.H + 511) / 512), dim3(256), 0, st, ids, k, L.E, L.H,
+    hipLaunchKernelGGL((combine<IdT>), dim3(M, (L.H + 1023) / 1024), dim3(256), 0, st, ids, k, L.E, L.H,
                        (const int*)rpos, (const float*)y, out);
   }
   return hipGetLastError();

@@ -26,7 +26,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 256 * 1024 * 1024  # bench.py --copy-probe: bytes read and written per dispatch
-KERNELS = ("fc1_kernel", "fc2_kernel", "fc1_gemm", "fc2_gemm", "route_count", "route_scatter", "combine")
+KERNELS = ("fc1_kernel", "fc2_kernel", "fc1_gemm", "fc2_gemm", "route_build", "combine")
 
 
 def source_hash() -> str:

@@ -124,7 +124,8 @@ moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size
  *           product enters FC2 as a pair of bf16 values (hi + lo, 16
  *           significant bits), as in the decode path.  Results are
  *           bit-reproducible.
- * Returns MOE_FP4_EUNSUPPORTED when max_tokens * k > 2^22. */
+ * Returns MOE_FP4_EUNSUPPORTED when max_tokens * k > 2^22, or when the
+ * grouped path is needed and E > 8192. */
 moe_fp4_status moe_fp4_forward(const moe_fp4_desc* desc, const void* prepared,
                                const uint16_t* x, int32_t M, const int32_t* topk_ids,
                                const float* topk_w, uint16_t* out, void* workspace,

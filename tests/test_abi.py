@@ -123,6 +123,9 @@ def test_decode_path_rejects_past_its_band(L):
     t = moe.Tuning(0, 0, 0, moe.PATH_DECODE)
     assert L.moe_fp4_forward_ex(ctypes.byref(wide.c()), 256, 16, 7, 4, 4, 16, 256, 1 << 30,
                                 ctypes.byref(t), 3, None) == 2   # 70 route slots > 64
+    # the grouped path's expert grouping holds at most 8192 experts
+    wide_e = moe.Desc("mxfp4", 9000, 64, 32, 8, 64)
+    assert _forward_status(L, wide_e, M=64) == 2
     many = moe.Desc("mxfp4", 8, 256, 128, 1, 32)
     assert L.moe_fp4_forward_ex(ctypes.byref(many.c()), 256, 16, 17, 4, 4, 16, 256, 1 << 30,
                                 ctypes.byref(t), 3, None) == 2   # 17 tokens > 16
