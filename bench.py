@@ -219,6 +219,17 @@ def main():
     fc1_us, _, _ = region(phases=1)
     fc2_us, _, _ = region(phases=2)
     log(f"[bench] fc1 only {fc1_us:.3f} us/launch, fc2 only {fc2_us:.3f} us/launch")
+    aux = {}
+    if grouped:
+        # the grouped halves also hold the routing (with FC1) and the combine
+        # (with FC2): time those alone and take them out of the GEMM figures
+        route_us, _, _ = region(phases=4)
+        comb_us, _, _ = region(phases=8)
+        aux = {"route_build": round(route_us, 3), "combine": round(comb_us, 3),
+               "fc1_half": round(fc1_us, 3), "fc2_half": round(fc2_us, 3)}
+        fc1_us, fc2_us = fc1_us - route_us, fc2_us - comb_us
+        log(f"[bench] routing {route_us:.3f} us, combine {comb_us:.3f} us; "
+            f"fc1_gemm {fc1_us:.3f} us, fc2_gemm {fc2_us:.3f} us")
 
     U, b13, b2 = routed_bytes(wl, groups[0][0].cpu().numpy())
     layer_bytes = b13 + b2
@@ -303,7 +314,7 @@ def main():
                    "M": wl.M, "top_k": wl.k, "unique_experts": U},
         "hbm_frac_layer": round(layer_bytes / (value * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "routed_bytes": {"fc1": b13, "fc2": b2},
-        "kernel_us": {"fc1": round(fc1_us, 3), "fc2": round(fc2_us, 3)},
+        "kernel_us": {"fc1": round(fc1_us, 3), "fc2": round(fc2_us, 3), **aux},
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": dom, ("algorithmic_flops" if grouped else "algorithmic_bytes"): dom_work,

@@ -70,7 +70,7 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
     if (path < MOE_FP4_PATH_AUTO || path > MOE_FP4_PATH_GROUPED || !moe::valid_shape(L, shape))
       return MOE_FP4_EINVAL;
   }
-  if (phases < 1 || phases > 3) return MOE_FP4_EINVAL;
+  if (phases != 1 && phases != 2 && phases != 3 && phases != 4 && phases != 8) return MOE_FP4_EINVAL;
   if (prefill_routes(desc) > moe::kPrefillMaxRoutes ||
       moe::prefill_max_workgroups(L, prefill_routes(desc)) >= ((int64_t)1 << 31))
     return MOE_FP4_EUNSUPPORTED;
@@ -79,6 +79,7 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
   if (path == MOE_FP4_PATH_AUTO) path = decode_ok ? MOE_FP4_PATH_DECODE : MOE_FP4_PATH_GROUPED;
   if (path == MOE_FP4_PATH_DECODE && !decode_ok) return MOE_FP4_EUNSUPPORTED;
   if (path == MOE_FP4_PATH_GROUPED && L.E > moe::kRouteMaxExperts) return MOE_FP4_EUNSUPPORTED;
+  if (path == MOE_FP4_PATH_DECODE && phases > 3) return MOE_FP4_EINVAL;
   if ((int64_t)ws_bytes < workspace_total(L, desc)) return MOE_FP4_EWORKSPACE;
   if (path == MOE_FP4_PATH_GROUPED)
     return from_hip(moe::launch_prefill<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,

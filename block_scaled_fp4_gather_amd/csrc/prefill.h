@@ -49,8 +49,9 @@ inline int64_t prefill_max_workgroups(const Layout& L, int64_t routes) {
   return mt * (nb1 > nb2 ? nb1 : nb2) + 8;
 }
 
-// phases: bit 0 queues routing + FC1, bit 1 queues FC2 + combine (which read
-// what the first part left in the workspace).
+// phases: 1 queues routing + FC1, 2 queues FC2 + combine (which read what
+// the first part left in the workspace), 3 both; 4 queues the routing alone
+// and 8 the combine alone (for timing the GEMMs apart from them).
 template <typename IdT>
 hipError_t launch_prefill(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                           const IdT* ids, const float* tw, uint16_t* out, uint8_t* ws,

@@ -32,8 +32,7 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 64;            // K elements per main-loop step (2 units)
-constexpr int kLdsRow = kBK + 8;   // bf16 per LDS row: 144 B, rotates banks by 4 per row
+constexpr int kBK = 64;  // K elements per main-loop step (2 units)
 
 template <typename IdT>
 __device__ __forceinline__ int route_expert(const IdT* __restrict__ ids, int r, int R, int E) {
@@ -175,114 +174,194 @@ __device__ __forceinline__ bf16x8_t lds_frag(const __bf16* p) {
   return __builtin_bit_cast(bf16x8_t, *(const u32x4*)p);
 }
 
-// Grouped GEMM main loop for one 128-row x 256-column output tile, K in
-// steps of 64.
-//
-// Wave w owns the 64 columns of one prepared weight tile (`btile`, read as
-// zero and skipped when !bok) and all 128 rows: 4 x 2 MFMA 32x32x16 blocks.
-// Within a step the K order of the MFMAs is permuted so that the lanes of
-// half h (lanes 32h..32h+31) take K values 32h + 8q + i in MFMA q: a lane's
-// B operand for the four MFMAs of a step is then one 16-byte unit of one
-// weight row, read straight from the prepared tile into registers two steps
-// ahead and widened there (no LDS for B; each widened fragment feeds four
-// MFMAs); its A operand for MFMA q is 16 bytes of the A row in LDS at K
-// offset 32h + 8q.
-//
-// A rows (bf16, K contiguous) come from `arow` per thread (two threads per
-// row, 32 K values each), and, for NP == 2, a second plane `plane` elements
-// further whose products are added to the same accumulators.  They are
-// double-buffered in LDS with one barrier per step.  `mact` masks the 32-row
-// MFMA blocks that hold rows of the tile.
-template <int FMT, int NP>
-__device__ __forceinline__ void gemm_main(const uint16_t* __restrict__ arow, int64_t plane, int kmax,
-                                          const uint8_t* __restrict__ btile, bool bok, int nC,
-                                          __bf16 (*As)[NP][kGemmBM][kLdsRow], f32x16_t (&acc)[4][2],
-                                          int mact) {
-  constexpr int SPD = FMT == kMXFP4 ? 4 : 2;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int ia = t >> 1, ha = t & 1;           // A loader: tile row, 32-value half of the step
-  const int n = lane & 31, h = lane >> 5;      // MFMA roles: row/column within a block, K half
-  const int nsteps = (nC + 1) / 2;
-  if (!bok) mact = 0;
+typedef __attribute__((address_space(3))) char lds_char;
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_char*)p);
+}
+
+// Direct global -> LDS copies (global_load_lds_dword[x4]): lane l's bytes at
+// `g` land at LDS byte lds + 4 * size_dwords * l.  Written as asm so that the
+// compiler does not put a wait for every copy in flight before each LDS read
+// (it cannot tell the ring slots apart); the caller waits with vm_wait.  m0,
+// which holds the LDS base, is saved and restored.  No memory clobber: a
+// copy only writes a ring slot that no LDS access of the current step
+// touches, and every read of it comes after vm_wait and a barrier, which the
+// compiler keeps in order.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  uint32_t tmp;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(tmp) : "v"(g), "s"(lds));
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  uint32_t tmp;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(tmp) : "v"(g), "s"(lds));
+}
+// Wait until at most N vector memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS of a grouped GEMM workgroup: an A ring of 2 slots x 128 rows x 128
+// bytes (64 bf16 per row, unpadded; the 16-byte chunk c of row r sits at
+// position c ^ swz(r)), and a weight ring of 3 slots x 4 waves x (2 x 1 KiB
+// codes + 2 x 256 B scales).
+constexpr int kARow = kBK * 2;                    // bytes of one A row of a step
+constexpr int kAPlane = kGemmBM * kARow;          // 16 KiB
+constexpr int kBWave = 2 * 1024 + 2 * 256;        // one wave's weights of a step
+constexpr int kBSlot = 4 * kBWave;
+constexpr int kBSlots = 3;
+constexpr int kGemmLds = 2 * kAPlane + kBSlots * kBSlot;
+
+// Position of 16-byte chunk c in row r of an A slot.
+__device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Grouped GEMM main loop for one 128-row x 256-column output tile, followed
+// by `epilogue(acc)`.  K runs over nU units of 32 values in steps of two; unit
+// u is unit u % nC of pass u / nC (FC2 makes two passes over its K, one per
+// activation plane, with the same weights).
+//
+// Wave w owns the 64 columns of one prepared weight tile (`btile`) and the
+// first 32 * NB rows: NB x 2 MFMA 32x32x16 blocks (NB = 1..4, the 32-row
+// blocks that hold rows of the tile; NB = 0 for a wave past the last weight
+// tile, which only helps stage A).  Within a step the K order of the MFMAs is
+// permuted so that the lanes of half h (lanes 32h..32h+31) take K values
+// 32h + 8q + i in MFMA q: a lane's B operand for the four MFMAs of a step is
+// then one 16-byte unit of one weight row plus its scale word, which the lane
+// itself copies into its slot of the wave's weight ring two steps ahead and
+// widens after reading it back; its A operand for MFMA q is the 16-byte chunk
+// 4h + q of its A row.
+//
+// A rows (bf16, K contiguous; pass p at `plane` elements past pass 0) are
+// copied into the A ring one step ahead: wave w copies rows 32w..32w+31,
+// eight rows (1 KiB) per copy, from `rowp[blk]` (row 32w + 8 blk + lane / 8).
+// Per step: wait until this step's copies have landed, one barrier, then
+// widen and multiply, with the copies of A for step s + 1 and of the weights
+// for step s + 2 issued between the MFMA groups (each copy occupies the
+// address unit for a while; issued between MFMAs that wait hides behind
+// them).  Copies past the last step are clamped to it (never used); with an
+// odd number of units the last step's second half (A and B both) is zeroed
+// when read.
+template <int FMT, int NB, typename Epilogue>
+__device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int64_t plane, int nU,
+                                          const uint8_t* __restrict__ btile, int nC, uint8_t* smem,
+                                          Epilogue&& epilogue) {
+  constexpr int SPD = FMT == kMXFP4 ? 4 : 2;
+  constexpr int NBA = NB > 0 ? NB : 1;
+  // copies this wave has in flight after issuing a step's: the weights of s + 2
+  constexpr int BCOPIES = NB > 0 ? 4 : 0;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int nsteps = (nU + 1) / 2;
+  const int full = nU / 2;
+  uint8_t* const aring = smem;
+  uint8_t* const bring = smem + 2 * kAPlane + wave * kBWave;
+
+  f32x16_t acc[NBA][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NBA; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-  u32x4 ra[NP][4];
-  u32x4 rb[2][2];  // [stage][j]
-  uint32_t rs[2][2];
-  auto load_a = [&](int s) {
-    const int ka = s * kBK + 32 * ha;
-    const bool aok = ka < kmax;
-#pragma unroll
-    for (int pl = 0; pl < NP; ++pl) {
-      const u32x4* ap = (const u32x4*)(arow + pl * plane + (aok ? ka : 0));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ra[pl][i] = aok ? ap[i] : u32x4{0u, 0u, 0u, 0u};
-    }
+  // this lane's A copy source chunk (per block parity) and A read position
+  const int cp_lo = (lane & 7) ^ (lane >> 3);
+  const int swz = a_swz(n);
+  // unit u (clamped to the last) -> byte offset in an A row
+  auto a_unit = [&](int u) -> int64_t {
+    u = min(u, nU - 1);
+    const int p = u >= nC ? 1 : 0;
+    return (int64_t)p * plane * 2 + (u - p * nC) * 64;
   };
-  auto load_b = [&](int s, u32x4 (&cb)[2], uint32_t (&cs)[2]) {
-    const int c = 2 * s + h;
-    const bool ok = mact != 0 && s < nsteps && c < nC;
-    const int cc = ok ? c : 0;
+  // copy of A rows block `blk` of step s into its ring slot
+  auto copy_a = [&](int s, int blk) {
+    const int sc = s < nsteps ? s : nsteps - 1;
+    const int c = cp_lo ^ (blk & 1);
+    const uint8_t* g = (const uint8_t*)rowp[blk] + a_unit(2 * sc + (c >> 2)) + (c & 3) * 16;
+    dma16(g, lds_addr(aring + (s & 1) * kAPlane + (32 * wave + 8 * blk) * kARow));
+  };
+  // chunk of this lane's weight unit in step s (clamped; within its pass)
+  auto b_chunk = [&](int s) {
+    const int u = min(2 * s + h, nU - 1);
+    return u >= nC ? u - nC : u;
+  };
+  // copy of weight half j (codes and scale word) of step s into its ring slot
+  auto copy_b = [&](int s, int j) {
+    const int cc = b_chunk(s < nsteps ? s : nsteps - 1);
+    uint8_t* slot = bring + (s % kBSlots) * kBSlot;
+    const int row = 32 * j + n;
+    dma16(btile + (int64_t)cc * 1024 + row * 16, lds_addr(slot + j * 1024));
+    dma4(btile + (int64_t)nC * 1024 + (cc / SPD) * 256 + row * 4, lds_addr(slot + 2048 + j * 256));
+  };
+  // Copies of a step, always issued in this order (vm_wait counts on it):
+  // copies 0..3 are A blocks for step s + 1, copies 4 and 5 the weight
+  // halves for step s + 2.
+  constexpr int NCOPY = NB > 0 ? 6 : 4;
+  constexpr int NGROUP = 4 * NB;                             // MFMA groups of a step
+  constexpr int NPRE = NCOPY > NGROUP ? NCOPY - NGROUP : 0;  // copies issued before them
+  auto copy = [&](int s, int ci) {
+    if (ci < 4)
+      copy_a(s + 1, ci);
+    else
+      copy_b(s + 2, ci - 4);
+  };
+  auto widen = [&](int s, bool tail, bf16x8_t (&bf)[4][2]) {
+    const uint8_t* slot = bring + (s % kBSlots) * kBSlot;
+    const int c = b_chunk(s);
+    const bool z = tail && h;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int row = 32 * j + n;
-      cb[j] = ok ? __builtin_nontemporal_load((const u32x4*)(btile + (int64_t)cc * 1024 + row * 16))
-                 : u32x4{0u, 0u, 0u, 0u};
-      cs[j] = ok ? __builtin_nontemporal_load(
-                       (const uint32_t*)(btile + (int64_t)nC * 1024 + (cc / SPD) * 256 + row * 4))
-                 : 0u;
+      const u32x4 w = *(const u32x4*)(slot + j * 1024 + lane * 16);
+      const uint32_t sw = *(const uint32_t*)(slot + 2048 + j * 256 + lane * 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bf[q][j] = z ? bf16x8_t{} : b_frag<FMT>(w[q], b_scale<FMT>(sw, c, q));
     }
   };
-  auto store_a = [&](int buf) {
+  auto mfmas = [&](int s, bool tail, const bf16x8_t (&bf)[4][2]) {
+    const uint8_t* slot = aring + (s & 1) * kAPlane;
 #pragma unroll
-    for (int pl = 0; pl < NP; ++pl) {
-      u32x4* ad = (u32x4*)&As[buf][pl][ia][32 * ha];
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ad[i] = ra[pl][i];
+      for (int i = 0; i < NB; ++i) {
+        bf16x8_t af = lds_frag((const __bf16*)(slot + (i * 32 + n) * kARow + (((4 * h + q) ^ swz) * 16)));
+        if (tail && h) af = bf16x8_t{};
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[q][j], acc[i][j], 0, 0, 0);
+        // one of this step's copies after each of the first MFMA groups
+        const int ci = NPRE + q * NB + i;
+        if (ci < NCOPY) copy(s, ci);
+      }
+    }
+  };
+  auto step = [&](int s, bool tail) {
+    vm_wait<BCOPIES>();  // this wave's copies of A(s) and B(s) have landed
+    __syncthreads();     // everyone's A(s) has; everyone is done with step s - 1
+#pragma unroll
+    for (int ci = 0; ci < NPRE; ++ci) copy(s, ci);
+    if constexpr (NB > 0) {
+      bf16x8_t bf[4][2];
+      widen(s, tail, bf);
+      mfmas(s, tail, bf);
     }
   };
 
-  load_a(0);
-  load_b(0, rb[0], rs[0]);
-  load_b(1, rb[1], rs[1]);
-  store_a(0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const u32x4 cb[2] = {rb[0][0], rb[0][1]};
-    const uint32_t cs[2] = {rs[0][0], rs[0][1]};
-    rb[0][0] = rb[1][0];
-    rb[0][1] = rb[1][1];
-    rs[0][0] = rs[1][0];
-    rs[0][1] = rs[1][1];
-    load_b(s + 2, rb[1], rs[1]);        // weights two steps ahead
-    if (s + 1 < nsteps) load_a(s + 1);  // activations one step ahead
-    const int c = 2 * s + h;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bf16x8_t bf[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = b_frag<FMT>(cb[j][q], b_scale<FMT>(cs[j], c, q));
-#pragma unroll
-      for (int pl = 0; pl < NP; ++pl) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (!((mact >> i) & 1)) continue;
-          const bf16x8_t af = lds_frag(&As[buf][pl][i * 32 + n][32 * h + 8 * q]);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[j], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-    if (s + 1 < nsteps) store_a(buf ^ 1);
-    __syncthreads();
+  for (int blk = 0; blk < 4; ++blk) copy_a(0, blk);
+  if constexpr (NB > 0) {
+    copy_b(0, 0);
+    copy_b(0, 1);
+    copy_b(1, 0);
+    copy_b(1, 1);
   }
+  for (int s = 0; s < full; ++s) step(s, false);
+  if (full < nsteps) step(full, true);
+  vm_wait<0>();      // no copy may land after the workgroup's LDS is released
+  __syncthreads();
+  if constexpr (NB > 0) epilogue(acc);
 }
 
 // Row (within the 32x32 block) of accumulator register r of this lane.
@@ -302,12 +381,23 @@ __device__ __forceinline__ TileId tile_id(int nblocks) {
   return TileId{logical / nblocks, logical % nblocks};
 }
 
-// Bit i set when 32-row block i holds rows of the tile.
-__device__ __forceinline__ int active_blocks(int rows) {
-  int m = 0;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) m |= (b * 32 < rows) << b;
-  return m;
+// gemm_main with NB = the number of 32-row blocks holding the tile's rows
+// (0 when the wave has no weight tile).  Each variant carries its own copy
+// of the epilogue, called with the NB x 2 accumulator blocks.
+template <int FMT, typename Epilogue>
+__device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp)[4], int64_t plane, int nU,
+                                          const uint8_t* __restrict__ btile, bool bok, int nC,
+                                          uint8_t* smem, Epilogue&& ep) {
+  if (!bok)
+    gemm_main<FMT, 0>(rowp, plane, nU, btile, nC, smem, ep);
+  else if (rows > 96)
+    gemm_main<FMT, 4>(rowp, plane, nU, btile, nC, smem, ep);
+  else if (rows > 64)
+    gemm_main<FMT, 3>(rowp, plane, nU, btile, nC, smem, ep);
+  else if (rows > 32)
+    gemm_main<FMT, 2>(rowp, plane, nU, btile, nC, smem, ep);
+  else
+    gemm_main<FMT, 1>(rowp, plane, nU, btile, nC, smem, ep);
 }
 
 // FC1 column blocks: 4 prepared tiles (128 gate + 128 up columns) each.
@@ -321,7 +411,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
              const int* __restrict__ counts, const int* __restrict__ grp_start,
              const int* __restrict__ tile_start, const int* __restrict__ perm,
              uint16_t* __restrict__ act, int64_t plane) {
-  __shared__ __bf16 As[2][1][kGemmBM][kLdsRow];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
   const TileId id = tile_id(fc1_blocks(L));
   if (id.gm >= tile_start[L.E]) return;
   const int e = tile_expert(tile_start, L.E, id.gm);
@@ -333,29 +423,37 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
   // 32b.., rows 32..63 the matching up columns
   const int b = 4 * id.nb + wave;
   const bool bok = b < L.nB1;
-  // A row of this thread's loader role: the token of grouped row gs + t / 2
-  const int token = perm[gs + min(t >> 1, rows - 1)] / k;
-  f32x16_t acc[4][2];
-  gemm_main<FMT, 1>(x + (int64_t)token * L.H, 0, L.H, prep + fc1_tile_offset(L, e, bok ? b : 0), bok,
-                    L.nC1, As, acc, active_blocks(rows));
-  if (!bok) return;
+  // A rows this lane copies: rows 32 wave + 8 blk + lane / 8 of the tile
+  // (grouped rows past the tile repeat its last row), each a token's x row
+  const uint16_t* rowp[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    const int r = min(32 * wave + 8 * blk + (lane >> 3), rows - 1);
+    rowp[blk] = x + (int64_t)(perm[gs + r] / k) * L.H;
+  }
   const float g13 = FMT == kNVFP4 ? ((const float*)prep)[e] : 1.0f;
   const int n = 32 * b + (lane & 31);
+  auto epilogue = [&](auto& acc) {
+    constexpr int NB = sizeof(acc) / sizeof(acc[0]);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NB; ++i) {
+      const bool whole = i * 32 + 32 <= rows;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = i * 32 + acc_row(r, lane);
-      if (row >= rows) continue;
-      const float gate = acc[i][0][r] * g13;
-      const float up = acc[i][1][r] * g13;
-      const float a = gate / (1.0f + __expf(-gate)) * up;
-      const uint16_t hi = f32_to_bf16_rne(a);
-      const int64_t o = (int64_t)(gs + row) * L.I + n;
-      act[o] = hi;
-      act[plane + o] = f32_to_bf16_rne(a - __uint_as_float((uint32_t)hi << 16));
+      for (int r = 0; r < 16; ++r) {
+        const int row = i * 32 + acc_row(r, lane);
+        if (!whole && row >= rows) continue;
+        const float gate = acc[i][0][r] * g13;
+        const float up = acc[i][1][r] * g13;
+        const float a = gate / (1.0f + __expf(-gate)) * up;
+        const uint16_t hi = f32_to_bf16_rne(a);
+        const int64_t o = (int64_t)(gs + row) * L.I + n;
+        act[o] = hi;
+        act[plane + o] = f32_to_bf16_rne(a - __uint_as_float((uint32_t)hi << 16));
+      }
     }
-  }
+  };
+  gemm_rows<FMT>(rows, rowp, 0, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, L.nC1, smem,
+                 epilogue);
 }
 
 template <int FMT>
@@ -364,7 +462,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
              const int* __restrict__ counts, const int* __restrict__ grp_start,
              const int* __restrict__ tile_start, const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, float* __restrict__ y) {
-  __shared__ __bf16 As[2][2][kGemmBM][kLdsRow];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
   __shared__ float wrow[kGemmBM];
   const TileId id = tile_id(fc2_blocks(L));
   if (id.gm >= tile_start[L.E]) return;
@@ -377,25 +475,32 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
   const int hb = 4 * id.nb + wave;
   const bool bok = hb < L.nB2;
   if (t < kGemmBM) wrow[t] = t < rows ? tw[perm[gs + t]] : 0.0f;
-  f32x16_t acc[4][2];
-  gemm_main<FMT, 2>(act + (int64_t)(gs + min(t >> 1, rows - 1)) * L.I, plane, L.I,
-                    prep + fc2_tile_offset(L, e, bok ? hb : 0), bok, L.nC2, As, acc, active_blocks(rows));
-  if (!bok) return;
   const float g2 = FMT == kNVFP4 ? ((const float*)prep)[L.E + e] : 1.0f;
+  auto epilogue = [&](auto& acc) {
+    constexpr int NB = sizeof(acc) / sizeof(acc[0]);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = 64 * hb + j * 32 + (lane & 31);
-    if (n >= L.H) continue;
+    for (int j = 0; j < 2; ++j) {
+      const int n = 64 * hb + j * 32 + (lane & 31);
+      if (n >= L.H) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < NB; ++i) {
+        const bool whole = i * 32 + 32 <= rows;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + acc_row(r, lane);
-        if (row >= rows) continue;
-        y[(int64_t)(gs + row) * L.H + n] = (acc[i][j][r] * g2) * wrow[row];
+        for (int r = 0; r < 16; ++r) {
+          const int row = i * 32 + acc_row(r, lane);
+          if (!whole && row >= rows) continue;
+          y[(int64_t)(gs + row) * L.H + n] = (acc[i][j][r] * g2) * wrow[row];
+        }
       }
     }
-  }
+  };
+  const uint16_t* rowp[4];
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk)
+    rowp[blk] = act + (int64_t)(gs + min(32 * wave + 8 * blk + (lane >> 3), rows - 1)) * L.I;
+  // two passes over K: the hi activation plane, then the lo plane
+  gemm_rows<FMT>(rows, rowp, plane, 2 * L.nC2, prep + fc2_tile_offset(L, e, bok ? hb : 0), bok, L.nC2, smem,
+                 epilogue);
 }
 
 // out[t][h] = bf16(sum over valid routes j of token t, in route order, of
@@ -465,9 +570,11 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   float* y = (float*)(ws + W.y);
   // m-tiles: at most one partial tile per expert beyond R / 128 full ones
   const unsigned mt = (unsigned)((R + kGemmBM - 1) / kGemmBM + L.E);
-  if (phases & 1) {
+  if (phases & 5) {
     hipLaunchKernelGGL((route_build<IdT>), dim3(L.E), dim3(1024), 0, st, ids, R, L.E, counts, grp_start,
                        tile_start, perm, rpos);
+  }
+  if (phases & 1) {
     hipLaunchKernelGGL((fc1_gemm<FMT>), dim3(grid8((int64_t)mt * fc1_blocks(L))), dim3(256), 0, st, prep, L, x, k,
                        (const int*)counts, (const int*)grp_start, (const int*)tile_start,
                        (const int*)perm, act, plane);
@@ -476,6 +583,8 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
     hipLaunchKernelGGL((fc2_gemm<FMT>), dim3(grid8((int64_t)mt * fc2_blocks(L))), dim3(256), 0, st, prep, L, tw,
                        (const int*)counts, (const int*)grp_start, (const int*)tile_start,
                        (const int*)perm, (const uint16_t*)act, plane, y);
+  }
+  if (phases & 10) {
     hipLaunchKernelGGL((combine<IdT>), dim3(M, (L.H + 1023) / 1024), dim3(256), 0, st, ids, k, L.E, L.H,
                        (const int*)rpos, (const float*)y, out);
   }

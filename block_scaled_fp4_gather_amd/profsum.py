@@ -9,8 +9,8 @@ same two counters for the benchmark's copy probe (a device copy of 256 MiB
 each way), and writes ``profiles/<kernel>.<workload>.md`` for each layer
 kernel (decode: fc1_kernel, fc2_kernel; grouped: fc1_gemm, fc2_gemm and the
 routing and combine kernels).  Each summary ends with a JSON block that bench.py reads back; the
-counters there are tied to a hash of the HIP sources so that a summary taken
-before a kernel change is not used after it.
+counters there are tied to a hash of the kernel's HIP sources so that a
+summary taken before a change to that kernel is not used after it.
 """
 from __future__ import annotations
 
@@ -29,10 +29,18 @@ COPY_BYTES = 256 * 1024 * 1024  # bench.py --copy-probe: bytes read and written 
 KERNELS = ("fc1_kernel", "fc2_kernel", "fc1_gemm", "fc2_gemm", "route_build", "combine")
 
 
-def source_hash() -> str:
+# HIP sources each kernel is built from: a summary stays valid while these
+# files are unchanged.
+_DECODE_SRC = ("decode_path.hip", "decode_path.h", "decode.h", "layout.h")
+_GROUPED_SRC = ("prefill.hip", "prefill.h", "decode.h", "layout.h")
+SOURCES = {"fc1_kernel": _DECODE_SRC, "fc2_kernel": _DECODE_SRC, "fc1_gemm": _GROUPED_SRC,
+           "fc2_gemm": _GROUPED_SRC, "route_build": _GROUPED_SRC, "combine": _GROUPED_SRC}
+
+
+def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(SOURCES[kernel]):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -81,14 +89,13 @@ def write(workload: str, trace_db: str, fetch_csv: str, write_csv: str, copy_fet
     ref_w = copy_reference(copy_write, "WRITE_SIZE")
     f_scale = COPY_BYTES / 1024 / ref_f  # true bytes per counted byte
     w_scale = COPY_BYTES / 1024 / ref_w
-    digest = source_hash()
     out = []
     os.makedirs(PROFILES, exist_ok=True)
     for k in KERNELS:
         if k not in stats:
             continue
         rec = {
-            "kernel": k, "workload": workload, "source_hash": digest,
+            "kernel": k, "workload": workload, "source_hash": source_hash(k),
             "duration_us": {kk: round(v, 3) for kk, v in stats[k].items() if kk != "calls"},
             "dispatches": stats[k]["calls"],
             "FETCH_SIZE_KiB": round(fetch.get(k, float("nan")), 1),
@@ -133,7 +140,7 @@ def lookup(kernel: str, workload: str) -> dict | None:
         rec = json.loads(text[text.rindex("```json") + 7:text.rindex("```")])
     except ValueError:
         return None
-    return rec if rec.get("source_hash") == source_hash() else None
+    return rec if rec.get("source_hash") == source_hash(kernel) else None
 
 
 if __name__ == "__main__":

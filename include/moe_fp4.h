@@ -173,7 +173,10 @@ typedef struct {
  * queues the first half (decode: FC1; grouped: routing and FC1), which fills
  * the workspace's activation; 2 queues the second half (FC2 and the combine
  * into `out`; it must follow a phase-1 call with the same arguments on the
- * same stream); 3 queues both. */
+ * same stream); 3 queues both.  On the grouped path, 4 queues only its
+ * routing (the grouping of the routes by expert) and 8 only its combine
+ * (which reads what a phase-2 call left), so the two GEMM launches can be
+ * timed on their own; the decode path rejects 4 and 8. */
 moe_fp4_status moe_fp4_forward_ex(const moe_fp4_desc* desc, const void* prepared,
                                   const uint16_t* x, int32_t M, const int32_t* topk_ids,
                                   const float* topk_w, uint16_t* out, void* workspace,

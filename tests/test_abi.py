@@ -114,7 +114,8 @@ def test_tuning_hook_rejects_bad_shapes(L):
     assert status(moe.Tuning(0, 0, 0, 3)) == 1      # no such path
     assert status(moe.Tuning(0, 0, 0, -1)) == 1
     assert status(None, phases=0) == 1
-    assert status(None, phases=4) == 1
+    assert status(None, phases=5) == 1
+    assert status(None, phases=4) == 1  # M = 1 takes the decode path: no routing-only phase
 
 
 def test_decode_path_rejects_past_its_band(L):

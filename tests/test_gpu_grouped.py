@@ -148,6 +148,12 @@ def test_grouped_phases_split():
     layer(x, ids, w, out=out, tuning=GROUPED, phases=2)
     torch.cuda.synchronize()
     assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), whole)
+    # routing alone and combine alone repeat their part: the result stays the same
+    out.fill_(float("nan"))
+    for ph in (4, 1, 2, 8):
+        layer(x, ids, w, out=out, tuning=GROUPED, phases=ph)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), whole)
 
 
 def test_grouped_graph_replay_with_changing_routes():
