@@ -188,27 +188,46 @@ def main():
     def call(g, phases=None):
         layer(x, g[0], g[1], out=out, tuning=tuning, phases=phases)
 
+    def graph_len(K):
+        """Steps per captured graph: K itself up to 512, else the largest
+        divisor of K in [64, 512] (so exactly K steps run), else 512 with a
+        final shorter graph for the rest."""
+        if K <= 512:
+            return K
+        for n in range(512, 63, -1):
+            if K % n == 0:
+                return n
+        return 512
+
     def region(phases=None, rotate=True):
-        """One graph holds a pass over the rotation; it is replayed until K
-        steps have run.  Returns (us per step from events, wall s per step)."""
-        # at least 64 steps per graph, so the graph launch itself is amortised
-        n = len(groups) * max(1, -(-64 // len(groups)))
-        reps = max(1, -(-K // n))
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                call(groups[i % len(groups)] if rotate else groups[0], phases)
-        g.replay()
+        """Exactly K steps as graph replays (steps cycle through the expert
+        rotation), between one event pair on the launch stream.  Returns (us
+        per step from events, wall s per step, steps)."""
+        n = graph_len(K)
+        sizes = [n] * (K // n) + ([K % n] if K % n else [])
+        graphs = {}
+        pos = 0
+        plan = []
+        for sz in sizes:
+            key = (sz, pos % len(groups))
+            if key not in graphs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(sz):
+                        call(groups[(pos + i) % len(groups)] if rotate else groups[0], phases)
+                g.replay()
+                graphs[key] = g
+            plan.append(graphs[key])
+            pos += sz
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         a.record()
-        for _ in range(reps):
+        for g in plan:
             g.replay()
         b.record()
         torch.cuda.synchronize()
-        steps = reps * n
-        return a.elapsed_time(b) * 1e3 / steps, (time.perf_counter() - t0) / steps, steps
+        return a.elapsed_time(b) * 1e3 / K, (time.perf_counter() - t0) / K, K
 
     for i in range(W):
         call(groups[i % len(groups)])

@@ -208,3 +208,37 @@ def test_prefill_workload_full_size_sampled():
     # expert load of this routing: every expert holds rows, several m-tiles each
     counts = np.bincount(d["ids"].ravel(), minlength=wl.E)
     say(f"  rows per expert: min {counts.min()} mean {counts.mean():.0f} max {counts.max()}")
+
+
+@pytest.mark.parametrize("fmt,k", [("mxfp4", 4), ("nvfp4", 8)])
+def test_band_edge_both_paths(fmt, k):
+    """At the last M of the decode band and the first past it, the automatic
+    path and the forced other path (where it exists) both match the oracle."""
+    edge = min(16, 64 // k)
+    for M in (edge, edge + 1):
+        rng = np.random.default_rng(40 + M)
+        d, _, _ = random_case(rng, fmt, 16, 512, 128, M, k)
+        d["ids"][0, 0] = -1
+        acc, _ = oracle.forward_f32(fmt, d)
+        layer = make_layer(fmt, d, k, M)
+        compare(run_layer(layer, d), acc, f"{fmt} k{k} M{M} auto")
+        compare(run_layer(layer, d, tuning=GROUPED), acc, f"{fmt} k{k} M{M} grouped")
+        if M == edge:
+            compare(run_layer(layer, d, tuning=moe.Tuning(0, 0, 0, moe.PATH_DECODE)), acc,
+                    f"{fmt} k{k} M{M} decode")
+        else:
+            with pytest.raises(moe.MoeFp4Error):
+                run_layer(layer, d, tuning=moe.Tuning(0, 0, 0, moe.PATH_DECODE))
+
+
+def test_grouped_nvfp4_decode_geometry_many_tokens():
+    """The E512/H2560/I320 NVFP4 geometry (64 of its experts) at 512 tokens,
+    top-10: E4M3 scales and globals through the grouped GEMMs, checked on a
+    sample of tokens."""
+    wl = synth.WORKLOADS["nvfp4_decode_e512"].replace(E=64, M=512)
+    d = synth.generate(wl)
+    layer = make_layer(wl.fmt, d, wl.k, wl.M)
+    got = run_layer(layer, d)
+    sample = np.array([0, 1, 100, 257, 511])
+    acc, _ = oracle.forward_f32(wl.fmt, dict(d, x=d["x"][sample], ids=d["ids"][sample], w=d["w"][sample]))
+    compare(got[sample], acc, "nvfp4 E64/H2560/I320 M512 k10 sampled")
