@@ -64,6 +64,12 @@ def lib():
         L.oracle_forward_f32.restype = i
         L.oracle_forward_f64.argtypes = common + [f64p]
         L.oracle_forward_f64.restype = i
+        L.oracle_mxfp8_quantize.argtypes = [f32p, i, i, u8p, u8p]
+        L.oracle_mxfp8_quantize.restype = i
+        L.oracle_mxfp8_value.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
+        L.oracle_mxfp8_value.restype = ctypes.c_double
+        L.oracle_forward_w4a8.argtypes = common + [i, f64p]
+        L.oracle_forward_w4a8.restype = i
         _lib = L
     return _lib
 
@@ -145,6 +151,34 @@ def forward_f64(fmt: str, d: dict) -> np.ndarray:
     rc = lib().oracle_forward_f64(*args, _p(acc, ctypes.c_double))
     if rc:
         raise ValueError("oracle_forward_f64 rejected its arguments")
+    del keep
+    return acc
+
+
+def mxfp8_quantize(v: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """MXFP8 codes [rows][cols] and UE8M0 scales [rows][cols/32] of fp32 `v`."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    rows, cols = v.shape
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    scales = np.empty((rows, cols // 32), dtype=np.uint8)
+    rc = lib().oracle_mxfp8_quantize(_p(v, ctypes.c_float), rows, cols, _p(codes, ctypes.c_uint8),
+                                     _p(scales, ctypes.c_uint8))
+    if rc:
+        raise ValueError("oracle_mxfp8_quantize rejected its arguments")
+    return codes, scales
+
+
+def mxfp8_value(code: int, scale: int) -> float:
+    return lib().oracle_mxfp8_value(code, scale)
+
+
+def forward_w4a8(fmt: str, d: dict, quant_act: bool = True) -> np.ndarray:
+    """The W4A8-MX layer (MXFP4 only) in fp64: [M][H] token sums."""
+    args, keep, M, H = _args(fmt, d)
+    acc = np.empty((M, H), dtype=np.float64)
+    rc = lib().oracle_forward_w4a8(*args, int(bool(quant_act)), _p(acc, ctypes.c_double))
+    if rc:
+        raise ValueError("oracle_forward_w4a8 rejected its arguments")
     del keep
     return acc
 

@@ -40,6 +40,21 @@
 //  * Duplicate ids within a token are separate routes.
 //  * A token with no valid route gives +0.
 //
+// The W4A8-MX variant (b12x PR #22, Measured table and the sentence on the
+// dynamic path: MXFP4 weights with activations quantised to MXFP8, cos
+// 0.9990 against an fp32 reference; flashinfer #4285 review of the direct
+// micro kernel: one E8M0 scale per 32 K values of the activation):
+//  * MXFP8 follows the OCP MX definition: per 32 consecutive values, shared
+//    exponent floor(log2(max |v|)) - 8 (8 = exponent of E4M3's largest
+//    power of two), clamped to [-127, 127]; every value divided by 2^shared
+//    and rounded to nearest-even E4M3, magnitudes above 448 set to 448.
+//    A block of zeros (max 0) gets scale byte 0; a block holding a NaN or an
+//    infinity gets scale byte 255 (NaN) and every element code 0x7F.
+//  * x is quantised per token along H; SiLU(gate) * up per route along I,
+//    after FC1's outputs and the product are rounded to fp32 (the fp32
+//    intermediate of the pages), so the codes are decided from fp32 values.
+//  * Only MXFP4 weights (the scaled products take E8M0 scales).
+//
 // Build: g++ -O2 -ffp-contract=off -shared -fPIC (no fast-math, no FMA
 // contraction, so every product and sum is one IEEE fp32 rounding in the
 // order written).
@@ -113,6 +128,63 @@ bool valid_args(int fmt, int E, int H, int I, int M, int k) {
   if (fmt != FMT_MXFP4 && fmt != FMT_NVFP4) return false;
   const int G = block_size(fmt);
   return E > 0 && H > 0 && I > 0 && M >= 0 && k > 0 && H % G == 0 && I % G == 0;
+}
+
+// E4M3 code nearest to v (ties to even code), magnitude capped at 448,
+// NaN -> 0x7F.  Works on the value, not its bits: finds the binade, rounds
+// the scaled significand, then re-encodes.
+uint8_t e4m3_encode(double v) {
+  if (std::isnan(v)) return 0x7F;
+  const uint8_t sign = std::signbit(v) ? 0x80 : 0x00;
+  double a = std::fabs(v);
+  if (a > 448.0) a = 448.0;
+  int e = 0;
+  double m = 0.0;  // significand times 8, an integer after rounding
+  if (a >= std::ldexp(1.0, -6)) {
+    std::frexp(a, &e);  // a = f * 2^e, f in [0.5, 1)
+    e -= 1;             // floor(log2(a))
+    m = std::nearbyint(std::ldexp(a, 3 - e));  // in [8, 16]
+    if (m == 16.0) {
+      m = 8.0;
+      e += 1;
+    }
+    if (e > 8 || (e == 8 && m > 14.0)) {  // above 448 after rounding
+      e = 8;
+      m = 14.0;
+    }
+    return (uint8_t)(sign | (uint8_t)((e + 7) << 3) | (uint8_t)(m - 8.0));
+  }
+  m = std::nearbyint(std::ldexp(a, 9));  // subnormal steps of 2^-9, 0..8
+  if (m == 8.0) return (uint8_t)(sign | 0x08);  // rounds up to the smallest normal
+  return (uint8_t)(sign | (uint8_t)m);
+}
+
+// One MXFP8 block of 32 values: codes[32] and the scale byte.
+uint8_t mxfp8_block(const float* v, uint8_t* codes) {
+  double amax = 0.0;
+  bool special = false;
+  for (int i = 0; i < 32; ++i) {
+    if (!std::isfinite(v[i])) special = true;
+    else if (std::fabs((double)v[i]) > amax) amax = std::fabs((double)v[i]);
+  }
+  if (special) {
+    for (int i = 0; i < 32; ++i) codes[i] = 0x7F;
+    return 255;
+  }
+  int shared = -127;
+  if (amax > 0.0) {
+    int e = 0;
+    std::frexp(amax, &e);  // floor(log2(amax)) = e - 1
+    shared = e - 1 - 8;
+  }
+  if (shared < -127) shared = -127;
+  if (shared > 127) shared = 127;
+  for (int i = 0; i < 32; ++i) codes[i] = e4m3_encode(std::ldexp((double)v[i], -shared));
+  return (uint8_t)(shared + 127);
+}
+
+double mxfp8_value(uint8_t code, uint8_t scale) {
+  return (double)e4m3fn(code) * (double)ue8m0(scale);
 }
 
 }  // namespace
@@ -220,6 +292,78 @@ int oracle_forward_f64(int fmt, int E, int H, int I, int M, int k, const uint8_t
         double y = 0.0;
         for (int n = 0; n < I; ++n)
           y += a[n] * weight(fmt, w2_codes + e * w2_cb, w2_scales + e * w2_sb, gl2, I, h, n);
+        acc_out[(size_t)t * H + h] += (double)topk_w[(size_t)t * k + j] * y;
+      }
+    }
+  }
+  return 0;
+}
+
+// MXFP8 quantisation of a [rows][cols] fp32 matrix (cols a multiple of 32):
+// codes [rows][cols], scales [rows][cols / 32].
+int oracle_mxfp8_quantize(const float* v, int rows, int cols, uint8_t* codes, uint8_t* scales) {
+  if (rows < 0 || cols <= 0 || cols % 32) return 1;
+  for (int r = 0; r < rows; ++r)
+    for (int b = 0; b < cols / 32; ++b)
+      scales[(size_t)r * (cols / 32) + b] =
+          mxfp8_block(v + (size_t)r * cols + 32 * b, codes + (size_t)r * cols + 32 * b);
+  return 0;
+}
+
+// Value of an MXFP8 element (E4M3 code times its UE8M0 scale), in fp64.
+double oracle_mxfp8_value(uint32_t code, uint32_t scale) {
+  return mxfp8_value((uint8_t)code, (uint8_t)scale);
+}
+
+// The W4A8-MX layer (MXFP4 weights only): x quantised to MXFP8 per token,
+// FC1 dot products in fp64 then rounded to fp32, a = SiLU(gate) * up rounded
+// to fp32, then (quant_act != 0) quantised to MXFP8 per route in blocks of 32
+// along I, FC2 and the router-weighted sum in fp64.  quant_act = 0 feeds the
+// fp32 a to FC2 unquantised (used to check the rest of the chain).
+int oracle_forward_w4a8(int fmt, int E, int H, int I, int M, int k, const uint8_t* w13_codes,
+                        const uint8_t* w13_scales, const uint8_t* w2_codes,
+                        const uint8_t* w2_scales, const float* g13, const float* g2,
+                        const uint16_t* x, const int64_t* ids, const float* topk_w,
+                        int quant_act, double* acc_out) {
+  (void)g13;
+  (void)g2;
+  if (fmt != FMT_MXFP4 || !valid_args(fmt, E, H, I, M, k)) return 1;
+  const size_t w13_cb = (size_t)2 * I * (H / 2), w13_sb = (size_t)2 * I * (H / 32);
+  const size_t w2_cb = (size_t)H * (I / 2), w2_sb = (size_t)H * (I / 32);
+  std::vector<float> xf(H), af(I);
+  std::vector<uint8_t> xc(H), ac(I), xs(H / 32), as(I / 32);
+  std::vector<double> xq(H), aq(I);
+  for (int t = 0; t < M; ++t) {
+    for (int h = 0; h < H; ++h) xf[h] = bf16_to_f32(x[(size_t)t * H + h]);
+    oracle_mxfp8_quantize(xf.data(), 1, H, xc.data(), xs.data());
+    for (int h = 0; h < H; ++h) xq[h] = mxfp8_value(xc[h], xs[h / 32]);
+    for (int h = 0; h < H; ++h) acc_out[(size_t)t * H + h] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      const int64_t id = ids[(size_t)t * k + j];
+      if (id < 0 || id >= E) continue;
+      const int e = (int)id;
+      const uint8_t* c13 = w13_codes + (size_t)e * w13_cb;
+      const uint8_t* s13 = w13_scales + (size_t)e * w13_sb;
+      for (int n = 0; n < I; ++n) {
+        double gate = 0.0, up = 0.0;
+        for (int h = 0; h < H; ++h) {
+          gate += xq[h] * weight(fmt, c13, s13, 1.0f, H, n, h);
+          up += xq[h] * weight(fmt, c13, s13, 1.0f, H, I + n, h);
+        }
+        const double g = (float)gate, u = (float)up;
+        af[n] = (float)(g / (1.0 + std::exp(-g)) * u);
+      }
+      if (quant_act) {
+        oracle_mxfp8_quantize(af.data(), 1, I, ac.data(), as.data());
+        for (int n = 0; n < I; ++n) aq[n] = mxfp8_value(ac[n], as[n / 32]);
+      } else {
+        for (int n = 0; n < I; ++n) aq[n] = af[n];
+      }
+      const uint8_t* c2 = w2_codes + (size_t)e * w2_cb;
+      const uint8_t* s2 = w2_scales + (size_t)e * w2_sb;
+      for (int h = 0; h < H; ++h) {
+        double y = 0.0;
+        for (int n = 0; n < I; ++n) y += aq[n] * weight(fmt, c2, s2, 1.0f, I, h, n);
         acc_out[(size_t)t * H + h] += (double)topk_w[(size_t)t * k + j] * y;
       }
     }
