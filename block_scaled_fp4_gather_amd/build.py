@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_fp4.so")
-SOURCES = ["api.hip", "prepare.hip", "decode_path.hip", "prefill.hip"]
+SOURCES = ["api.hip", "prepare.hip", "decode_path.hip", "prefill.hip", "prefill_a8.hip", "mxfp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -6,6 +6,7 @@
 #include "../../include/moe_fp4.h"
 #include "decode_path.h"
 #include "layout.h"
+#include "mxfp8.h"
 #include "prefill.h"
 
 using moe::Layout;
@@ -23,6 +24,8 @@ moe_fp4_status desc_layout(const moe_fp4_desc* d, Layout* L) {
   if (d->hidden % G || d->inter % G) return MOE_FP4_EINVAL;  // not whole scale blocks
   if (d->hidden % 32 || d->inter % 32) return MOE_FP4_EUNSUPPORTED;
   if ((int64_t)d->hidden * d->inter > (int64_t)1 << 30) return MOE_FP4_EUNSUPPORTED;
+  if (d->act_format != MOE_FP4_ACT_BF16 && d->act_format != MOE_FP4_ACT_MXFP8) return MOE_FP4_EINVAL;
+  if (d->act_format == MOE_FP4_ACT_MXFP8 && d->format != MOE_FP4_MXFP4) return MOE_FP4_EUNSUPPORTED;
   if (!moe::make_layout(d->format, d->num_experts, d->hidden, d->inter, L)) return MOE_FP4_EINVAL;
   return MOE_FP4_OK;
 }
@@ -39,10 +42,19 @@ int64_t prefill_routes(const moe_fp4_desc* d) {
   return (int64_t)(d->max_tokens < 1 ? 1 : d->max_tokens) * d->top_k;
 }
 
+bool act_mxfp8(const moe_fp4_desc* d) { return d->act_format == MOE_FP4_ACT_MXFP8; }
+
+// Tokens the grouped path's workspace is sized for.
+int64_t prefill_tokens(const moe_fp4_desc* d) { return d->max_tokens < 1 ? 1 : d->max_tokens; }
+
+moe::PrefillWs prefill_layout(const Layout& L, const moe_fp4_desc* d) {
+  return moe::prefill_ws(L, prefill_routes(d), prefill_tokens(d), act_mxfp8(d));
+}
+
 // Workspace layout: both paths start at offset 0 and never run in one call.
 int64_t workspace_total(const Layout& L, const moe_fp4_desc* d) {
   const int64_t a = moe::decode_ws(L, decode_slots(d)).total;
-  const int64_t b = moe::prefill_ws(L, prefill_routes(d)).total;
+  const int64_t b = prefill_layout(L, d).total;
   return a > b ? a : b;
 }
 
@@ -83,8 +95,8 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
   if ((int64_t)ws_bytes < workspace_total(L, desc)) return MOE_FP4_EWORKSPACE;
   if (path == MOE_FP4_PATH_GROUPED)
     return from_hip(moe::launch_prefill<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
-                                             (uint8_t*)workspace, moe::prefill_ws(L, prefill_routes(desc)),
-                                             phases, (hipStream_t)stream));
+                                             (uint8_t*)workspace, prefill_layout(L, desc), phases,
+                                             act_mxfp8(desc), (hipStream_t)stream));
   const moe::DecodeWs W = moe::decode_ws(L, decode_slots(desc));
   shape = moe::resolve_shape(L, M * k, shape);
   return from_hip(moe::launch_decode<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
@@ -192,6 +204,15 @@ moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prep
   if (!aligned(prepared, 256) || !aligned(out, 4)) return MOE_FP4_EINVAL;
   return from_hip(moe::launch_export(L, expert, which, (const uint8_t*)prepared, out,
                                      (hipStream_t)stream));
+}
+
+moe_fp4_status moe_fp4_mxfp8_quantize(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* codes,
+                                      uint8_t* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32) return MOE_FP4_EINVAL;
+  if (rows == 0) return MOE_FP4_OK;
+  if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 8)) return MOE_FP4_EINVAL;
+  if (rows > ((int64_t)1 << 40) / cols) return MOE_FP4_EUNSUPPORTED;
+  return from_hip(launch_mxfp8_quantize(x, rows, cols, codes, scales, cols / 32, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -18,28 +18,56 @@ struct PrefillWs {
   int64_t tile_start;  // int32 [E+1] first m-tile of each expert; [E] = total tiles
   int64_t perm;        // int32 [R]   grouped row -> route index t*k + j
   int64_t rpos;        // int32 [R]   route index -> grouped row (valid routes)
+  // bf16 activations:
   int64_t act;         // bf16 [2][R][I] SiLU(gate)*up per grouped row: hi plane, then
                        // lo plane (hi = bf16(a), lo = bf16(a - hi): 16 significant bits)
+  // MXFP8 activations (W4A8-MX; scale rows padded to whole dwords):
+  int64_t xq;          // u8 [M][H]  x codes per token
+  int64_t xs;          // u8 [M][a8_scale_stride(H)]  x scales
+  int64_t aq;          // u8 [R][I]  SiLU(gate)*up codes per grouped row
+  int64_t as;          // u8 [R][a8_scale_stride(I)]  their scales
   int64_t y;           // fp32 [R][H] router-weighted FC2 output per grouped row
   int64_t total;
 };
 
-inline PrefillWs prefill_ws(const Layout& L, int64_t routes) {
+// Bytes of one MXFP8 scale row of n values: n / 32 scales rounded up to
+// whole dwords (the A8 GEMMs copy 4 unit scales at a time).
+__host__ __device__ inline int a8_scale_stride(int n) { return (n / 32 + 3) / 4 * 4; }
+
+// Workspace of the grouped path for `routes` routes of `tokens` tokens;
+// `a8` lays out the MXFP8-activation buffers instead of the bf16 planes.
+inline PrefillWs prefill_ws(const Layout& L, int64_t routes, int64_t tokens, bool a8) {
   PrefillWs w;
   w.counts = 0;
   w.grp_start = align_up(4 * (int64_t)L.E, 256);
   w.tile_start = w.grp_start + align_up(4 * (int64_t)L.E, 256);
   w.perm = w.tile_start + align_up(4 * ((int64_t)L.E + 1), 256);
   w.rpos = w.perm + align_up(4 * routes, 256);
-  w.act = w.rpos + align_up(4 * routes, 256);
-  w.y = w.act + 2 * align_up(2 * routes * L.I, 256);
+  int64_t o = w.rpos + align_up(4 * routes, 256);
+  w.act = w.xq = w.xs = w.aq = w.as = o;
+  if (a8) {
+    w.xq = o;
+    w.xs = w.xq + align_up(tokens * L.H, 256);
+    w.aq = w.xs + align_up(tokens * a8_scale_stride(L.H), 256);
+    w.as = w.aq + align_up(routes * L.I, 256);
+    o = w.as + align_up(routes * a8_scale_stride(L.I), 256);
+  } else {
+    o = w.act + 2 * align_up(2 * routes * L.I, 256);
+  }
+  w.y = o;
   w.total = w.y + align_up(4 * routes * L.H, 256);
   return w;
 }
 
 // Largest routes (M * k) the grouped path takes: grouped-row indexes stay in
-// int32 and the workspace within 4 * (I + H) bytes per route.
+// int32 and the workspace within 4 * (I + H) bytes per route (bf16
+// activations; less with MXFP8 activations, plus H + H / 32 per token).
 constexpr int64_t kPrefillMaxRoutes = int64_t(1) << 22;
+
+// FC1 column blocks: 4 prepared tiles (128 gate + 128 up columns) each.
+__host__ __device__ inline int fc1_blocks(const Layout& L) { return (L.nB1 + 3) / 4; }
+// FC2 column blocks: 4 prepared tiles (256 output columns) each.
+__host__ __device__ inline int fc2_blocks(const Layout& L) { return (L.nB2 + 3) / 4; }
 
 // Workgroups of the larger grouped GEMM grid for `routes` routes; the grid
 // must stay below 2^31 workgroups.
@@ -51,10 +79,19 @@ inline int64_t prefill_max_workgroups(const Layout& L, int64_t routes) {
 
 // phases: 1 queues routing + FC1, 2 queues FC2 + combine (which read what
 // the first part left in the workspace), 3 both; 4 queues the routing alone
-// and 8 the combine alone (for timing the GEMMs apart from them).
+// and 8 the combine alone (for timing the GEMMs apart from them).  `a8`
+// selects MXFP8 activations (MXFP4 weights only): x is quantised in phase 1
+// and both GEMMs run on the scaled matrix instruction.
 template <typename IdT>
 hipError_t launch_prefill(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                           const IdT* ids, const float* tw, uint16_t* out, uint8_t* ws,
-                          const PrefillWs& W, int phases, hipStream_t st);
+                          const PrefillWs& W, int phases, bool a8, hipStream_t st);
+
+// The A8 GEMM launches (x quantisation + FC1, FC2) over a grid of `grid`
+// workgroups (the same tile grids as the bf16 GEMMs).
+hipError_t launch_fc1_a8(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k, uint8_t* ws,
+                         const PrefillWs& W, unsigned grid, hipStream_t st);
+hipError_t launch_fc2_a8(const Layout& L, const uint8_t* prep, const float* tw, uint8_t* ws, const PrefillWs& W,
+                         unsigned grid, hipStream_t st);
 
 }  // namespace moe

@@ -24,13 +24,11 @@
 #include <hip/hip_runtime.h>
 
 #include "decode.h"
+#include "gemm_util.h"
 #include "layout.h"
 #include "prefill.h"
 
 namespace moe {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBK = 64;  // K elements per main-loop step (2 units)
 
@@ -119,20 +117,6 @@ __global__ void __launch_bounds__(1024)
   }
 }
 
-// Expert of grouped m-tile gm (tile_start is non-decreasing; the expert is
-// the last e with tile_start[e] <= gm).
-__device__ __forceinline__ int tile_expert(const int* __restrict__ tile_start, int E, int gm) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (tile_start[mid] <= gm)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
 // MFMA B fragment q (K values 8q..8q+7 of a 32-value unit) from dword q of
 // the unit's codes, with the block scale applied (exact: E2M1 times a UE8M0
 // or E4M3 scale has at most 6 significant bits).  MXFP4: v_cvt_scalef32_pk_
@@ -174,37 +158,6 @@ __device__ __forceinline__ bf16x8_t lds_frag(const __bf16* p) {
   return __builtin_bit_cast(bf16x8_t, *(const u32x4*)p);
 }
 
-typedef __attribute__((address_space(3))) char lds_char;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_char*)p);
-}
-
-// Direct global -> LDS copies (global_load_lds_dword[x4]): lane l's bytes at
-// `g` land at LDS byte lds + 4 * size_dwords * l.  Written as asm so that the
-// compiler does not put a wait for every copy in flight before each LDS read
-// (it cannot tell the ring slots apart); the caller waits with vm_wait.  m0,
-// which holds the LDS base, is saved and restored.  No memory clobber: a
-// copy only writes a ring slot that no LDS access of the current step
-// touches, and every read of it comes after vm_wait and a barrier, which the
-// compiler keeps in order.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  uint32_t tmp;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(tmp) : "v"(g), "s"(lds));
-}
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  uint32_t tmp;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(tmp) : "v"(g), "s"(lds));
-}
-// Wait until at most N vector memory operations of this wave are in flight.
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // LDS of a grouped GEMM workgroup: an A ring of 2 slots x 128 rows x 128
 // bytes (64 bf16 per row, unpadded; the 16-byte chunk c of row r sits at
 // position c ^ swz(r)), and a weight ring of 3 slots x 4 waves x (2 x 1 KiB
@@ -215,9 +168,6 @@ constexpr int kBWave = 2 * 1024 + 2 * 256;        // one wave's weights of a ste
 constexpr int kBSlot = 4 * kBWave;
 constexpr int kBSlots = 3;
 constexpr int kGemmLds = 2 * kAPlane + kBSlots * kBSlot;
-
-// Position of 16-byte chunk c in row r of an A slot.
-__device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // Grouped GEMM main loop for one 128-row x 256-column output tile, followed
 // by `epilogue(acc)`.  K runs over nU units of 32 values in steps of two; unit
@@ -364,23 +314,6 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
   if constexpr (NB > 0) epilogue(acc);
 }
 
-// Row (within the 32x32 block) of accumulator register r of this lane.
-__device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
-
-// Workgroup -> (m-tile, column block).  Workgroups are dealt to the 8 XCDs
-// in turn, so consecutive ids are remapped to give each XCD a contiguous
-// range of tiles, column block fastest: the column blocks of one m-tile run
-// together on one XCD and share its A rows through that XCD's L2, and the
-// m-tiles of one expert follow each other there and share its weights.
-struct TileId {
-  int gm, nb;
-};
-__device__ __forceinline__ TileId tile_id(int nblocks) {
-  const int per = gridDim.x / 8;
-  const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  return TileId{logical / nblocks, logical % nblocks};
-}
-
 // gemm_main with NB = the number of 32-row blocks holding the tile's rows
 // (0 when the wave has no weight tile).  Each variant carries its own copy
 // of the epilogue, called with the NB x 2 accumulator blocks.
@@ -399,11 +332,6 @@ __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp
   else
     gemm_main<FMT, 1>(rowp, plane, nU, btile, nC, smem, ep);
 }
-
-// FC1 column blocks: 4 prepared tiles (128 gate + 128 up columns) each.
-__host__ __device__ inline int fc1_blocks(const Layout& L) { return (L.nB1 + 3) / 4; }
-// FC2 column blocks: 4 prepared tiles (256 output columns) each.
-__host__ __device__ inline int fc2_blocks(const Layout& L) { return (L.nB2 + 3) / 4; }
 
 template <int FMT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
@@ -552,13 +480,10 @@ __global__ void __launch_bounds__(256)
   *(uint2*)(out + (int64_t)tok * H + h) = o;
 }
 
-// Grid of n tiles rounded up to whole XCD rounds (tile_id needs a multiple of 8).
-inline unsigned grid8(int64_t n) { return (unsigned)((n + 7) / 8 * 8); }
-
 template <int FMT, typename IdT>
 hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                               const IdT* ids, const float* tw, uint16_t* out, uint8_t* ws,
-                              const PrefillWs& W, int phases, hipStream_t st) {
+                              const PrefillWs& W, int phases, bool a8, hipStream_t st) {
   const int R = M * k;
   int* counts = (int*)(ws + W.counts);
   int* grp_start = (int*)(ws + W.grp_start);
@@ -574,13 +499,20 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
     hipLaunchKernelGGL((route_build<IdT>), dim3(L.E), dim3(1024), 0, st, ids, R, L.E, counts, grp_start,
                        tile_start, perm, rpos);
   }
-  if (phases & 1) {
-    hipLaunchKernelGGL((fc1_gemm<FMT>), dim3(grid8((int64_t)mt * fc1_blocks(L))), dim3(256), 0, st, prep, L, x, k,
+  const unsigned grid1 = grid8((int64_t)mt * fc1_blocks(L)), grid2 = grid8((int64_t)mt * fc2_blocks(L));
+  if ((phases & 1) && a8) {
+    const hipError_t err = launch_fc1_a8(L, prep, x, M, k, ws, W, grid1, st);
+    if (err != hipSuccess) return err;
+  } else if (phases & 1) {
+    hipLaunchKernelGGL((fc1_gemm<FMT>), dim3(grid1), dim3(256), 0, st, prep, L, x, k,
                        (const int*)counts, (const int*)grp_start, (const int*)tile_start,
                        (const int*)perm, act, plane);
   }
-  if (phases & 2) {
-    hipLaunchKernelGGL((fc2_gemm<FMT>), dim3(grid8((int64_t)mt * fc2_blocks(L))), dim3(256), 0, st, prep, L, tw,
+  if ((phases & 2) && a8) {
+    const hipError_t err = launch_fc2_a8(L, prep, tw, ws, W, grid2, st);
+    if (err != hipSuccess) return err;
+  } else if (phases & 2) {
+    hipLaunchKernelGGL((fc2_gemm<FMT>), dim3(grid2), dim3(256), 0, st, prep, L, tw,
                        (const int*)counts, (const int*)grp_start, (const int*)tile_start,
                        (const int*)perm, (const uint16_t*)act, plane, y);
   }
@@ -594,17 +526,17 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
 template <typename IdT>
 hipError_t launch_prefill(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                           const IdT* ids, const float* tw, uint16_t* out, uint8_t* ws,
-                          const PrefillWs& W, int phases, hipStream_t st) {
+                          const PrefillWs& W, int phases, bool a8, hipStream_t st) {
   if (L.fmt == kMXFP4)
-    return launch_prefill_fmt<kMXFP4, IdT>(L, prep, x, M, k, ids, tw, out, ws, W, phases, st);
-  return launch_prefill_fmt<kNVFP4, IdT>(L, prep, x, M, k, ids, tw, out, ws, W, phases, st);
+    return launch_prefill_fmt<kMXFP4, IdT>(L, prep, x, M, k, ids, tw, out, ws, W, phases, a8, st);
+  return launch_prefill_fmt<kNVFP4, IdT>(L, prep, x, M, k, ids, tw, out, ws, W, phases, false, st);
 }
 
 template hipError_t launch_prefill<int32_t>(const Layout&, const uint8_t*, const uint16_t*, int, int,
                                             const int32_t*, const float*, uint16_t*, uint8_t*,
-                                            const PrefillWs&, int, hipStream_t);
+                                            const PrefillWs&, int, bool, hipStream_t);
 template hipError_t launch_prefill<int64_t>(const Layout&, const uint8_t*, const uint16_t*, int, int,
                                             const int64_t*, const float*, uint16_t*, uint8_t*,
-                                            const PrefillWs&, int, hipStream_t);
+                                            const PrefillWs&, int, bool, hipStream_t);
 
 }  // namespace moe

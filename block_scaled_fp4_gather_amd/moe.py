@@ -31,6 +31,9 @@ class MoeFp4Error(RuntimeError):
 
 PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
 
+ACT_BF16, ACT_MXFP8 = 0, 1
+ACT_FORMATS = {"bf16": ACT_BF16, "mxfp8": ACT_MXFP8}
+
 
 class Tuning(ctypes.Structure):
     """Launch shape of the decode kernels and the execution path (0 keeps the
@@ -42,21 +45,26 @@ class Tuning(ctypes.Structure):
 class _Desc(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+                ("act_format", ctypes.c_int32)]
 
 
 @dataclasses.dataclass(frozen=True)
 class Desc:
+    """Layer shape; `act` is "bf16" or "mxfp8" (the W4A8-MX variant of the
+    grouped path, MXFP4 weights only)."""
     fmt: str
     E: int
     H: int
     I: int
     k: int
     max_tokens: int
+    act: str = "bf16"
 
     def c(self) -> _Desc:
+        act = ACT_FORMATS.get(self.act, self.act) if isinstance(self.act, str) else self.act
         return _Desc(FORMATS.get(self.fmt, self.fmt) if isinstance(self.fmt, str) else self.fmt,
-                     self.E, self.H, self.I, self.k, self.max_tokens)
+                     self.E, self.H, self.I, self.k, self.max_tokens, act)
 
 
 _lib = None
@@ -75,6 +83,7 @@ _SIGS = {
     "moe_fp4_forward_ex": ([ctypes.POINTER(_Desc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ,
                             ctypes.POINTER(Tuning), _I32, _VP], ctypes.c_int),
     "moe_fp4_dequant_export": ([ctypes.POINTER(_Desc), _VP, _I32, _I32, _VP, _VP], ctypes.c_int),
+    "moe_fp4_mxfp8_quantize": ([_VP, ctypes.c_int64, _I32, _VP, _VP, _VP], ctypes.c_int),
 }
 
 
@@ -163,6 +172,18 @@ def forward(desc: Desc, prepared, x, ids, w, out, workspace, stream=None, tuning
 def dequant_export(desc: Desc, prepared, expert: int, which: int, out, stream=None):
     _check("moe_fp4_dequant_export", lib().moe_fp4_dequant_export(
         ctypes.byref(desc.c()), _ptr(prepared), expert, which, _ptr(out), _stream(stream)))
+
+
+def mxfp8_quantize(x, codes=None, scales=None, stream=None):
+    """MXFP8 codes uint8 [rows][cols] and scales uint8 [rows][cols/32] of bf16 x."""
+    rows, cols = x.shape
+    if codes is None:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _check("moe_fp4_mxfp8_quantize", lib().moe_fp4_mxfp8_quantize(
+        _ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
 
 
 class Fp4MoE:

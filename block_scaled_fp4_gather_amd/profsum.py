@@ -7,7 +7,8 @@ reads one kernel-trace database (``--kernel-trace --stats``), two counter
 runs of the benchmark (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``) and the
 same two counters for the benchmark's copy probe (a device copy of 256 MiB
 each way), and writes ``profiles/<kernel>.<workload>.md`` for each layer
-kernel (decode: fc1_kernel, fc2_kernel; grouped: fc1_gemm, fc2_gemm and the
+kernel (decode: fc1_kernel, fc2_kernel; grouped: fc1_gemm, fc2_gemm, or with
+MXFP8 activations fc1_gemm_a8, fc2_gemm_a8 and mxfp8_quantize, and the
 routing and combine kernels).  Each summary ends with a JSON block that bench.py reads back; the
 counters there are tied to a hash of the kernel's HIP sources so that a
 summary taken before a change to that kernel is not used after it.
@@ -26,15 +27,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 256 * 1024 * 1024  # bench.py --copy-probe: bytes read and written per dispatch
-KERNELS = ("fc1_kernel", "fc2_kernel", "fc1_gemm", "fc2_gemm", "route_build", "combine")
+# (more specific names first: a kernel is named by the first entry its symbol contains)
+KERNELS = ("fc1_kernel", "fc2_kernel", "fc1_gemm_a8", "fc2_gemm_a8", "mxfp8_quantize", "fc1_gemm", "fc2_gemm",
+           "route_build", "combine")
 
 
 # HIP sources each kernel is built from: a summary stays valid while these
 # files are unchanged.
 _DECODE_SRC = ("decode_path.hip", "decode_path.h", "decode.h", "layout.h")
-_GROUPED_SRC = ("prefill.hip", "prefill.h", "decode.h", "layout.h")
+_GROUPED_SRC = ("prefill.hip", "prefill.h", "gemm_util.h", "decode.h", "layout.h")
+_A8_SRC = ("prefill_a8.hip", "prefill.h", "gemm_util.h", "mxfp8.h", "layout.h")
 SOURCES = {"fc1_kernel": _DECODE_SRC, "fc2_kernel": _DECODE_SRC, "fc1_gemm": _GROUPED_SRC,
-           "fc2_gemm": _GROUPED_SRC, "route_build": _GROUPED_SRC, "combine": _GROUPED_SRC}
+           "fc2_gemm": _GROUPED_SRC, "route_build": _GROUPED_SRC, "combine": _GROUPED_SRC,
+           "fc1_gemm_a8": _A8_SRC, "fc2_gemm_a8": _A8_SRC, "mxfp8_quantize": ("mxfp8.hip", "mxfp8.h")}
 
 
 def source_hash(kernel: str) -> str:

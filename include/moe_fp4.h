@@ -59,9 +59,32 @@ typedef enum {
   MOE_FP4_NVFP4 = 2  /* E2M1 + E4M3 scale per 16, times an fp32 global */
 } moe_fp4_format;
 
+/* Activation format of the grouped path.
+ *   BF16:  x and SiLU(gate) * up enter the GEMMs at bf16 precision or better
+ *          (the layer as defined above).
+ *   MXFP8: the W4A8-MX variant (b12x PR #22, Measured table and its note on
+ *          the dynamic path, which quantises activations to MXFP8; MXFP4
+ *          weights only).  x is quantised per token in blocks of 32 along H,
+ *          and SiLU(gate) * up (from fp32 FC1 outputs, rounded to fp32) per
+ *          route in blocks of 32 along I, each to MXFP8 as the OCP MX format
+ *          defines it: one UE8M0 scale 2^(floor(log2(max |v|)) - 8) per
+ *          block (clamped to 2^[-127, 127]; a zero block gets byte 0, a
+ *          block with a NaN or an infinity byte 255), elements v / scale
+ *          rounded to nearest-even E4M3 with magnitudes capped at 448 (a
+ *          NaN/Inf block's codes are all 0x7F).  FC1 and FC2 then run on the
+ *          scaled matrix instruction with fp32 accumulation.  The decode
+ *          path (small M) keeps bf16 activations in both modes, as the
+ *          pages' M = 1 kernel does. */
+typedef enum {
+  MOE_FP4_ACT_BF16 = 0,
+  MOE_FP4_ACT_MXFP8 = 1
+} moe_fp4_act_format;
+
 /* Shape of one MoE layer.  H and I must be multiples of 32 for both formats
  * (the kernels work in 32-element units); max_tokens is the largest M that
- * later forward calls will pass, used only to size the workspace. */
+ * later forward calls will pass, used only to size the workspace.
+ * act_format is a moe_fp4_act_format (0 keeps bf16 activations); MXFP8 with
+ * NVFP4 weights returns MOE_FP4_EUNSUPPORTED. */
 typedef struct {
   int32_t format;      /* moe_fp4_format */
   int32_t num_experts; /* E, resident experts; ids outside [0, E) are invalid */
@@ -69,6 +92,7 @@ typedef struct {
   int32_t inter;       /* I: intermediate size */
   int32_t top_k;       /* k: routes per token */
   int32_t max_tokens;  /* capacity for workspace sizing */
+  int32_t act_format;  /* moe_fp4_act_format */
 } moe_fp4_desc;
 
 /* Human-readable name of a status code (static string). */
@@ -101,8 +125,9 @@ moe_fp4_status moe_fp4_unprepare(const moe_fp4_desc* desc, const void* prepared,
  * aligned, caller-owned).  The size depends only on the descriptor, so one
  * workspace serves every M <= max_tokens; `M` is checked against max_tokens.
  * The grouped path needs about 4I + 4H bytes per route (max_tokens * k
- * routes).  Its contents on entry do not matter and are
- * overwritten. */
+ * routes) with bf16 activations, and about I + 4H per route plus H per
+ * token with MXFP8 activations.  Its contents on entry do not matter and
+ * are overwritten. */
 moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size_t* bytes);
 
 /* The layer.  x: bf16 [M][H]; topk_ids: int32 [M][k]; topk_w: fp32 [M][k]
@@ -182,6 +207,15 @@ moe_fp4_status moe_fp4_forward_ex(const moe_fp4_desc* desc, const void* prepared
                                   const float* topk_w, uint16_t* out, void* workspace,
                                   size_t workspace_bytes, const moe_fp4_tuning* tuning,
                                   int32_t phases, void* stream);
+
+/* The MXFP8 quantisation of the MXFP8 activation format (see
+ * moe_fp4_act_format), as the grouped path applies it to x: bf16 `x`
+ * [rows][cols] (device, 16-byte aligned, cols a multiple of 32) to E4M3
+ * `codes` [rows][cols] (device, 8-byte aligned) and UE8M0 `scales`
+ * [rows][cols / 32] (device), one scale per 32 consecutive values of a row.
+ * rows may be 0 (nothing is launched). */
+moe_fp4_status moe_fp4_mxfp8_quantize(const uint16_t* x, int64_t rows, int32_t cols, uint8_t* codes,
+                                      uint8_t* scales, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,16 @@ from block_scaled_fp4_gather_amd import moe, synth
 COS_MIN = 0.99995
 MAXABS_REL_RMS = 2e-2
 
+# The W4A8-MX variant against the oracle's W4A8 layer: the same cosine, and
+# max-abs beyond bf16 rounding <= 0.1 * RMS.  Its activations are quantised
+# to E4M3 from fp32 FC1 results that GPU and oracle sum in different orders,
+# so an activation on a rounding midpoint can take the adjacent code (the
+# identity-projection test measures 1.7e-4 of the codes flipping, every one
+# to a neighbour).  One flip moves a route's output by one E4M3 step of that
+# activation (at most |a| / 8) times the W2 column: for a route's largest
+# activation on these heavy-tailed rows, a few percent of the output RMS.
+W4A8_MAXABS_REL_RMS = 0.1
+
 
 def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
     """Half the bf16 spacing at |v| (8 significant bits)."""
@@ -39,9 +49,9 @@ def to_dev(a):
     return torch.from_numpy(a).cuda()
 
 
-def make_layer(fmt: str, d: dict, k: int, max_tokens: int) -> moe.Fp4MoE:
+def make_layer(fmt: str, d: dict, k: int, max_tokens: int, act: str = "bf16") -> moe.Fp4MoE:
     E, twoI, Hh = d["w13_codes"].shape
-    desc = moe.Desc(fmt, E, 2 * Hh, twoI // 2, k, max_tokens)
+    desc = moe.Desc(fmt, E, 2 * Hh, twoI // 2, k, max_tokens, act)
     return moe.Fp4MoE(desc, to_dev(d["w13_codes"]), to_dev(d["w13_scales"]), to_dev(d["w2_codes"]),
                       to_dev(d["w2_scales"]), to_dev(d.get("g13")), to_dev(d.get("g2")))
 
@@ -59,7 +69,7 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return oracle.bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def compare(gpu_bits: np.ndarray, acc: np.ndarray, label: str = "") -> dict:
+def compare(gpu_bits: np.ndarray, acc: np.ndarray, label: str = "", maxabs: float = MAXABS_REL_RMS) -> dict:
     g = bf16_to_f64(gpu_bits).ravel()
     r = acc.astype(np.float64).ravel()
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
@@ -73,7 +83,7 @@ def compare(gpu_bits: np.ndarray, acc: np.ndarray, label: str = "") -> dict:
     excess = float(np.max(err - bf16_half_ulp(r))) / rms
     say(f"  {label}: cos={cos:.8f} maxabs/rms={maxabs:.3e} beyond-rounding/rms={excess:.3e}")
     assert cos >= COS_MIN, f"{label}: cosine {cos}"
-    assert excess <= MAXABS_REL_RMS, f"{label}: max-abs/RMS beyond bf16 rounding {excess}"
+    assert excess <= maxabs, f"{label}: max-abs/RMS beyond bf16 rounding {excess}"
     return dict(cos=cos, maxabs_rel=maxabs, excess_rel=excess)
 
 

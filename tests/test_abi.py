@@ -149,3 +149,38 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         moe.lib()
+
+
+def test_activation_format_validation(L):
+    def status(desc):
+        n = ctypes.c_size_t()
+        return L.moe_fp4_workspace_bytes(ctypes.byref(desc.c()), 1, ctypes.byref(n))
+
+    assert status(moe.Desc("mxfp4", 8, 256, 128, 2, 4, "mxfp8")) == 0
+    assert status(moe.Desc("nvfp4", 8, 256, 128, 2, 4, "mxfp8")) == 2   # E8M0 scales only
+    assert status(moe.Desc("mxfp4", 8, 256, 128, 2, 4, 2)) == 1         # no such format
+    assert status(moe.Desc("mxfp4", 8, 256, 128, 2, 4, -1)) == 1
+    d = moe.Desc("nvfp4", 8, 256, 128, 2, 4, "mxfp8")
+    assert _forward_status(L, d, M=1) == 2
+
+
+def test_mxfp8_workspace_size(L):
+    M, k, H, I = 300, 4, 1024, 256
+    d = moe.Desc("mxfp4", 16, H, I, k, M, "mxfp8")
+    size = moe.workspace_bytes(d, 1)
+    routes = M * k
+    # grouped: x codes + scales per token; act codes + scales and an fp32
+    # output row per route; routing tables (5 int32 arrays) in between
+    need = M * (H + H // 32) + routes * (I + I // 32 + 4 * H)
+    assert need <= size <= need + 8 * 4 * routes + 64 * 1024
+    assert size < moe.workspace_bytes(moe.Desc("mxfp4", 16, H, I, k, M), 1)
+
+
+def test_mxfp8_quantize_rejects_before_launch(L):
+    q = L.moe_fp4_mxfp8_quantize
+    assert q(16, 4, 48, 16, 16, None) == 1      # cols not a multiple of 32
+    assert q(16, -1, 64, 16, 16, None) == 1
+    assert q(None, 4, 64, 16, 16, None) == 1
+    assert q(18, 4, 64, 16, 16, None) == 1      # misaligned input
+    assert q(16, 4, 64, 12, 16, None) == 1      # misaligned codes
+    assert q(None, 0, 64, None, None, None) == 0  # nothing to do

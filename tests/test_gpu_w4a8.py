@@ -1,0 +1,205 @@
+"""GPU parity of the W4A8-MX variant (MXFP4 weights, MXFP8 activations on
+the scaled matrix instruction) against the oracle's W4A8 layer: the
+activation quantiser bit-exact; the quantised SiLU product code by code
+(identical up to rare adjacent-code flips at rounding midpoints); the
+grouped layer at cosine >= 0.99995 and max-abs beyond bf16 rounding <= 0.1 *
+RMS (the effect of such a flip; the derivation is beside the constant in
+gpu_util); NaN propagation and invalid routes, the phase split, and the
+decode band, which keeps bf16 activations."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scaled_fp4_gather_amd import moe, synth
+from gpu_util import W4A8_MAXABS_REL_RMS, compare as _compare, make_layer, run_layer, say, to_dev
+from pins_util import bits_to_f32, random_case
+
+pytestmark = pytest.mark.gpu
+
+GROUPED = moe.Tuning(0, 0, 0, moe.PATH_GROUPED)
+
+
+def compare(gpu_bits, acc, label=""):
+    return _compare(gpu_bits, acc, label, maxabs=W4A8_MAXABS_REL_RMS)
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    say(f"\n[gpu] {request.node.nodeid}")
+    yield
+
+
+def _bf16_rows(rng, rows, cols):
+    """bf16 bit patterns with a per-block exponent spread, zeros, subnormals,
+    the largest finite values and a few NaN / Inf blocks."""
+    v = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-60, 60, (rows, cols // 32)).repeat(32, 1))
+    v *= np.exp2(rng.integers(-14, 1, (rows, cols)))
+    bits = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # truncation: any bf16 pattern
+    flat = bits.reshape(-1, 32)
+    nb = flat.shape[0]
+    pick = rng.permutation(nb)
+    flat[pick[0::11]] = 0                                              # zero blocks
+    flat[pick[1::11], 0] = 0x7FC0                                      # NaN
+    flat[pick[2::11], 5] = 0xFF80                                      # -Inf
+    flat[pick[3::11]] = rng.integers(0, 0x80, (len(pick[3::11]), 32))  # subnormal bf16
+    flat[pick[4::11], 7] = 0x7F7F                                      # largest finite
+    flat[pick[5::11]] |= 0x8000                                        # all negative
+    return bits
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 96), (300, 7168), (5, 4096)])
+def test_mxfp8_quantize_bit_exact(rows, cols):
+    rng = np.random.default_rng(rows * 7 + cols)
+    bits = _bf16_rows(rng, rows, cols)
+    want_c, want_s = oracle.mxfp8_quantize(bits_to_f32(bits))
+    x = to_dev(bits).view(torch.bfloat16)
+    codes, scales = moe.mxfp8_quantize(x)
+    torch.cuda.synchronize()
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(got_s, want_s), f"scales differ at {np.argwhere(got_s != want_s)[:5]}"
+    assert np.array_equal(got_c, want_c), f"codes differ at {np.argwhere(got_c != want_c)[:5]}"
+    say(f"  {rows}x{cols}: bit-exact ({np.mean(want_s == 255):.3f} NaN blocks)")
+
+
+CASES = [
+    # E, H, I, M, k, seed, hot-expert fraction
+    (4, 64, 32, 20, 1, 1, 0.0),       # 2 FC1 units (half a step), 1 FC2 unit
+    (6, 96, 64, 33, 3, 2, 0.0),       # 3 FC1 units, 2 FC2 units
+    (5, 160, 96, 40, 4, 3, 0.0),      # 5 FC1 units: one whole step + 1; I = 3 units
+    (8, 512, 128, 300, 2, 4, 0.5),    # 2 m-tiles for the hot expert
+    (16, 1024, 256, 520, 4, 5, 0.9),  # hot expert: 4 full m-tiles + a ragged one
+    (3, 1536, 544, 100, 2, 7, 0.0),   # 17 FC1 tiles: last column block half empty
+    (1, 224, 160, 130, 1, 8, 0.0),    # a single expert, 128 + 2 rows; 7 and 5 units
+]
+
+
+@pytest.mark.parametrize("E,H,I,M,k,seed,hot", CASES)
+def test_w4a8_grouped_small_shapes(E, H, I, M, k, seed, hot):
+    rng = np.random.default_rng(200 + seed)
+    d, _, _ = random_case(rng, "mxfp4", E, H, I, M, k)
+    if hot:
+        ids = d["ids"]
+        for t in range(M):
+            if rng.random() < hot and E // 2 not in ids[t]:
+                ids[t, rng.integers(0, k)] = E // 2
+    flat = d["ids"].reshape(-1)
+    if flat.size > 2:
+        flat[1] = -1
+        flat[-1] = E + seed
+    if M > 1 and k > 1:
+        d["ids"][1, 1] = d["ids"][1, 0]
+    acc = oracle.forward_w4a8("mxfp4", d)
+    layer = make_layer("mxfp4", d, k, M, act="mxfp8")
+    label = f"w4a8 E{E} H{H} I{I} M{M} k{k}"
+    got = run_layer(layer, d, tuning=GROUPED)
+    compare(got, acc, label)
+    if M > min(16, 64 // k):
+        assert np.array_equal(run_layer(layer, d), got)
+        assert np.array_equal(run_layer(layer, d, ids_dtype=torch.int64), got), "int64 ids"
+    assert np.array_equal(run_layer(layer, d, tuning=GROUPED), got), "not bit-reproducible"
+
+
+def test_w4a8_decode_band_keeps_bf16_activations():
+    rng = np.random.default_rng(41)
+    d, _, _ = random_case(rng, "mxfp4", 16, 512, 128, 3, 4)
+    a8 = make_layer("mxfp4", d, 4, 3, act="mxfp8")
+    bf = make_layer("mxfp4", d, 4, 3)
+    assert np.array_equal(run_layer(a8, d), run_layer(bf, d))
+    acc, _ = oracle.forward_f32("mxfp4", d)
+    _compare(run_layer(a8, d), acc, "w4a8 desc, decode band (bf16 activations)")
+    # forced onto the grouped path the same call quantises
+    compare(run_layer(a8, d, tuning=GROUPED), oracle.forward_w4a8("mxfp4", d), "w4a8 forced grouped, M3")
+
+
+def test_w4a8_nan_propagation_and_poisoned_expert():
+    rng = np.random.default_rng(42)
+    M, k = 48, 4
+    d, _, _ = random_case(rng, "mxfp4", 6, 256, 64, M, k)
+    d["ids"][:] = rng.integers(1, 6, size=(M, k))
+    d["w13_scales"][0] = 0xFF                 # expert 0 is NaN and never routed
+    d["w2_scales"][0] = 0xFF
+    d["ids"][:, 2] = np.resize(np.array([-1, 6, 2**31 - 1, -(2**31)], np.int32), M)
+    d["x"][7, 40] = 0x7FC0                    # NaN in token 7's x
+    acc = oracle.forward_w4a8("mxfp4", d)
+    assert np.isnan(acc[7]).all() and np.isfinite(np.delete(acc, 7, 0)).all()
+    layer = make_layer("mxfp4", d, k, M, act="mxfp8")
+    got = run_layer(layer, d)
+    g = oracle.bf16_bits_to_f32(got)
+    assert np.isnan(g[7]).all(), "a NaN in x reaches every output of its token"
+    keep = np.delete(np.arange(M), 7)
+    compare(got[keep], acc[keep], "w4a8 poisoned expert 0, NaN token excluded")
+
+
+def test_w4a8_phases_split_and_poisoned_workspace():
+    rng = np.random.default_rng(43)
+    d, _, _ = random_case(rng, "mxfp4", 8, 288, 96, 64, 2)
+    layer = make_layer("mxfp4", d, 2, 64, act="mxfp8")
+    whole = run_layer(layer, d, tuning=GROUPED)
+    x = to_dev(d["x"]).view(torch.bfloat16)
+    ids, w = to_dev(d["ids"]), to_dev(d["w"])
+    out = torch.empty_like(x)
+    layer.workspace.fill_(0xFF)               # NaN scale bytes in every padding byte
+    for ph in (1, 2):
+        layer(x, ids, w, out=out, tuning=GROUPED, phases=ph)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), whole)
+    out.fill_(float("nan"))
+    for ph in (4, 1, 2, 8):
+        layer(x, ids, w, out=out, tuning=GROUPED, phases=ph)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.view(torch.int16).cpu().numpy().view(np.uint16), whole)
+    compare(whole, oracle.forward_w4a8("mxfp4", d), "w4a8 H288 (9 units) I96")
+
+
+def test_w4a8_prefill_workload_full_size_sampled():
+    """The E128/H4096/I1536 prefill (4096 tokens, top-8) with MXFP8
+    activations, run whole; the oracle checks a sample of tokens."""
+    wl = synth.WORKLOADS["mxfp4_prefill_e128"]
+    d = synth.generate(wl)
+    layer = make_layer(wl.fmt, d, wl.k, wl.M, act="mxfp8")
+    got = run_layer(layer, d)
+    assert np.array_equal(run_layer(layer, d), got), "not bit-reproducible"
+    rng = np.random.default_rng(44)
+    sample = np.unique(np.concatenate([[0, 1, wl.M - 1], rng.integers(0, wl.M, 5)]))
+    sub = dict(d, x=d["x"][sample], ids=d["ids"][sample], w=d["w"][sample])
+    say(f"  oracle on tokens {sample.tolist()}")
+    compare(got[sample], oracle.forward_w4a8(wl.fmt, sub), f"{wl.name} w4a8 sampled")
+
+
+def test_w4a8_act_codes_through_identity_down_projection():
+    """With H = I, W2 = identity (E2M1 1.0 on the diagonal, scale 1) and one
+    route of weight 1 per token, the layer's output is exactly the quantised
+    activation SiLU(gate) * up (E4M3 times a power of two is exact in fp32
+    and bf16), so the GPU's activation codes can be compared with the
+    oracle's element by element.  GPU and oracle round FC1's sums to fp32 in
+    different orders, so an activation sitting on a rounding midpoint may
+    take the adjacent code: such flips must be rare and adjacent."""
+    rng = np.random.default_rng(45)
+    E, H, M = 3, 512, 300
+    d, _, _ = random_case(rng, "mxfp4", E, H, H, M, 1)
+    nib = np.zeros((E, H, H), np.uint8)
+    nib[:, np.arange(H), np.arange(H)] = 2
+    d["w2_codes"] = np.ascontiguousarray(nib[..., 0::2] | (nib[..., 1::2] << 4))
+    d["w2_scales"] = np.full((E, H, H // 32), 127, np.uint8)
+    d["w"] = np.ones((M, 1), np.float32)
+    d["ids"][::17] = -1
+    want = oracle.forward_w4a8("mxfp4", d)
+    layer = make_layer("mxfp4", d, 1, M, act="mxfp8")
+    got = oracle.bf16_bits_to_f32(run_layer(layer, d)).astype(np.float64)
+    valid = d["ids"][:, 0] >= 0
+    assert np.all(got[~valid] == 0)
+    g, r = got[valid], want[valid]
+    diff = g != r
+    frac = diff.mean()
+    say(f"  activation codes differing: {diff.sum()} of {diff.size} ({frac:.2e})")
+    assert frac <= 1e-3
+    # a flip moves one element to a neighbouring code of the same block scale
+    blk = np.abs(r).reshape(r.shape[0], -1, 32).max(-1)
+    _, e = np.frexp(blk)
+    X = np.repeat(np.where(blk > 0, np.ldexp(1.0, e - 1 - 8), 0.0), 32, axis=-1)
+    step = np.maximum(np.abs(g), np.abs(r)) / 8 + X * 2.0 ** -9
+    assert np.all(np.abs(g - r)[diff] <= step[diff] * (1 + 1e-12))
+    assert np.all((np.sign(g) * np.sign(r))[diff] >= 0)
