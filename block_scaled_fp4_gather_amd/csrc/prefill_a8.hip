@@ -35,7 +35,8 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 // values of FP8, the 16-byte chunk c of row r at position c ^ swz(r)); A
 // scale ring of 2 slots x 4 waves x 256 bytes (rows 32w..32w+31 of the tile,
 // one dword of 4 unit scales per row; the upper 128 bytes are spare); weight
-// ring of 2 slots x 4 waves x (4 x 1 KiB codes + 2 x 256 B scale dwords).
+// ring of 2 slots x 4 waves x (4 x 1 KiB codes + 256 B of scale dwords, one
+// per weight row, + 256 B spare).
 constexpr int kStepK8 = 128;                 // K values per main-loop step (4 units)
 constexpr int kARow8 = kStepK8;              // bytes of one A row of a step
 constexpr int kAPlane8 = kGemmBM * kARow8;   // 16 KiB
@@ -61,7 +62,7 @@ __device__ __forceinline__ int scale_byte(uint32_t w, int b) { return (int)((w >
 // 8 rows per copy, from `rowp[blk]`), their scale dwords (from `srow`, this
 // lane's row 32w + lane % 32), and the wave's weights, which lane (n, h)
 // copies for the units it multiplies (unit 4s + 2t + h of weight rows n and
-// 32 + n) with the scale dwords of those rows.  Copies past the last unit
+// 32 + n) and one copy of the scale dwords of all 64 rows.  Copies past the last unit
 // are clamped to it; in a last step with fewer than 4 units the absent
 // units' operands are zeroed and their scales set to 1 when read.
 template <int NB, typename Epilogue>
@@ -102,14 +103,14 @@ __device__ __forceinline__ void gemm_main_a8(const uint8_t* const (&rowp)[4], co
     const int u = min(4 * sc + 2 * tt + h, nU - 1);
     dma16(btile + (int64_t)u * 1024 + (32 * j + n) * 16, lds_addr(bring + (s & 1) * kBSlot8 + q * 1024));
   };
-  auto copy_bs = [&](int s, int j) {
+  // the scale dwords of the step's 4 units for all 64 weight rows (lane l: row l)
+  auto copy_bs = [&](int s) {
     const int sc = min(s, nsteps - 1);
-    dma4(btile + (int64_t)nU * 1024 + sc * 256 + (32 * j + n) * 4,
-         lds_addr(bring + (s & 1) * kBSlot8 + 4096 + j * 256));
+    dma4(btile + (int64_t)nU * 1024 + sc * 256 + lane * 4, lds_addr(bring + (s & 1) * kBSlot8 + 4096));
   };
   // copies of one step, in issue order: 4 A row blocks, the A scales, then
-  // (waves with a weight tile) 4 weight unit sets and 2 weight scale sets
-  constexpr int NCOPY = NB > 0 ? 11 : 5;
+  // (waves with a weight tile) 4 weight unit sets and the weight scales
+  constexpr int NCOPY = NB > 0 ? 10 : 5;
   auto copy = [&](int s, int ci) {
     if (ci < 4)
       copy_a(s, ci);
@@ -118,7 +119,7 @@ __device__ __forceinline__ void gemm_main_a8(const uint8_t* const (&rowp)[4], co
     else if (ci < 9)
       copy_b(s, ci - 5);
     else
-      copy_bs(s, ci - 9);
+      copy_bs(s);
   };
 
   auto step = [&](int s, int rem) {  // rem: units of this step (4 unless the last)
@@ -133,7 +134,7 @@ __device__ __forceinline__ void gemm_main_a8(const uint8_t* const (&rowp)[4], co
       const uint8_t* ss = sring + (s & 1) * kASlot8;
       uint32_t bsw[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) bsw[j] = *(const uint32_t*)(bs + 4096 + j * 256 + lane * 4);
+      for (int j = 0; j < 2; ++j) bsw[j] = *(const uint32_t*)(bs + 4096 + (32 * j + n) * 4);
       int ci = 0;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -221,28 +222,56 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     rowp[blk] = xq + (int64_t)(perm[gs + r] / k) * L.H;
   }
   const uint8_t* srow = xs + (int64_t)(perm[gs + min(32 * wave + (lane & 31), rows - 1)] / k) * xss;
+  // Epilogue, per 32-row block: a = SiLU(gate) * up in fp32 goes to this
+  // wave's part of the (now idle) A ring as 32 rows x 32 columns (row stride
+  // 144 B), then lane l takes row l / 2, columns 16 (l % 2) .. + 15: the
+  // block maximum is its own 16 values and its neighbour's, and its 16 codes
+  // leave in one 16-byte store.
   auto epilogue = [&](auto& acc) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
+    constexpr int kStride = 36;  // dwords per staged row
+    float* st = (float*)(smem + wave * 32 * kStride * 4);
     const int n = lane & 31;
+    const int rr = lane >> 1, half = lane & 1;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + acc_row(r, lane);
         const float gate = acc[i][0][r];
         const float up = acc[i][1][r];
-        const float a = gate / (1.0f + expf(-gate)) * up;
-        // the block of 32 values is this row's 32 columns: lanes 32h..32h+31
-        uint32_t m = __float_as_uint(a) & 0x7FFFFFFFu;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-        const uint32_t sb = mx_scale_byte(m);
-        const uint32_t code = sb == 255u ? 0x7Fu : e4m3_code(a * mx_inv_scale(sb));
-        if (row < rows) {
-          aq[(int64_t)(gs + row) * L.I + 32 * b + n] = (uint8_t)code;
-          if (n == 0) as[(int64_t)(gs + row) * ass + b] = (uint8_t)sb;
-        }
+        st[acc_row(r, lane) * kStride + n] = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
       }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging stores are done
+      __builtin_amdgcn_wave_barrier();
+      float v[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 f = *(const float4*)(st + rr * kStride + 16 * half + 4 * q);
+        v[4 * q] = f.x;
+        v[4 * q + 1] = f.y;
+        v[4 * q + 2] = f.z;
+        v[4 * q + 3] = f.w;
+      }
+      uint32_t m = 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) m = max(m, __float_as_uint(v[q]) & 0x7FFFFFFFu);
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+      const uint32_t sb = mx_scale_byte(m);
+      uint32_t w[4] = {0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+      if (sb != 255u) {
+        const float inv = mx_inv_scale(sb);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          w[q] = e4m3_code(v[4 * q] * inv) | (e4m3_code(v[4 * q + 1] * inv) << 8) |
+                 (e4m3_code(v[4 * q + 2] * inv) << 16) | (e4m3_code(v[4 * q + 3] * inv) << 24);
+      }
+      const int row = i * 32 + rr;
+      if (row < rows) {
+        *(uint4*)(aq + (int64_t)(gs + row) * L.I + 32 * b + 16 * half) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (half == 0) as[(int64_t)(gs + row) * ass + b] = (uint8_t)sb;
+      }
+      __builtin_amdgcn_wave_barrier();  // the next block's stores come after these reads
+      __builtin_amdgcn_s_waitcnt(0xC07F);
     }
   };
   gemm_rows_a8(rows, rowp, srow, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, smem, epilogue);
