@@ -6,7 +6,9 @@ test suite, the smoke check and the benchmark's CPU-baseline leg may import
 this package; the library's product path never does.
 
 Numpy arrays in the logical layout that ``block_scaled_fp4_gather_amd.synth``
-produces go in; fp32 token sums and their bf16 bit patterns come out.
+produces go in; fp32 token sums and their bf16 bit patterns come out.  The
+case dict may name a gated activation ("fn": "silu", "gelu_tanh" or
+"swigluoai", with "alpha", "beta", "limit"); SiLU when absent.
 """
 from __future__ import annotations
 
@@ -21,6 +23,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.cpp")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
 FMT = {"mxfp4": 1, "nvfp4": 2}
+ACT = {"silu": 0, "gelu_tanh": 1, "swigluoai": 2}
 
 
 def build(force: bool = True) -> str:
@@ -60,15 +63,18 @@ def lib():
         L.oracle_dequant.argtypes = [i, u8p, u8p, ctypes.c_float, i, i, f32p]
         L.oracle_dequant.restype = i
         common = [i, i, i, i, i, i, u8p, u8p, u8p, u8p, f32p, f32p, u16p, i64p, f32p]
-        L.oracle_forward_f32.argtypes = common + [f32p, u16p]
+        actp = [i, ctypes.c_float, ctypes.c_float, ctypes.c_float]
+        L.oracle_forward_f32.argtypes = common + [f32p, u16p] + actp
         L.oracle_forward_f32.restype = i
-        L.oracle_forward_f64.argtypes = common + [f64p]
+        L.oracle_forward_f64.argtypes = common + [f64p] + actp
         L.oracle_forward_f64.restype = i
         L.oracle_mxfp8_quantize.argtypes = [f32p, i, i, u8p, u8p]
         L.oracle_mxfp8_quantize.restype = i
         L.oracle_mxfp8_value.argtypes = [ctypes.c_uint32, ctypes.c_uint32]
         L.oracle_mxfp8_value.restype = ctypes.c_double
-        L.oracle_forward_w4a8.argtypes = common + [i, f64p]
+        L.oracle_forward_w4a8.argtypes = common + [i, f64p] + actp
+        L.oracle_activation.argtypes = [i] + [ctypes.c_double] * 5
+        L.oracle_activation.restype = ctypes.c_double
         L.oracle_forward_w4a8.restype = i
         _lib = L
     return _lib
@@ -115,6 +121,16 @@ def dequant(fmt: str, codes: np.ndarray, scales: np.ndarray, global_scale: float
     return out
 
 
+def _act(d):
+    """(kind, alpha, beta, limit) from the case dict; SiLU when absent."""
+    fn = d.get("fn", "silu")
+    return [ACT.get(fn, fn), float(d.get("alpha", 0.0)), float(d.get("beta", 0.0)), float(d.get("limit", 0.0))]
+
+
+def activation(fn: str, gate: float, up: float, alpha: float = 0.0, beta: float = 0.0, limit: float = 0.0) -> float:
+    return lib().oracle_activation(ACT[fn], alpha, beta, limit, gate, up)
+
+
 def _args(fmt, d):
     E, twoI, Hh = d["w13_codes"].shape
     H, I = 2 * Hh, twoI // 2
@@ -138,7 +154,7 @@ def forward_f32(fmt: str, d: dict) -> tuple[np.ndarray, np.ndarray]:
     args, keep, M, H = _args(fmt, d)
     acc = np.empty((M, H), dtype=np.float32)
     out = np.empty((M, H), dtype=np.uint16)
-    rc = lib().oracle_forward_f32(*args, _p(acc, ctypes.c_float), _p(out, ctypes.c_uint16))
+    rc = lib().oracle_forward_f32(*args, _p(acc, ctypes.c_float), _p(out, ctypes.c_uint16), *_act(d))
     if rc:
         raise ValueError("oracle_forward_f32 rejected its arguments")
     del keep
@@ -148,7 +164,7 @@ def forward_f32(fmt: str, d: dict) -> tuple[np.ndarray, np.ndarray]:
 def forward_f64(fmt: str, d: dict) -> np.ndarray:
     args, keep, M, H = _args(fmt, d)
     acc = np.empty((M, H), dtype=np.float64)
-    rc = lib().oracle_forward_f64(*args, _p(acc, ctypes.c_double))
+    rc = lib().oracle_forward_f64(*args, _p(acc, ctypes.c_double), *_act(d))
     if rc:
         raise ValueError("oracle_forward_f64 rejected its arguments")
     del keep
@@ -176,7 +192,7 @@ def forward_w4a8(fmt: str, d: dict, quant_act: bool = True) -> np.ndarray:
     """The W4A8-MX layer (MXFP4 only) in fp64: [M][H] token sums."""
     args, keep, M, H = _args(fmt, d)
     acc = np.empty((M, H), dtype=np.float64)
-    rc = lib().oracle_forward_w4a8(*args, int(bool(quant_act)), _p(acc, ctypes.c_double))
+    rc = lib().oracle_forward_w4a8(*args, int(bool(quant_act)), _p(acc, ctypes.c_double), *_act(d))
     if rc:
         raise ValueError("oracle_forward_w4a8 rejected its arguments")
     del keep

@@ -55,6 +55,15 @@
 //    intermediate of the pages), so the codes are decided from fp32 values.
 //  * Only MXFP4 weights (the scaled products take E8M0 scales).
 //
+// Other gated activations (flashinfer #4285, reviews of moe_activation.py
+// and of the direct micro kernel's activation coverage name gelu_tanh and
+// swigluoai_uninterleave with alpha, beta and limit, without formulas):
+//  * gelu_tanh(gate) * up with the tanh form of GELU,
+//    0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)));
+//  * swigluoai: g = min(gate, limit), u = clamp(up, -limit, limit),
+//    g * sigmoid(alpha g) * (u + beta), the clamps written as comparisons so
+//    that a NaN passes through; gate and up are the separate halves of W13.
+//
 // Build: g++ -O2 -ffp-contract=off -shared -fPIC (no fast-math, no FMA
 // contraction, so every product and sum is one IEEE fp32 rounding in the
 // order written).
@@ -187,6 +196,34 @@ double mxfp8_value(uint8_t code, uint8_t scale) {
   return (double)e4m3fn(code) * (double)ue8m0(scale);
 }
 
+const int ACT_SILU = 0;
+const int ACT_GELU_TANH = 1;
+const int ACT_SWIGLUOAI = 2;
+
+struct Act {
+  int kind;
+  double alpha, beta, limit;
+};
+
+// The gated activation in the precision T (float for the fp32 oracle,
+// double for the others), each operation rounded in T.
+template <typename T>
+T gated(const Act& a, T g, T u) {
+  if (a.kind == ACT_GELU_TANH) {
+    const T c = (T)0.7978845608028654;  // sqrt(2 / pi)
+    return (T)0.5 * g * ((T)1 + std::tanh(c * (g + (T)0.044715 * g * g * g))) * u;
+  }
+  if (a.kind == ACT_SWIGLUOAI) {
+    const T lim = (T)a.limit;
+    const T gc = g > lim ? lim : g;
+    const T uc = u > lim ? lim : (u < -lim ? -lim : u);
+    return gc / ((T)1 + std::exp(-(T)a.alpha * gc)) * (uc + (T)a.beta);
+  }
+  return g / ((T)1 + std::exp(-g)) * u;
+}
+
+bool valid_act(int kind) { return kind == ACT_SILU || kind == ACT_GELU_TANH || kind == ACT_SWIGLUOAI; }
+
 }  // namespace
 
 extern "C" {
@@ -214,8 +251,10 @@ int oracle_forward_f32(int fmt, int E, int H, int I, int M, int k, const uint8_t
                        const uint8_t* w13_scales, const uint8_t* w2_codes,
                        const uint8_t* w2_scales, const float* g13, const float* g2,
                        const uint16_t* x, const int64_t* ids, const float* topk_w,
-                       float* acc_out, uint16_t* out_bf16) {
-  if (!valid_args(fmt, E, H, I, M, k)) return 1;
+                       float* acc_out, uint16_t* out_bf16, int act, float alpha, float beta,
+                       float limit) {
+  if (!valid_args(fmt, E, H, I, M, k) || !valid_act(act)) return 1;
+  const Act A{act, alpha, beta, limit};
   const int G = block_size(fmt);
   const size_t w13_cb = (size_t)2 * I * (H / 2), w13_sb = (size_t)2 * I * (H / G);
   const size_t w2_cb = (size_t)H * (I / 2), w2_sb = (size_t)H * (I / G);
@@ -240,7 +279,7 @@ int oracle_forward_f32(int fmt, int E, int H, int I, int M, int k, const uint8_t
         for (int h = 0; h < H; ++h) gate += xf[h] * grow[h];
         for (int h = 0; h < H; ++h) grow[h] = weight(fmt, c13, s13, gl13, H, I + n, h);
         for (int h = 0; h < H; ++h) up += xf[h] * grow[h];
-        a[n] = gate / (1.0f + std::exp(-gate)) * up;
+        a[n] = gated<float>(A, gate, up);
       }
       // FC2 and router-weighted combine.
       const float wt = topk_w[(size_t)t * k + j];
@@ -265,8 +304,9 @@ int oracle_forward_f64(int fmt, int E, int H, int I, int M, int k, const uint8_t
                        const uint8_t* w13_scales, const uint8_t* w2_codes,
                        const uint8_t* w2_scales, const float* g13, const float* g2,
                        const uint16_t* x, const int64_t* ids, const float* topk_w,
-                       double* acc_out) {
-  if (!valid_args(fmt, E, H, I, M, k)) return 1;
+                       double* acc_out, int act, float alpha, float beta, float limit) {
+  if (!valid_args(fmt, E, H, I, M, k) || !valid_act(act)) return 1;
+  const Act A{act, alpha, beta, limit};
   const int G = block_size(fmt);
   const size_t w13_cb = (size_t)2 * I * (H / 2), w13_sb = (size_t)2 * I * (H / G);
   const size_t w2_cb = (size_t)H * (I / 2), w2_sb = (size_t)H * (I / G);
@@ -286,7 +326,7 @@ int oracle_forward_f64(int fmt, int E, int H, int I, int M, int k, const uint8_t
           gate += xv * weight(fmt, w13_codes + e * w13_cb, w13_scales + e * w13_sb, gl13, H, n, h);
           up += xv * weight(fmt, w13_codes + e * w13_cb, w13_scales + e * w13_sb, gl13, H, I + n, h);
         }
-        a[n] = gate / (1.0 + std::exp(-gate)) * up;
+        a[n] = gated<double>(A, gate, up);
       }
       for (int h = 0; h < H; ++h) {
         double y = 0.0;
@@ -297,6 +337,11 @@ int oracle_forward_f64(int fmt, int E, int H, int I, int M, int k, const uint8_t
     }
   }
   return 0;
+}
+
+// The gated activation in fp64 (act: 0 SiLU, 1 gelu_tanh, 2 swigluoai).
+double oracle_activation(int act, double alpha, double beta, double limit, double gate, double up) {
+  return gated<double>(Act{act, alpha, beta, limit}, gate, up);
 }
 
 // MXFP8 quantisation of a [rows][cols] fp32 matrix (cols a multiple of 32):
@@ -319,15 +364,18 @@ double oracle_mxfp8_value(uint32_t code, uint32_t scale) {
 // FC1 dot products in fp64 then rounded to fp32, a = SiLU(gate) * up rounded
 // to fp32, then (quant_act != 0) quantised to MXFP8 per route in blocks of 32
 // along I, FC2 and the router-weighted sum in fp64.  quant_act = 0 feeds the
-// fp32 a to FC2 unquantised (used to check the rest of the chain).
+// fp32 a to FC2 unquantised (used to check the rest of the chain).  `act`
+// and its parameters choose the gated activation, as in the other forms.
 int oracle_forward_w4a8(int fmt, int E, int H, int I, int M, int k, const uint8_t* w13_codes,
                         const uint8_t* w13_scales, const uint8_t* w2_codes,
                         const uint8_t* w2_scales, const float* g13, const float* g2,
                         const uint16_t* x, const int64_t* ids, const float* topk_w,
-                        int quant_act, double* acc_out) {
+                        int quant_act, double* acc_out, int act, float alpha, float beta,
+                        float limit) {
   (void)g13;
   (void)g2;
-  if (fmt != FMT_MXFP4 || !valid_args(fmt, E, H, I, M, k)) return 1;
+  if (fmt != FMT_MXFP4 || !valid_args(fmt, E, H, I, M, k) || !valid_act(act)) return 1;
+  const Act A{act, alpha, beta, limit};
   const size_t w13_cb = (size_t)2 * I * (H / 2), w13_sb = (size_t)2 * I * (H / 32);
   const size_t w2_cb = (size_t)H * (I / 2), w2_sb = (size_t)H * (I / 32);
   std::vector<float> xf(H), af(I);
@@ -351,7 +399,7 @@ int oracle_forward_w4a8(int fmt, int E, int H, int I, int M, int k, const uint8_
           up += xq[h] * weight(fmt, c13, s13, 1.0f, H, I + n, h);
         }
         const double g = (float)gate, u = (float)up;
-        af[n] = (float)(g / (1.0 + std::exp(-g)) * u);
+        af[n] = (float)gated<double>(A, g, u);
       }
       if (quant_act) {
         oracle_mxfp8_quantize(af.data(), 1, I, ac.data(), as.data());

@@ -73,9 +73,10 @@ def bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def dense_layer_f64(w13: np.ndarray, w2: np.ndarray, x: np.ndarray, ids: np.ndarray,
-                    w: np.ndarray) -> np.ndarray:
+                    w: np.ndarray, act=None) -> np.ndarray:
     """Textbook gated MLP per route, summed with router weights, in fp64.
-    w13 [E][2I][H] (gate rows first), w2 [E][H][I], x [M][H]."""
+    w13 [E][2I][H] (gate rows first), w2 [E][H][I], x [M][H]; `act(g, u)`
+    replaces SiLU(g) * u when given."""
     E, twoI, H = w13.shape
     I = twoI // 2
     M, k = ids.shape
@@ -87,7 +88,7 @@ def dense_layer_f64(w13: np.ndarray, w2: np.ndarray, x: np.ndarray, ids: np.ndar
                 continue
             g = w13[e, :I].astype(np.float64) @ x[t].astype(np.float64)
             u = w13[e, I:].astype(np.float64) @ x[t].astype(np.float64)
-            a = g / (1.0 + np.exp(-g)) * u
+            a = g / (1.0 + np.exp(-g)) * u if act is None else act(g, u)
             out[t] += float(w[t, j]) * (w2[e].astype(np.float64) @ a)
     return out
 
