@@ -1,0 +1,34 @@
+// The gated activations of the FC1 epilogues, a = f(gate, up) in fp32.
+// The pages name SiLU (b12x PR #22, What: FC2 applies SiLU inline),
+// gelu_tanh and swigluoai_uninterleave with alpha, beta and limit (flashinfer
+// #4285, the review of moe_activation.py and of the direct micro kernel's
+// activation coverage) without formulas; these are the standard ones:
+//   silu:       gate * sigmoid(gate) * up
+//   gelu_tanh:  0.5 * gate * (1 + tanh(sqrt(2/pi) * (gate + 0.044715 gate^3))) * up
+//   swigluoai:  g = min(gate, limit), u = clamp(up, -limit, limit),
+//               g * sigmoid(alpha * g) * (u + beta)
+// (gate and up are separate halves of W13, not interleaved).  The clamps
+// are comparisons, so a NaN passes through them.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "layout.h"
+
+namespace moe {
+
+__device__ __forceinline__ float gated_act(const ActParams& p, float g, float u) {
+  if (p.kind == kActGeluTanh) {
+    const float z = 0.7978845608028654f * (g + 0.044715f * g * g * g);
+    const float th = 1.0f - 2.0f / (1.0f + __expf(2.0f * z));  // tanh(z), saturating to +-1
+    return 0.5f * g * (1.0f + th) * u;
+  }
+  if (p.kind == kActSwigluOai) {
+    const float gc = g > p.limit ? p.limit : g;
+    const float uc = u > p.limit ? p.limit : (u < -p.limit ? -p.limit : u);
+    return gc / (1.0f + __expf(-p.alpha * gc)) * (uc + p.beta);
+  }
+  return g / (1.0f + __expf(-g)) * u;
+}
+
+}  // namespace moe

@@ -26,6 +26,7 @@
 // #311: commit message on invalid routes and the tiny_decode.py review).
 #include <hip/hip_runtime.h>
 
+#include "act.h"
 #include "decode.h"
 #include "decode_path.h"
 #include "layout.h"
@@ -292,7 +293,7 @@ __global__ void __launch_bounds__(1024)
       }
       gate *= g13;
       up *= g13;
-      const float a = gate / (1.0f + __expf(-gate)) * up;
+      const float a = gated_act(L.act, gate, up);
       // a = hi + lo in two bf16 planes: 16 significant bits for FC2's bf16
       // dot products.
       const uint16_t hi = f32_to_bf16_rne(a);

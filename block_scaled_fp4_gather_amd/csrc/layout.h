@@ -35,6 +35,13 @@ namespace moe {
 
 enum { kMXFP4 = 1, kNVFP4 = 2 };
 
+// Gated activation applied to (gate, up) in the FC1 epilogues.
+enum { kActSilu = 0, kActGeluTanh = 1, kActSwigluOai = 2 };
+struct ActParams {
+  int32_t kind;
+  float alpha, beta, limit;  // kActSwigluOai only
+};
+
 struct Layout {
   int32_t fmt, E, H, I;
   int32_t G;        // elements per scale byte
@@ -50,6 +57,7 @@ struct Layout {
   int64_t expert;   // expert stride
   int64_t globals;  // bytes of the globals header
   int64_t total;    // whole prepared buffer
+  ActParams act;    // the layer's activation (not part of the byte layout)
 };
 
 MOE_HD inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
@@ -75,6 +83,7 @@ MOE_HD inline bool make_layout(int32_t fmt, int32_t E, int32_t H, int32_t I, Lay
   L->expert = align_up(L->w13 + L->tile2 * L->nB2, 256);
   L->globals = fmt == kNVFP4 ? align_up(8 * (int64_t)E, 256) : 0;
   L->total = L->globals + L->expert * E;
+  L->act = ActParams{kActSilu, 0.0f, 0.0f, 0.0f};
   return true;
 }
 

@@ -23,6 +23,7 @@
 // Invalid ids (negative or >= E) join no group and are skipped by combine.
 #include <hip/hip_runtime.h>
 
+#include "act.h"
 #include "decode.h"
 #include "gemm_util.h"
 #include "layout.h"
@@ -372,7 +373,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
         if (!whole && row >= rows) continue;
         const float gate = acc[i][0][r] * g13;
         const float up = acc[i][1][r] * g13;
-        const float a = gate / (1.0f + __expf(-gate)) * up;
+        const float a = gated_act(L.act, gate, up);
         const uint16_t hi = f32_to_bf16_rne(a);
         const int64_t o = (int64_t)(gs + row) * L.I + n;
         act[o] = hi;

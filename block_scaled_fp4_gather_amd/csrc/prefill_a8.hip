@@ -21,6 +21,7 @@
 //                same fp32 rows that the combine sums.
 #include <hip/hip_runtime.h>
 
+#include "act.h"
 #include "gemm_util.h"
 #include "layout.h"
 #include "mxfp8.h"
@@ -239,7 +240,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
       for (int r = 0; r < 16; ++r) {
         const float gate = acc[i][0][r];
         const float up = acc[i][1][r];
-        st[acc_row(r, lane) * kStride + n] = gate * __builtin_amdgcn_rcpf(1.0f + __expf(-gate)) * up;
+        st[acc_row(r, lane) * kStride + n] = gated_act(L.act, gate, up);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging stores are done
       __builtin_amdgcn_wave_barrier();

@@ -34,6 +34,9 @@ PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
 ACT_BF16, ACT_MXFP8 = 0, 1
 ACT_FORMATS = {"bf16": ACT_BF16, "mxfp8": ACT_MXFP8}
 
+FN_SILU, FN_GELU_TANH, FN_SWIGLUOAI = 0, 1, 2
+ACT_FNS = {"silu": FN_SILU, "gelu_tanh": FN_GELU_TANH, "swigluoai": FN_SWIGLUOAI}
+
 
 class Tuning(ctypes.Structure):
     """Launch shape of the decode kernels and the execution path (0 keeps the
@@ -46,13 +49,15 @@ class _Desc(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
-                ("act_format", ctypes.c_int32)]
+                ("act_format", ctypes.c_int32), ("act_fn", ctypes.c_int32),
+                ("act_alpha", ctypes.c_float), ("act_beta", ctypes.c_float), ("act_limit", ctypes.c_float)]
 
 
 @dataclasses.dataclass(frozen=True)
 class Desc:
     """Layer shape; `act` is "bf16" or "mxfp8" (the W4A8-MX variant of the
-    grouped path, MXFP4 weights only)."""
+    grouped path, MXFP4 weights only); `fn` the gated activation ("silu",
+    "gelu_tanh" or "swigluoai" with alpha, beta and limit)."""
     fmt: str
     E: int
     H: int
@@ -60,11 +65,17 @@ class Desc:
     k: int
     max_tokens: int
     act: str = "bf16"
+    fn: str = "silu"
+    alpha: float = 0.0
+    beta: float = 0.0
+    limit: float = 0.0
 
     def c(self) -> _Desc:
         act = ACT_FORMATS.get(self.act, self.act) if isinstance(self.act, str) else self.act
+        fn = ACT_FNS.get(self.fn, self.fn) if isinstance(self.fn, str) else self.fn
         return _Desc(FORMATS.get(self.fmt, self.fmt) if isinstance(self.fmt, str) else self.fmt,
-                     self.E, self.H, self.I, self.k, self.max_tokens, act)
+                     self.E, self.H, self.I, self.k, self.max_tokens, act, fn,
+                     self.alpha, self.beta, self.limit)
 
 
 _lib = None

@@ -80,11 +80,30 @@ typedef enum {
   MOE_FP4_ACT_MXFP8 = 1
 } moe_fp4_act_format;
 
+/* Gated activation a = f(gate, up) between FC1 and FC2.  The pages name
+ * SiLU (b12x PR #22, What: FC2 applies SiLU inline), gelu_tanh and
+ * swigluoai_uninterleave with alpha, beta and limit (flashinfer #4285,
+ * reviews of moe_activation.py and of the direct micro kernel's activation
+ * coverage) without formulas; these are the standard definitions:
+ *   SILU:      gate * sigmoid(gate) * up
+ *   GELU_TANH: 0.5 * gate * (1 + tanh(sqrt(2/pi) * (gate + 0.044715 * gate^3))) * up
+ *   SWIGLUOAI: g = min(gate, limit), u = max(min(up, limit), -limit),
+ *              g * sigmoid(alpha * g) * (u + beta)
+ *              (act_alpha, act_beta finite, act_limit > 0 or +inf; gate and
+ *              up are the separate halves of W13; a NaN passes the clamps)
+ * Every path applies the same function. */
+typedef enum {
+  MOE_FP4_FN_SILU = 0,
+  MOE_FP4_FN_GELU_TANH = 1,
+  MOE_FP4_FN_SWIGLUOAI = 2
+} moe_fp4_act_fn;
+
 /* Shape of one MoE layer.  H and I must be multiples of 32 for both formats
  * (the kernels work in 32-element units); max_tokens is the largest M that
  * later forward calls will pass, used only to size the workspace.
  * act_format is a moe_fp4_act_format (0 keeps bf16 activations); MXFP8 with
- * NVFP4 weights returns MOE_FP4_EUNSUPPORTED. */
+ * NVFP4 weights returns MOE_FP4_EUNSUPPORTED.  act_fn and its parameters
+ * choose the gated activation (0 and zeros: SiLU). */
 typedef struct {
   int32_t format;      /* moe_fp4_format */
   int32_t num_experts; /* E, resident experts; ids outside [0, E) are invalid */
@@ -93,6 +112,10 @@ typedef struct {
   int32_t top_k;       /* k: routes per token */
   int32_t max_tokens;  /* capacity for workspace sizing */
   int32_t act_format;  /* moe_fp4_act_format */
+  int32_t act_fn;      /* moe_fp4_act_fn (0: SiLU) */
+  float act_alpha;     /* SWIGLUOAI only, else ignored */
+  float act_beta;
+  float act_limit;
 } moe_fp4_desc;
 
 /* Human-readable name of a status code (static string). */

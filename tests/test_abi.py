@@ -184,3 +184,20 @@ def test_mxfp8_quantize_rejects_before_launch(L):
     assert q(18, 4, 64, 16, 16, None) == 1      # misaligned input
     assert q(16, 4, 64, 12, 16, None) == 1      # misaligned codes
     assert q(None, 0, 64, None, None, None) == 0  # nothing to do
+
+
+def test_activation_function_validation(L):
+    def status(**kw):
+        n = ctypes.c_size_t()
+        d = moe.Desc("mxfp4", 8, 256, 128, 2, 4, **kw)
+        return L.moe_fp4_workspace_bytes(ctypes.byref(d.c()), 1, ctypes.byref(n))
+
+    assert status(fn="silu") == 0
+    assert status(fn="gelu_tanh") == 0
+    assert status(fn="swigluoai", alpha=1.702, beta=1.0, limit=7.0) == 0
+    assert status(fn="swigluoai", alpha=1.702, beta=1.0, limit=float("inf")) == 0
+    assert status(fn=3) == 1
+    assert status(fn="swigluoai", alpha=1.702, beta=1.0, limit=0.0) == 1       # limit must be > 0
+    assert status(fn="swigluoai", alpha=float("nan"), beta=1.0, limit=7.0) == 1
+    assert status(fn="swigluoai", alpha=1.0, beta=float("inf"), limit=7.0) == 1
+    assert status(fn="swigluoai", alpha=1.0, beta=0.0, limit=float("nan")) == 1
