@@ -7,8 +7,9 @@ this package; the library's product path never does.
 
 Numpy arrays in the logical layout that ``block_scaled_fp4_gather_amd.synth``
 produces go in; fp32 token sums and their bf16 bit patterns come out.  The
-case dict may name a gated activation ("fn": "silu", "gelu_tanh" or
-"swigluoai", with "alpha", "beta", "limit"); SiLU when absent.
+case dict may name the activation ("fn": "silu", "gelu_tanh",
+"swigluoai" with "alpha", "beta", "limit", or "relu2", which is not gated:
+W13 then has I rows); SiLU when absent.
 """
 from __future__ import annotations
 
@@ -23,7 +24,7 @@ _SRC = os.path.join(_HERE, "moe_oracle.cpp")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
 FMT = {"mxfp4": 1, "nvfp4": 2}
-ACT = {"silu": 0, "gelu_tanh": 1, "swigluoai": 2}
+ACT = {"silu": 0, "gelu_tanh": 1, "swigluoai": 2, "relu2": 3}
 
 
 def build(force: bool = True) -> str:
@@ -132,8 +133,8 @@ def activation(fn: str, gate: float, up: float, alpha: float = 0.0, beta: float 
 
 
 def _args(fmt, d):
-    E, twoI, Hh = d["w13_codes"].shape
-    H, I = 2 * Hh, twoI // 2
+    E, _, Hh = d["w13_codes"].shape
+    H, I = 2 * Hh, 2 * d["w2_codes"].shape[2]  # W13 has 2I rows, or I for relu2
     M, k = d["ids"].shape
     arr = {key: np.ascontiguousarray(d[key]) for key in
            ("w13_codes", "w13_scales", "w2_codes", "w2_scales", "x", "w")}

@@ -63,6 +63,10 @@
 //  * swigluoai: g = min(gate, limit), u = clamp(up, -limit, limit),
 //    g * sigmoid(alpha g) * (u + beta), the clamps written as comparisons so
 //    that a NaN passes through; gate and up are the separate halves of W13.
+//  * relu2 is not gated (b12x #311, commit message on the FP4 quantiser, which
+//    keeps relu2 on its exact path because it is not a gated activation; the
+//    survey's reading): W13 then has I rows, h_n = x . W13[n], and
+//    a_n = max(h_n, 0)^2, a NaN passing through.
 //
 // Build: g++ -O2 -ffp-contract=off -shared -fPIC (no fast-math, no FMA
 // contraction, so every product and sum is one IEEE fp32 rounding in the
@@ -199,6 +203,7 @@ double mxfp8_value(uint8_t code, uint8_t scale) {
 const int ACT_SILU = 0;
 const int ACT_GELU_TANH = 1;
 const int ACT_SWIGLUOAI = 2;
+const int ACT_RELU2 = 3;  // not gated: one projection of I rows
 
 struct Act {
   int kind;
@@ -222,7 +227,19 @@ T gated(const Act& a, T g, T u) {
   return g / ((T)1 + std::exp(-g)) * u;
 }
 
-bool valid_act(int kind) { return kind == ACT_SILU || kind == ACT_GELU_TANH || kind == ACT_SWIGLUOAI; }
+// relu(h)^2; NaN stays NaN.
+template <typename T>
+T relu2(T h) {
+  if (h != h) return h;
+  return h > (T)0 ? h * h : (T)0;
+}
+
+bool valid_act(int kind) {
+  return kind == ACT_SILU || kind == ACT_GELU_TANH || kind == ACT_SWIGLUOAI || kind == ACT_RELU2;
+}
+
+// Rows of W13: 2I for the gated activations, I for relu2.
+int w13_rows(int act, int I) { return act == ACT_RELU2 ? I : 2 * I; }
 
 }  // namespace
 
@@ -256,7 +273,7 @@ int oracle_forward_f32(int fmt, int E, int H, int I, int M, int k, const uint8_t
   if (!valid_args(fmt, E, H, I, M, k) || !valid_act(act)) return 1;
   const Act A{act, alpha, beta, limit};
   const int G = block_size(fmt);
-  const size_t w13_cb = (size_t)2 * I * (H / 2), w13_sb = (size_t)2 * I * (H / G);
+  const size_t w13_cb = (size_t)w13_rows(act, I) * (H / 2), w13_sb = (size_t)w13_rows(act, I) * (H / G);
   const size_t w2_cb = (size_t)H * (I / 2), w2_sb = (size_t)H * (I / G);
   std::vector<float> xf(H), grow(H), a(I), acc(H), w2row(I);
   for (int t = 0; t < M; ++t) {
@@ -272,8 +289,14 @@ int oracle_forward_f32(int fmt, int E, int H, int I, int M, int k, const uint8_t
       const uint8_t* s2 = w2_scales + (size_t)e * w2_sb;
       const float gl13 = fmt == FMT_NVFP4 ? g13[e] : 1.0f;
       const float gl2 = fmt == FMT_NVFP4 ? g2[e] : 1.0f;
-      // FC1 and activation: a[n] = silu(gate_n) * up_n.
-      for (int n = 0; n < I; ++n) {
+      // FC1 and activation: a[n] = f(gate_n, up_n), or relu2(h_n) (not gated).
+      for (int n = 0; n < I && act == ACT_RELU2; ++n) {
+        float h1 = 0.0f;
+        for (int h = 0; h < H; ++h) grow[h] = weight(fmt, c13, s13, gl13, H, n, h);
+        for (int h = 0; h < H; ++h) h1 += xf[h] * grow[h];
+        a[n] = relu2<float>(h1);
+      }
+      for (int n = 0; n < I && act != ACT_RELU2; ++n) {
         float gate = 0.0f, up = 0.0f;
         for (int h = 0; h < H; ++h) grow[h] = weight(fmt, c13, s13, gl13, H, n, h);
         for (int h = 0; h < H; ++h) gate += xf[h] * grow[h];
@@ -308,7 +331,7 @@ int oracle_forward_f64(int fmt, int E, int H, int I, int M, int k, const uint8_t
   if (!valid_args(fmt, E, H, I, M, k) || !valid_act(act)) return 1;
   const Act A{act, alpha, beta, limit};
   const int G = block_size(fmt);
-  const size_t w13_cb = (size_t)2 * I * (H / 2), w13_sb = (size_t)2 * I * (H / G);
+  const size_t w13_cb = (size_t)w13_rows(act, I) * (H / 2), w13_sb = (size_t)w13_rows(act, I) * (H / G);
   const size_t w2_cb = (size_t)H * (I / 2), w2_sb = (size_t)H * (I / G);
   std::vector<double> a(I);
   for (int t = 0; t < M; ++t) {
@@ -324,9 +347,10 @@ int oracle_forward_f64(int fmt, int E, int H, int I, int M, int k, const uint8_t
         for (int h = 0; h < H; ++h) {
           const double xv = bf16_to_f32(x[(size_t)t * H + h]);
           gate += xv * weight(fmt, w13_codes + e * w13_cb, w13_scales + e * w13_sb, gl13, H, n, h);
-          up += xv * weight(fmt, w13_codes + e * w13_cb, w13_scales + e * w13_sb, gl13, H, I + n, h);
+          if (act != ACT_RELU2)
+            up += xv * weight(fmt, w13_codes + e * w13_cb, w13_scales + e * w13_sb, gl13, H, I + n, h);
         }
-        a[n] = gated<double>(A, gate, up);
+        a[n] = act == ACT_RELU2 ? relu2<double>(gate) : gated<double>(A, gate, up);
       }
       for (int h = 0; h < H; ++h) {
         double y = 0.0;
@@ -339,8 +363,10 @@ int oracle_forward_f64(int fmt, int E, int H, int I, int M, int k, const uint8_t
   return 0;
 }
 
-// The gated activation in fp64 (act: 0 SiLU, 1 gelu_tanh, 2 swigluoai).
+// The activation in fp64 (act: 0 SiLU, 1 gelu_tanh, 2 swigluoai, 3 relu2,
+// which takes `gate` as its one input and ignores `up`).
 double oracle_activation(int act, double alpha, double beta, double limit, double gate, double up) {
+  if (act == ACT_RELU2) return relu2<double>(gate);
   return gated<double>(Act{act, alpha, beta, limit}, gate, up);
 }
 
@@ -376,7 +402,7 @@ int oracle_forward_w4a8(int fmt, int E, int H, int I, int M, int k, const uint8_
   (void)g2;
   if (fmt != FMT_MXFP4 || !valid_args(fmt, E, H, I, M, k) || !valid_act(act)) return 1;
   const Act A{act, alpha, beta, limit};
-  const size_t w13_cb = (size_t)2 * I * (H / 2), w13_sb = (size_t)2 * I * (H / 32);
+  const size_t w13_cb = (size_t)w13_rows(act, I) * (H / 2), w13_sb = (size_t)w13_rows(act, I) * (H / 32);
   const size_t w2_cb = (size_t)H * (I / 2), w2_sb = (size_t)H * (I / 32);
   std::vector<float> xf(H), af(I);
   std::vector<uint8_t> xc(H), ac(I), xs(H / 32), as(I / 32);
@@ -396,10 +422,10 @@ int oracle_forward_w4a8(int fmt, int E, int H, int I, int M, int k, const uint8_
         double gate = 0.0, up = 0.0;
         for (int h = 0; h < H; ++h) {
           gate += xq[h] * weight(fmt, c13, s13, 1.0f, H, n, h);
-          up += xq[h] * weight(fmt, c13, s13, 1.0f, H, I + n, h);
+          if (act != ACT_RELU2) up += xq[h] * weight(fmt, c13, s13, 1.0f, H, I + n, h);
         }
         const double g = (float)gate, u = (float)up;
-        af[n] = (float)gated<double>(A, g, u);
+        af[n] = (float)(act == ACT_RELU2 ? relu2<double>(g) : gated<double>(A, g, u));
       }
       if (quant_act) {
         oracle_mxfp8_quantize(af.data(), 1, I, ac.data(), as.data());

@@ -97,3 +97,53 @@ def test_unknown_activation_rejected(oracle_lib):
     d["fn"] = 7
     with pytest.raises(ValueError):
         oracle_lib.forward_f64("mxfp4", d)
+
+
+def test_relu2_matches_torch(oracle_lib):
+    got = np.array([oracle_lib.activation("relu2", g, 123.0) for g in PTS])
+    want = (F.relu(torch.from_numpy(PTS)) ** 2).numpy()
+    assert np.array_equal(got, want)
+    assert math.isnan(oracle_lib.activation("relu2", math.nan, 0.0))
+
+
+def _relu2_case(rng, fmt, E, H, I, M, k):
+    """A layer whose W13 has I rows (relu2 is not gated)."""
+    from pins_util import bf16_bits, make_matrix
+    c13, s13, v13 = make_matrix(rng, fmt, (E, I), H, 1.0 / 512)
+    c2, s2, v2 = make_matrix(rng, fmt, (E, H), I, 1.0 / 512)
+    d = dict(w13_codes=c13, w13_scales=s13, w2_codes=c2, w2_scales=s2,
+             x=bf16_bits(rng.standard_normal((M, H)).astype(np.float32)),
+             ids=rng.integers(0, E, size=(M, k)).astype(np.int32), w=rng.random((M, k)).astype(np.float32),
+             g13=np.full(E, 1.0 / 512, np.float32) if fmt == "nvfp4" else None,
+             g2=np.full(E, 1.0 / 512, np.float32) if fmt == "nvfp4" else None, fn="relu2")
+    return d, v13, v2
+
+
+def _relu2_textbook(v13, v2, x, ids, w):
+    M, k = ids.shape
+    out = np.zeros((M, v2.shape[1]))
+    for t in range(M):
+        for j in range(k):
+            e = int(ids[t, j])
+            if 0 <= e < v13.shape[0]:
+                h = v13[e].astype(np.float64) @ x[t].astype(np.float64)
+                out[t] += float(w[t, j]) * (v2[e].astype(np.float64) @ (F.relu(torch.from_numpy(h)) ** 2).numpy())
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_relu2_layer_is_textbook_non_gated_mlp(oracle_lib, fmt):
+    rng = np.random.default_rng(17)
+    d, v13, v2 = _relu2_case(rng, fmt, 5, 96, 64, 3, 3)
+    d["ids"][1, 2] = -1
+    ref = _relu2_textbook(v13, v2, bits_to_f32(d["x"]), d["ids"], d["w"])
+    scale = np.abs(ref).max()
+    assert np.abs(oracle_lib.forward_f64(fmt, d) - ref).max() <= 1e-12 * scale
+    acc, _ = oracle_lib.forward_f32(fmt, d)
+    assert np.abs(acc - ref).max() <= 2e-5 * scale
+    if fmt == "mxfp4":
+        from test_oracle_w4a8_pins import decode
+        xc, xs = oracle_lib.mxfp8_quantize(bits_to_f32(d["x"]))
+        ref_q = _relu2_textbook(v13, v2, decode(xc, xs), d["ids"], d["w"])
+        got = oracle_lib.forward_w4a8(fmt, d, quant_act=False)
+        assert np.abs(got - ref_q).max() <= 1e-6 * np.abs(ref_q).max()
