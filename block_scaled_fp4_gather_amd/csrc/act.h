@@ -8,7 +8,8 @@
 //   swigluoai:  g = min(gate, limit), u = clamp(up, -limit, limit),
 //               g * sigmoid(alpha * g) * (u + beta)
 // (gate and up are separate halves of W13, not interleaved).  The clamps
-// are comparisons, so a NaN passes through them.
+// are comparisons, so a NaN passes through them.  relu2 is not gated:
+// max(h, 0)^2 of each FC1 output on its own (relu2()).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,5 +31,8 @@ __device__ __forceinline__ float gated_act(const ActParams& p, float g, float u)
   }
   return g / (1.0f + __expf(-g)) * u;
 }
+
+// relu(h)^2, NaN passing through.
+__device__ __forceinline__ float relu2(float h) { return h != h ? h : (h > 0.0f ? h * h : 0.0f); }
 
 }  // namespace moe

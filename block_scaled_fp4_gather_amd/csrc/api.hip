@@ -28,12 +28,15 @@ moe_fp4_status desc_layout(const moe_fp4_desc* d, Layout* L) {
   if ((int64_t)d->hidden * d->inter > (int64_t)1 << 30) return MOE_FP4_EUNSUPPORTED;
   if (d->act_format != MOE_FP4_ACT_BF16 && d->act_format != MOE_FP4_ACT_MXFP8) return MOE_FP4_EINVAL;
   if (d->act_format == MOE_FP4_ACT_MXFP8 && d->format != MOE_FP4_MXFP4) return MOE_FP4_EUNSUPPORTED;
-  if (d->act_fn != MOE_FP4_FN_SILU && d->act_fn != MOE_FP4_FN_GELU_TANH && d->act_fn != MOE_FP4_FN_SWIGLUOAI)
+  if (d->act_fn != MOE_FP4_FN_SILU && d->act_fn != MOE_FP4_FN_GELU_TANH && d->act_fn != MOE_FP4_FN_SWIGLUOAI &&
+      d->act_fn != MOE_FP4_FN_RELU2)
     return MOE_FP4_EINVAL;
+  const bool gated = d->act_fn != MOE_FP4_FN_RELU2;
+  if (!gated && d->inter % 64) return MOE_FP4_EUNSUPPORTED;  // two 32-row halves per FC1 tile
   if (d->act_fn == MOE_FP4_FN_SWIGLUOAI &&
       (!std::isfinite(d->act_alpha) || !std::isfinite(d->act_beta) || !(d->act_limit > 0.0f)))
     return MOE_FP4_EINVAL;
-  if (!moe::make_layout(d->format, d->num_experts, d->hidden, d->inter, L)) return MOE_FP4_EINVAL;
+  if (!moe::make_layout(d->format, d->num_experts, d->hidden, d->inter, L, gated)) return MOE_FP4_EINVAL;
   L->act = moe::ActParams{d->act_fn, d->act_alpha, d->act_beta, d->act_limit};
   return MOE_FP4_OK;
 }

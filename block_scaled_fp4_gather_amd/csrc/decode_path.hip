@@ -293,13 +293,20 @@ __global__ void __launch_bounds__(1024)
       }
       gate *= g13;
       up *= g13;
-      const float a = gated_act(L.act, gate, up);
       // a = hi + lo in two bf16 planes: 16 significant bits for FC2's bf16
       // dot products.
-      const uint16_t hi = f32_to_bf16_rne(a);
       const int64_t at = (int64_t)(t * k + __builtin_ctzll(tm)) * L.I + 32 * b + blk * (R / 2) + lane;
-      act_hi[at] = hi;
-      act_lo[at] = f32_to_bf16_rne(a - __uint_as_float((uint32_t)hi << 16));
+      auto put = [&](int64_t o, float a) {
+        const uint16_t hi = f32_to_bf16_rne(a);
+        act_hi[o] = hi;
+        act_lo[o] = f32_to_bf16_rne(a - __uint_as_float((uint32_t)hi << 16));
+      };
+      if (L.act.kind == kActRelu2) {  // not gated: both halves are outputs
+        put(at, relu2(gate));
+        put(at + L.Ip, relu2(up));
+      } else {
+        put(at, gated_act(L.act, gate, up));
+      }
     }
     ++ti;
   }

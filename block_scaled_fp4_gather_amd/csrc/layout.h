@@ -16,7 +16,9 @@
 //   scales: [group q][lane l][4 B]    -> bytes 4q..4q+3 of row l's scale row
 // FC1 tile b of an expert holds gate rows 32b..32b+31 in lanes 0..31 and the
 // matching up rows I+32b..I+32b+31 in lanes 32..63, so SiLU(gate)*up pairs
-// lane l with lane l+32.  FC2 tile hb holds rows 64hb..64hb+63 of W2 (rows
+// lane l with lane l+32.  With a non-gated activation (relu2) W13 has I rows,
+// and tile b holds rows 32b.. and I/2+32b.. of it the same way (Ip = I/2
+// row pairs instead of I), two independent outputs per lane pair.  FC2 tile hb holds rows 64hb..64hb+63 of W2 (rows
 // past H are zero padding).  Padding bytes are zero and are never read as
 // weights of a real row.
 //
@@ -36,7 +38,7 @@ namespace moe {
 enum { kMXFP4 = 1, kNVFP4 = 2 };
 
 // Gated activation applied to (gate, up) in the FC1 epilogues.
-enum { kActSilu = 0, kActGeluTanh = 1, kActSwigluOai = 2 };
+enum { kActSilu = 0, kActGeluTanh = 1, kActSwigluOai = 2, kActRelu2 = 3 };
 struct ActParams {
   int32_t kind;
   float alpha, beta, limit;  // kActSwigluOai only
@@ -44,10 +46,11 @@ struct ActParams {
 
 struct Layout {
   int32_t fmt, E, H, I;
+  int32_t Ip;       // FC1 row pairs per expert: I (gated), I / 2 (relu2)
   int32_t G;        // elements per scale byte
   int32_t nC1;      // FC1 chunks per row (H/32)
   int32_t nC2;      // FC2 chunks per row (I/32)
-  int32_t nB1;      // FC1 tiles per expert (I/32)
+  int32_t nB1;      // FC1 tiles per expert (Ip/32)
   int32_t nB2;      // FC2 tiles per expert (ceil(H/64))
   int32_t nQ1;      // FC1 scale dwords per lane (ceil(H/G/4))
   int32_t nQ2;      // FC2 scale dwords per lane (ceil(I/G/4))
@@ -62,10 +65,13 @@ struct Layout {
 
 MOE_HD inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-// Returns false when the shape is outside what the layout supports.
-MOE_HD inline bool make_layout(int32_t fmt, int32_t E, int32_t H, int32_t I, Layout* L) {
+// Returns false when the shape is outside what the layout supports.  W13
+// has 2I rows when `gated`, I rows (I a multiple of 64) otherwise.
+MOE_HD inline bool make_layout(int32_t fmt, int32_t E, int32_t H, int32_t I, Layout* L, bool gated = true) {
   if (fmt != kMXFP4 && fmt != kNVFP4) return false;
   if (E <= 0 || H <= 0 || I <= 0 || H % 32 || I % 32) return false;
+  if (!gated && I % 64) return false;
+  L->Ip = gated ? I : I / 2;
   L->fmt = fmt;
   L->E = E;
   L->H = H;
@@ -73,7 +79,7 @@ MOE_HD inline bool make_layout(int32_t fmt, int32_t E, int32_t H, int32_t I, Lay
   L->G = fmt == kMXFP4 ? 32 : 16;
   L->nC1 = H / 32;
   L->nC2 = I / 32;
-  L->nB1 = I / 32;
+  L->nB1 = L->Ip / 32;
   L->nB2 = (H + 63) / 64;
   L->nQ1 = (H / L->G + 3) / 4;
   L->nQ2 = (I / L->G + 3) / 4;
@@ -89,7 +95,7 @@ MOE_HD inline bool make_layout(int32_t fmt, int32_t E, int32_t H, int32_t I, Lay
 
 // Logical FC1 row held by lane l of FC1 tile b.
 MOE_HD inline int32_t fc1_row(const Layout& L, int32_t b, int32_t l) {
-  return l < 32 ? 32 * b + l : L.I + 32 * b + (l - 32);
+  return l < 32 ? 32 * b + l : L.Ip + 32 * b + (l - 32);
 }
 
 MOE_HD inline int64_t fc1_tile_offset(const Layout& L, int32_t e, int32_t b) {

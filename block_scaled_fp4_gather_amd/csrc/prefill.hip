@@ -373,11 +373,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
         if (!whole && row >= rows) continue;
         const float gate = acc[i][0][r] * g13;
         const float up = acc[i][1][r] * g13;
-        const float a = gated_act(L.act, gate, up);
-        const uint16_t hi = f32_to_bf16_rne(a);
         const int64_t o = (int64_t)(gs + row) * L.I + n;
-        act[o] = hi;
-        act[plane + o] = f32_to_bf16_rne(a - __uint_as_float((uint32_t)hi << 16));
+        auto put = [&](int64_t at, float a) {
+          const uint16_t hi = f32_to_bf16_rne(a);
+          act[at] = hi;
+          act[plane + at] = f32_to_bf16_rne(a - __uint_as_float((uint32_t)hi << 16));
+        };
+        if (L.act.kind == kActRelu2) {  // not gated: both halves are outputs
+          put(o, relu2(gate));
+          put(o + L.Ip, relu2(up));
+        } else {
+          put(o, gated_act(L.act, gate, up));
+        }
       }
     }
   };

@@ -223,56 +223,61 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     rowp[blk] = xq + (int64_t)(perm[gs + r] / k) * L.H;
   }
   const uint8_t* srow = xs + (int64_t)(perm[gs + min(32 * wave + (lane & 31), rows - 1)] / k) * xss;
-  // Epilogue, per 32-row block: a = SiLU(gate) * up in fp32 goes to this
-  // wave's part of the (now idle) A ring as 32 rows x 32 columns (row stride
-  // 144 B), then lane l takes row l / 2, columns 16 (l % 2) .. + 15: the
-  // block maximum is its own 16 values and its neighbour's, and its 16 codes
-  // leave in one 16-byte store.
+  // Epilogue, per 32-row block: a = f(gate, up) in fp32 goes to this wave's
+  // part of the (now idle) A ring as 32 rows x 32 columns (row stride 144 B),
+  // then lane l takes row l / 2, columns 16 (l % 2) .. + 15: the block
+  // maximum is its own 16 values and its neighbour's, and its 16 codes leave
+  // in one 16-byte store.  A non-gated activation (relu2) makes two such
+  // blocks per row block, columns 32b.. from the first accumulator and
+  // Ip + 32b.. from the second.
   auto epilogue = [&](auto& acc) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
     constexpr int kStride = 36;  // dwords per staged row
     float* st = (float*)(smem + wave * 32 * kStride * 4);
     const int n = lane & 31;
     const int rr = lane >> 1, half = lane & 1;
+    const bool gated = L.act.kind != kActRelu2;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float gate = acc[i][0][r];
-        const float up = acc[i][1][r];
-        st[acc_row(r, lane) * kStride + n] = gated_act(L.act, gate, up);
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging stores are done
-      __builtin_amdgcn_wave_barrier();
-      float v[16];
+      for (int jj = 0; jj < 2; ++jj) {
+        if (jj == 1 && gated) break;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 f = *(const float4*)(st + rr * kStride + 16 * half + 4 * q);
-        v[4 * q] = f.x;
-        v[4 * q + 1] = f.y;
-        v[4 * q + 2] = f.z;
-        v[4 * q + 3] = f.w;
-      }
-      uint32_t m = 0;
+        for (int r = 0; r < 16; ++r)
+          st[acc_row(r, lane) * kStride + n] = gated ? gated_act(L.act, acc[i][0][r], acc[i][1][r]) : relu2(acc[i][jj][r]);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging stores are done
+        __builtin_amdgcn_wave_barrier();
+        float v[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) m = max(m, __float_as_uint(v[q]) & 0x7FFFFFFFu);
-      m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-      const uint32_t sb = mx_scale_byte(m);
-      uint32_t w[4] = {0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
-      if (sb != 255u) {
-        const float inv = mx_inv_scale(sb);
+        for (int q = 0; q < 4; ++q) {
+          const float4 f = *(const float4*)(st + rr * kStride + 16 * half + 4 * q);
+          v[4 * q] = f.x;
+          v[4 * q + 1] = f.y;
+          v[4 * q + 2] = f.z;
+          v[4 * q + 3] = f.w;
+        }
+        uint32_t m = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          w[q] = e4m3_code(v[4 * q] * inv) | (e4m3_code(v[4 * q + 1] * inv) << 8) |
-                 (e4m3_code(v[4 * q + 2] * inv) << 16) | (e4m3_code(v[4 * q + 3] * inv) << 24);
+        for (int q = 0; q < 16; ++q) m = max(m, __float_as_uint(v[q]) & 0x7FFFFFFFu);
+        m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+        const uint32_t sb = mx_scale_byte(m);
+        uint32_t w[4] = {0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+        if (sb != 255u) {
+          const float inv = mx_inv_scale(sb);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            w[q] = e4m3_code(v[4 * q] * inv) | (e4m3_code(v[4 * q + 1] * inv) << 8) |
+                   (e4m3_code(v[4 * q + 2] * inv) << 16) | (e4m3_code(v[4 * q + 3] * inv) << 24);
+        }
+        const int row = i * 32 + rr;
+        const int col0 = (jj ? L.Ip : 0) + 32 * b;
+        if (row < rows) {
+          *(uint4*)(aq + (int64_t)(gs + row) * L.I + col0 + 16 * half) = make_uint4(w[0], w[1], w[2], w[3]);
+          if (half == 0) as[(int64_t)(gs + row) * ass + col0 / 32] = (uint8_t)sb;
+        }
+        __builtin_amdgcn_wave_barrier();  // the next block's stores come after these reads
+        __builtin_amdgcn_s_waitcnt(0xC07F);
       }
-      const int row = i * 32 + rr;
-      if (row < rows) {
-        *(uint4*)(aq + (int64_t)(gs + row) * L.I + 32 * b + 16 * half) = make_uint4(w[0], w[1], w[2], w[3]);
-        if (half == 0) as[(int64_t)(gs + row) * ass + b] = (uint8_t)sb;
-      }
-      __builtin_amdgcn_wave_barrier();  // the next block's stores come after these reads
-      __builtin_amdgcn_s_waitcnt(0xC07F);
     }
   };
   gemm_rows_a8(rows, rowp, srow, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, smem, epilogue);

@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(256) repack_kernel(Layout L, PrepShape P, int 
   const int lane = r2 % 64;
   const int slot = r2 / 64;  // chunk (< nC) or scale word (>= nC)
   const int cols = fc1 ? L.H : L.I;
-  const int rows = fc1 ? 2 * L.I : L.H;
+  const int rows = fc1 ? 2 * L.Ip : L.H;
   const int row = fc1 ? fc1_row(L, tile, lane) : tile * 64 + lane;
   const int64_t toff = fc1 ? fc1_tile_offset(L, e, tile) : fc2_tile_offset(L, e, tile);
   const bool real = row < rows;
@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(256) export_kernel(Layout L, int e, int which,
                                                      const uint8_t* __restrict__ prep,
                                                      float* __restrict__ out) {
   const bool fc1 = which == 0;
-  const int rows = fc1 ? 2 * L.I : L.H;
+  const int rows = fc1 ? 2 * L.Ip : L.H;
   const int nC = fc1 ? L.nC1 : L.nC2;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)rows * nC) return;
@@ -101,8 +101,8 @@ __global__ void __launch_bounds__(256) export_kernel(Layout L, int e, int which,
   int tile, lane;
   int64_t toff;
   if (fc1) {
-    const bool up = row >= L.I;
-    const int n = up ? row - L.I : row;
+    const bool up = row >= L.Ip;
+    const int n = up ? row - L.Ip : row;
     tile = n / 32;
     lane = (up ? 32 : 0) + n % 32;
     toff = fc1_tile_offset(L, e, tile);
@@ -168,7 +168,7 @@ hipError_t launch_repack(const Layout& L, int dir, uint8_t* w13c, uint8_t* w13s,
 
 hipError_t launch_export(const Layout& L, int e, int which, const uint8_t* prep, float* out,
                          hipStream_t st) {
-  const int rows = which == 0 ? 2 * L.I : L.H;
+  const int rows = which == 0 ? 2 * L.Ip : L.H;
   const int nC = which == 0 ? L.nC1 : L.nC2;
   const int64_t n = (int64_t)rows * nC;
   hipLaunchKernelGGL(export_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, L, e, which,

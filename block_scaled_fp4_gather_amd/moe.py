@@ -34,8 +34,8 @@ PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
 ACT_BF16, ACT_MXFP8 = 0, 1
 ACT_FORMATS = {"bf16": ACT_BF16, "mxfp8": ACT_MXFP8}
 
-FN_SILU, FN_GELU_TANH, FN_SWIGLUOAI = 0, 1, 2
-ACT_FNS = {"silu": FN_SILU, "gelu_tanh": FN_GELU_TANH, "swigluoai": FN_SWIGLUOAI}
+FN_SILU, FN_GELU_TANH, FN_SWIGLUOAI, FN_RELU2 = 0, 1, 2, 3
+ACT_FNS = {"silu": FN_SILU, "gelu_tanh": FN_GELU_TANH, "swigluoai": FN_SWIGLUOAI, "relu2": FN_RELU2}
 
 
 class Tuning(ctypes.Structure):
@@ -56,8 +56,9 @@ class _Desc(ctypes.Structure):
 @dataclasses.dataclass(frozen=True)
 class Desc:
     """Layer shape; `act` is "bf16" or "mxfp8" (the W4A8-MX variant of the
-    grouped path, MXFP4 weights only); `fn` the gated activation ("silu",
-    "gelu_tanh" or "swigluoai" with alpha, beta and limit)."""
+    grouped path, MXFP4 weights only); `fn` the activation ("silu",
+    "gelu_tanh", "swigluoai" with alpha, beta and limit, or the non-gated
+    "relu2", whose W13 has I rows)."""
     fmt: str
     E: int
     H: int

@@ -19,7 +19,7 @@
  * review of tiny_decode.py); a token with no valid route yields +0.
  *
  * Logical weight layout (the input of moe_fp4_prepare), row-major, G = 32
- * (MXFP4) or 16 (NVFP4):
+ * (MXFP4) or 16 (NVFP4), for the gated activations (relu2: W13 has I rows):
  *   w13_codes  u8[E][2I][H/2]  rows [0, I) gate, [I, 2I) up; element 2b of a
  *                              row in the low nibble of byte b, 2b+1 in the high
  *   w13_scales u8[E][2I][H/G]
@@ -91,11 +91,17 @@ typedef enum {
  *              g * sigmoid(alpha * g) * (u + beta)
  *              (act_alpha, act_beta finite, act_limit > 0 or +inf; gate and
  *              up are the separate halves of W13; a NaN passes the clamps)
+ *   RELU2:     not gated (b12x PR #311, commit message on the FP4 quantiser,
+ *              which treats relu2 apart from the gated activations): W13 has
+ *              I rows (w13_codes u8[E][I][H/2], w13_scales u8[E][I][H/G]),
+ *              h = x . W13[n] and a_n = max(h, 0)^2; I must be a multiple
+ *              of 64 (else MOE_FP4_EUNSUPPORTED)
  * Every path applies the same function. */
 typedef enum {
   MOE_FP4_FN_SILU = 0,
   MOE_FP4_FN_GELU_TANH = 1,
-  MOE_FP4_FN_SWIGLUOAI = 2
+  MOE_FP4_FN_SWIGLUOAI = 2,
+  MOE_FP4_FN_RELU2 = 3
 } moe_fp4_act_fn;
 
 /* Shape of one MoE layer.  H and I must be multiples of 32 for both formats

@@ -196,8 +196,24 @@ def test_activation_function_validation(L):
     assert status(fn="gelu_tanh") == 0
     assert status(fn="swigluoai", alpha=1.702, beta=1.0, limit=7.0) == 0
     assert status(fn="swigluoai", alpha=1.702, beta=1.0, limit=float("inf")) == 0
-    assert status(fn=3) == 1
+    assert status(fn=4) == 1                                                # no such activation
+    assert status(fn=-1) == 1
     assert status(fn="swigluoai", alpha=1.702, beta=1.0, limit=0.0) == 1       # limit must be > 0
     assert status(fn="swigluoai", alpha=float("nan"), beta=1.0, limit=7.0) == 1
     assert status(fn="swigluoai", alpha=1.0, beta=float("inf"), limit=7.0) == 1
     assert status(fn="swigluoai", alpha=1.0, beta=0.0, limit=float("nan")) == 1
+
+
+def test_relu2_layout_and_validation(L):
+    def status(I):
+        n = ctypes.c_size_t()
+        return L.moe_fp4_prepared_bytes(ctypes.byref(moe.Desc("mxfp4", 8, 256, I, 2, 4, fn="relu2").c()),
+                                        ctypes.byref(n))
+    assert status(128) == 0
+    assert status(96) == 2     # I must hold two 32-row halves per FC1 tile
+    gated = moe.prepared_bytes(moe.Desc("mxfp4", 8, 256, 128, 2, 4))
+    non_gated = moe.prepared_bytes(moe.Desc("mxfp4", 8, 256, 128, 2, 4, fn="relu2"))
+    # W13 holds I rows instead of 2I: the FC1 part of every expert halves
+    E, H, I = 8, 256, 128
+    fc1_gated = 2 * I * (H // 2 + H // 32)
+    assert gated - non_gated == E * fc1_gated // 2
