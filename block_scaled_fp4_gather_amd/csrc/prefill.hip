@@ -362,31 +362,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
   }
   const float g13 = FMT == kNVFP4 ? ((const float*)prep)[e] : 1.0f;
   const int n = 32 * b + (lane & 31);
+  // a = f(gate, up) as hi/lo bf16 planes; a non-gated activation (relu2)
+  // writes both halves as outputs, at columns n and Ip + n.
   auto epilogue = [&](auto& acc) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
+    with_act_kind(L.act.kind, [&](auto kind) {
+      constexpr int K = decltype(kind)::value;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const bool whole = i * 32 + 32 <= rows;
+      for (int i = 0; i < NB; ++i) {
+        const bool whole = i * 32 + 32 <= rows;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + acc_row(r, lane);
-        if (!whole && row >= rows) continue;
-        const float gate = acc[i][0][r] * g13;
-        const float up = acc[i][1][r] * g13;
-        const int64_t o = (int64_t)(gs + row) * L.I + n;
-        auto put = [&](int64_t at, float a) {
+        for (int r = 0; r < 16; ++r) {
+          const int row = i * 32 + acc_row(r, lane);
+          if (!whole && row >= rows) continue;
+          const float gate = acc[i][0][r] * g13;
+          const float up = acc[i][1][r] * g13;
+          const int64_t o = (int64_t)(gs + row) * L.I + n;
+          const float a = act_of<K>(L.act, gate, up);
           const uint16_t hi = f32_to_bf16_rne(a);
-          act[at] = hi;
-          act[plane + at] = f32_to_bf16_rne(a - __uint_as_float((uint32_t)hi << 16));
-        };
-        if (L.act.kind == kActRelu2) {  // not gated: both halves are outputs
-          put(o, relu2(gate));
-          put(o + L.Ip, relu2(up));
-        } else {
-          put(o, gated_act(L.act, gate, up));
+          act[o] = hi;
+          act[plane + o] = f32_to_bf16_rne(a - __uint_as_float((uint32_t)hi << 16));
+          if constexpr (K == kActRelu2) {
+            const float a2 = act_of<K>(L.act, up, 0.0f);
+            const uint16_t hi2 = f32_to_bf16_rne(a2);
+            act[o + L.Ip] = hi2;
+            act[plane + o + L.Ip] = f32_to_bf16_rne(a2 - __uint_as_float((uint32_t)hi2 << 16));
+          }
         }
       }
-    }
+    });
   };
   gemm_rows<FMT>(rows, rowp, 0, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, L.nC1, smem,
                  epilogue);

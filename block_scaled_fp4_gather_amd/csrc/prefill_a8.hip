@@ -236,15 +236,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     float* st = (float*)(smem + wave * 32 * kStride * 4);
     const int n = lane & 31;
     const int rr = lane >> 1, half = lane & 1;
-    const bool gated = L.act.kind != kActRelu2;
+    with_act_kind(L.act.kind, [&](auto kind) {
+    constexpr int K = decltype(kind)::value;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        if (jj == 1 && gated) break;
+      for (int jj = 0; jj < (K == kActRelu2 ? 2 : 1); ++jj) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          st[acc_row(r, lane) * kStride + n] = gated ? gated_act(L.act, acc[i][0][r], acc[i][1][r]) : relu2(acc[i][jj][r]);
+          st[acc_row(r, lane) * kStride + n] =
+              K == kActRelu2 ? act_of<K>(L.act, acc[i][jj][r], 0.0f) : act_of<K>(L.act, acc[i][0][r], acc[i][1][r]);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging stores are done
         __builtin_amdgcn_wave_barrier();
         float v[16];
@@ -279,6 +280,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
         __builtin_amdgcn_s_waitcnt(0xC07F);
       }
     }
+    });
   };
   gemm_rows_a8(rows, rowp, srow, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, smem, epilogue);
 }
