@@ -112,3 +112,29 @@ def test_relu2_w4a8_and_prepare_round_trip():
     torch.cuda.synchronize()
     want = oracle.dequant("mxfp4", d["w13_codes"][3], d["w13_scales"][3])
     assert np.array_equal(out.cpu().numpy(), want)
+
+
+def test_activations_at_full_sizes_sampled():
+    """Each activation on a full-size geometry: gelu_tanh on the E512/H2560/I320
+    NVFP4 decode layer (M = 1, top-10), swigluoai on the H7168/I256 MXFP4
+    shard at 96 tokens through both grouped paths, checked on sampled tokens."""
+    from block_scaled_fp4_gather_amd import synth
+    wl = synth.WORKLOADS["nvfp4_decode_e512"]
+    d = synth.generate(wl)
+    d.update(fn="gelu_tanh", alpha=0.0, beta=0.0, limit=0.0)
+    acc, _ = oracle.forward_f32(wl.fmt, d)
+    layer = _layer(wl.fmt, d, wl.k, wl.M)
+    compare(run_layer(layer, d), acc, "E512 NVFP4 decode, gelu_tanh")
+    wl = synth.WORKLOADS["mxfp4_shard_e256_m4"].replace(M=96)
+    d = synth.generate(wl)
+    d.update(fn="swigluoai", alpha=1.702, beta=1.0, limit=7.0)
+    sample = np.array([0, 17, 95])
+    sub = dict(d, x=d["x"][sample], ids=d["ids"][sample], w=d["w"][sample])
+    for act in ("bf16", "mxfp8"):
+        layer = _layer(wl.fmt, d, wl.k, wl.M, act=act)
+        got = run_layer(layer, d)[sample]
+        if act == "bf16":
+            compare(got, oracle.forward_f32(wl.fmt, sub)[0], "H7168/I256 M96 swigluoai, grouped bf16")
+        else:
+            compare(got, oracle.forward_w4a8(wl.fmt, sub), "H7168/I256 M96 swigluoai, grouped mxfp8",
+                    maxabs=W4A8_MAXABS_REL_RMS)

@@ -203,3 +203,15 @@ def test_w4a8_act_codes_through_identity_down_projection():
     step = np.maximum(np.abs(g), np.abs(r)) / 8 + X * 2.0 ** -9
     assert np.all(np.abs(g - r)[diff] <= step[diff] * (1 + 1e-12))
     assert np.all((np.sign(g) * np.sign(r))[diff] >= 0)
+
+
+def test_w4a8_shard_geometry_sampled():
+    """The H7168/I256 MXFP4 shard geometry (56 FC1 steps, FC2 K of two steps)
+    at 300 tokens, top-8, MXFP8 activations; sampled tokens."""
+    wl = synth.WORKLOADS["mxfp4_shard_e256_m4"].replace(M=300)
+    d = synth.generate(wl)
+    layer = make_layer(wl.fmt, d, wl.k, wl.M, act="mxfp8")
+    got = run_layer(layer, d)
+    sample = np.array([0, 1, 150, 299])
+    sub = dict(d, x=d["x"][sample], ids=d["ids"][sample], w=d["w"][sample])
+    compare(got[sample], oracle.forward_w4a8(wl.fmt, sub), "E256/H7168/I256 M300 w4a8 sampled")
