@@ -242,3 +242,42 @@ def test_grouped_nvfp4_decode_geometry_many_tokens():
     sample = np.array([0, 1, 100, 257, 511])
     acc, _ = oracle.forward_f32(wl.fmt, dict(d, x=d["x"][sample], ids=d["ids"][sample], w=d["w"][sample]))
     compare(got[sample], acc, "nvfp4 E64/H2560/I320 M512 k10 sampled")
+
+
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_grouped_at_the_route_limit(act):
+    """Exactly 2^22 routes (2^20 tokens, top-4), the most the grouped path
+    takes: grouped-row indexes and workspace offsets at their largest.
+    Sampled tokens against the oracle, including the last one."""
+    rng = np.random.default_rng(37)
+    E, H, I, M, k = 16, 64, 32, 1 << 20, 4
+    d, _, _ = random_case(rng, "mxfp4", E, H, I, 8, k)   # weights; tokens drawn below
+    d["x"] = rng.integers(0, 1 << 16, size=(M, H), dtype=np.uint16)
+    d["x"][(d["x"] & 0x7F80) == 0x7F80] = 0x3F80           # no Inf/NaN bit patterns
+    d["x"] = (d["x"] & 0x3FFF) | (d["x"] & 0x8000)         # |x| < 2
+    d["ids"] = rng.integers(-1, E, size=(M, k)).astype(np.int32)
+    d["w"] = rng.random((M, k)).astype(np.float32)
+    layer = make_layer("mxfp4", d, k, M, act=act)
+    got = run_layer(layer, d)
+    sample = np.array([0, 1, 777777, M - 2, M - 1])
+    sub = dict(d, x=d["x"][sample], ids=d["ids"][sample], w=d["w"][sample])
+    if act == "bf16":
+        compare(got[sample], oracle.forward_f32("mxfp4", sub)[0], "2^22 routes, bf16")
+    else:
+        from gpu_util import W4A8_MAXABS_REL_RMS
+        compare(got[sample], oracle.forward_w4a8("mxfp4", sub), "2^22 routes, mxfp8", maxabs=W4A8_MAXABS_REL_RMS)
+
+
+def test_grouped_with_8192_experts():
+    """The most experts the grouping's LDS histogram holds, with routes
+    spread over all of them (most experts get one or two rows)."""
+    rng = np.random.default_rng(38)
+    E, H, I, M, k = 8192, 64, 32, 2048, 8
+    d, _, _ = random_case(rng, "nvfp4", E, H, I, M, k)
+    d["ids"][:, 0] = np.arange(M) % E                 # experts 0 and 8191 both used
+    d["ids"][-1, -1] = E - 1
+    layer = make_layer("nvfp4", d, k, M)
+    got = run_layer(layer, d)
+    sample = np.array([0, 5, 1000, M - 1])
+    acc, _ = oracle.forward_f32("nvfp4", dict(d, x=d["x"][sample], ids=d["ids"][sample], w=d["w"][sample]))
+    compare(got[sample], acc, "E8192 grouped")
