@@ -174,10 +174,13 @@ moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size
  *           dequantised exactly) with fp32 accumulation, per-route fp32 rows
  *           summed per token in route order and cast once (flashinfer #4285,
  *           description: the prefill kernel's per-expert tiles; b12x PR #311,
- *           commit message on the prefill fused-sum epilogue).  The SiLU
- *           product enters FC2 as a pair of bf16 values (hi + lo, 16
- *           significant bits), as in the decode path.  Results are
- *           bit-reproducible.
+ *           commit message on the prefill fused-sum epilogue).  The
+ *           activation enters FC2 as a pair of bf16 values (hi + lo, 16
+ *           significant bits), as in the decode path.  With act_format =
+ *           MXFP8 both GEMMs instead take MXFP8 activations on the scaled
+ *           FP8 x FP4 matrix instruction (the W4A8-MX variant above).
+ *           Results are bit-reproducible.
+ * The activation function (act_fn) is the same on both paths.
  * Returns MOE_FP4_EUNSUPPORTED when max_tokens * k > 2^22, or when the
  * grouped path is needed and E > 8192. */
 moe_fp4_status moe_fp4_forward(const moe_fp4_desc* desc, const void* prepared,
