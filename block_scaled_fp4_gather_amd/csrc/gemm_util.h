@@ -11,20 +11,6 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// Expert of grouped m-tile gm (tile_start is non-decreasing; the expert is
-// the last e with tile_start[e] <= gm).
-__device__ __forceinline__ int tile_expert(const int* __restrict__ tile_start, int E, int gm) {
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (tile_start[mid] <= gm)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  return lo;
-}
-
 typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -62,21 +48,40 @@ __device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 // Row (within the 32x32 block) of accumulator register r of this lane.
 __device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
-// Workgroup -> (m-tile, column block).  Workgroups are dealt to the 8 XCDs
-// in turn, so consecutive ids are remapped to give each XCD a contiguous
-// range of tiles, column block fastest: the column blocks of one m-tile run
-// together on one XCD and share its A rows through that XCD's L2, and the
-// m-tiles of one expert follow each other there and share its weights.
-struct TileId {
-  int gm, nb;
+// Workgroup -> (expert, m-tile, column block) of a grouped GEMM whose experts
+// own m-tiles [tile_start[e], tile_start[e + 1]).  Workgroups are dealt to the
+// 8 XCDs in turn, so consecutive ids are remapped to give each XCD a
+// contiguous range of tiles; within it the order is expert by expert, column
+// block by column block, with the expert's m-tiles innermost: the workgroups
+// that stream the same weight slab (same expert and column block) are
+// dispatched together and share it in that XCD's L2, and the column blocks of
+// an m-tile share its A rows there.  The grid is a multiple of 8; ok is false
+// past the last tile.
+struct GroupTile {
+  int e, gm, nb;
+  bool ok;
 };
-__device__ __forceinline__ TileId tile_id(int nblocks) {
+__device__ __forceinline__ GroupTile group_tile(int nblocks, const int* __restrict__ tile_start, int E) {
   const int per = gridDim.x / 8;
   const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  return TileId{logical / nblocks, logical % nblocks};
+  const int total = tile_start[E];
+  if (logical >= total * nblocks) return GroupTile{0, 0, 0, false};
+  // the last expert whose tiles start at or before this one (it owns tiles:
+  // the next expert's range starts past `logical`)
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (tile_start[mid] * nblocks <= logical)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int nt = tile_start[lo + 1] - tile_start[lo];
+  const int local = logical - tile_start[lo] * nblocks;
+  return GroupTile{lo, tile_start[lo] + local % nt, local / nt, true};
 }
 
-// Grid of n tiles rounded up to whole XCD rounds (tile_id needs a multiple of 8).
+// Grid of n tiles rounded up to whole XCD rounds (group_tile needs a multiple of 8).
 inline unsigned grid8(int64_t n) { return (unsigned)((n + 7) / 8 * 8); }
 
 }  // namespace moe

@@ -341,9 +341,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
              const int* __restrict__ tile_start, const int* __restrict__ perm,
              uint16_t* __restrict__ act, int64_t plane) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
-  const TileId id = tile_id(fc1_blocks(L));
-  if (id.gm >= tile_start[L.E]) return;
-  const int e = tile_expert(tile_start, L.E, id.gm);
+  const GroupTile id = group_tile(fc1_blocks(L), tile_start, L.E);
+  if (!id.ok) return;
+  const int e = id.e;
   const int m0 = (id.gm - tile_start[e]) * kGemmBM;
   const int rows = min(kGemmBM, counts[e] - m0);
   const int gs = grp_start[e] + m0;
@@ -404,9 +404,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
              const uint16_t* __restrict__ act, int64_t plane, float* __restrict__ y) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
   __shared__ float wrow[kGemmBM];
-  const TileId id = tile_id(fc2_blocks(L));
-  if (id.gm >= tile_start[L.E]) return;
-  const int e = tile_expert(tile_start, L.E, id.gm);
+  const GroupTile id = group_tile(fc2_blocks(L), tile_start, L.E);
+  if (!id.ok) return;
+  const int e = id.e;
   const int m0 = (id.gm - tile_start[e]) * kGemmBM;
   const int rows = min(kGemmBM, counts[e] - m0);
   const int gs = grp_start[e] + m0;

@@ -207,9 +207,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
                 const int* __restrict__ grp_start, const int* __restrict__ tile_start,
                 const int* __restrict__ perm, uint8_t* __restrict__ aq, uint8_t* __restrict__ as, int ass) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds8];
-  const TileId id = tile_id(fc1_blocks(L));
-  if (id.gm >= tile_start[L.E]) return;
-  const int e = tile_expert(tile_start, L.E, id.gm);
+  const GroupTile id = group_tile(fc1_blocks(L), tile_start, L.E);
+  if (!id.ok) return;
+  const int e = id.e;
   const int m0 = (id.gm - tile_start[e]) * kGemmBM;
   const int rows = min(kGemmBM, counts[e] - m0);
   const int gs = grp_start[e] + m0;
@@ -292,9 +292,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
                 const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds8];
   __shared__ float wrow[kGemmBM];
-  const TileId id = tile_id(fc2_blocks(L));
-  if (id.gm >= tile_start[L.E]) return;
-  const int e = tile_expert(tile_start, L.E, id.gm);
+  const GroupTile id = group_tile(fc2_blocks(L), tile_start, L.E);
+  if (!id.ok) return;
+  const int e = id.e;
   const int m0 = (id.gm - tile_start[e]) * kGemmBM;
   const int rows = min(kGemmBM, counts[e] - m0);
   const int gs = grp_start[e] + m0;
