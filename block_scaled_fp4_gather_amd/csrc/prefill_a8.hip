@@ -14,9 +14,10 @@
 // of the prepared weights (one row, 32 K values) and its scale byte.
 //
 //   fc1_gemm_a8  x rows (MXFP8, quantised once per token) gathered by
-//                grouped row, SiLU(gate) * up in fp32, quantised to MXFP8 in
-//                blocks of 32 along I (the 32 gate/up columns of one wave's
-//                prepared tile are one block) -> act codes and scales;
+//                grouped row, the activation f(gate, up) in fp32 (relu2:
+//                both halves as outputs), quantised to MXFP8 in blocks of 32
+//                along I (the 32 columns of one wave's prepared tile are one
+//                block) -> act codes and scales;
 //   fc2_gemm_a8  act rows times W2, times the route's router weight -> the
 //                same fp32 rows that the combine sums.
 #include <hip/hip_runtime.h>
@@ -63,9 +64,9 @@ __device__ __forceinline__ int scale_byte(uint32_t w, int b) { return (int)((w >
 // 8 rows per copy, from `rowp[blk]`), their scale dwords (from `srow`, this
 // lane's row 32w + lane % 32), and the wave's weights, which lane (n, h)
 // copies for the units it multiplies (unit 4s + 2t + h of weight rows n and
-// 32 + n) and one copy of the scale dwords of all 64 rows.  Copies past the last unit
-// are clamped to it; in a last step with fewer than 4 units the absent
-// units' operands are zeroed and their scales set to 1 when read.
+// 32 + n), with one copy of the scale dwords of all 64 rows.  Copies past
+// the last unit are clamped to it; in a last step with fewer than 4 units
+// the absent units' operands are zeroed and their scales set to 1 when read.
 template <int NB, typename Epilogue>
 __device__ __forceinline__ void gemm_main_a8(const uint8_t* const (&rowp)[4], const uint8_t* srow, int nU,
                                              const uint8_t* __restrict__ btile, uint8_t* smem,

@@ -32,22 +32,45 @@ KERNELS = ("fc1_kernel", "fc2_kernel", "fc1_gemm_a8", "fc2_gemm_a8", "mxfp8_quan
            "route_build", "combine")
 
 
-# HIP sources each kernel is built from: a summary stays valid while these
-# files are unchanged.
-_DECODE_SRC = ("decode_path.hip", "decode_path.h", "decode.h", "layout.h")
-_GROUPED_SRC = ("prefill.hip", "prefill.h", "gemm_util.h", "decode.h", "layout.h")
-_A8_SRC = ("prefill_a8.hip", "prefill.h", "gemm_util.h", "mxfp8.h", "layout.h")
+# HIP sources each kernel is built from: a summary stays valid while their
+# code (comments and blank space aside) is unchanged.
+_DECODE_SRC = ("decode_path.hip", "decode_path.h", "decode.h", "act.h", "layout.h")
+_GROUPED_SRC = ("prefill.hip", "prefill.h", "gemm_util.h", "decode.h", "act.h", "layout.h")
+_A8_SRC = ("prefill_a8.hip", "prefill.h", "gemm_util.h", "mxfp8.h", "act.h", "layout.h")
 SOURCES = {"fc1_kernel": _DECODE_SRC, "fc2_kernel": _DECODE_SRC, "fc1_gemm": _GROUPED_SRC,
            "fc2_gemm": _GROUPED_SRC, "route_build": _GROUPED_SRC, "combine": _GROUPED_SRC,
            "fc1_gemm_a8": _A8_SRC, "fc2_gemm_a8": _A8_SRC, "mxfp8_quantize": ("mxfp8.hip", "mxfp8.h")}
+
+
+def _code(text: str) -> str:
+    """Source text without comments, with runs of blank space collapsed."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif text[i] == '"':  # string literal, copied whole
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
 
 
 def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "csrc")
     for name in sorted(SOURCES[kernel]):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + _code(f.read()).encode())
     return h.hexdigest()[:16]
 
 
