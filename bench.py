@@ -113,6 +113,27 @@ def cold_groups(wl, d, dev):
             for i, w in tables]
 
 
+def run_env(torch) -> dict:
+    """GPU and host identity for the record (the commit when a git checkout is present)."""
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    commit = None
+    try:
+        import subprocess
+        commit = subprocess.run(["git", "rev-parse", "--short", "HEAD"], capture_output=True, text=True,
+                                cwd=os.path.dirname(os.path.abspath(__file__)), timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    props = torch.cuda.get_device_properties(0)
+    return {"gpu": torch.cuda.get_device_name(0), "gpu_arch": getattr(props, "gcnArchName", None),
+            "gpu_cus": props.multi_processor_count, "host_cpu": cpu_model, "host_cpus": os.cpu_count(),
+            "commit": commit}
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -351,6 +372,7 @@ def main():
                      "rocprof_mean_us": prof["duration_us"]["mean_us"] if prof else None},
         "cpu_baseline": cpu,
         "check": check,
+        "env": run_env(torch),
     }
     line.update(extra)
     print(json.dumps(line), flush=True)
