@@ -140,7 +140,7 @@ def main():
         copy_probe()
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}); "
               "the layer would shard by experts or by I with one exchange of the [M, H] output.",
               file=sys.stderr)
         sys.exit(2)

@@ -49,7 +49,7 @@ extern "C" {
 typedef enum {
   MOE_FP4_OK = 0,
   MOE_FP4_EINVAL = 1,      /* null/misaligned pointer, bad size or count */
-  MOE_FP4_EUNSUPPORTED = 2,/* valid request outside what this build handles */
+  MOE_FP4_EUNSUPPORTED = 2,/* valid request outside what the library handles */
   MOE_FP4_EWORKSPACE = 3,  /* workspace or prepared buffer too small */
   MOE_FP4_EHIP = 4         /* a HIP launch or runtime call failed */
 } moe_fp4_status;
