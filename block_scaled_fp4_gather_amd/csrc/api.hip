@@ -71,6 +71,45 @@ int64_t workspace_total(const Layout& L, const moe_fp4_desc* d) {
 
 moe_fp4_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_FP4_OK : MOE_FP4_EHIP; }
 
+// The path and launch shape of a call: a moe_fp4_path (GROUPED, or one of
+// the decode forms) and the decode shape with every field resolved.
+struct Plan {
+  int path;
+  moe::DecodeShape shape;
+};
+
+moe_fp4_status make_plan(const moe_fp4_desc* desc, const Layout& L, int32_t M,
+                         const moe_fp4_tuning* tuning, Plan* plan) {
+  moe::DecodeShape shape{0, 0, 0, moe::kFormAuto};
+  int path = MOE_FP4_PATH_AUTO;
+  if (tuning) {
+    path = tuning->path;
+    if (path < MOE_FP4_PATH_AUTO || path > MOE_FP4_PATH_DECODE_SPLIT) return MOE_FP4_EINVAL;
+    const int form = path == MOE_FP4_PATH_DECODE_TWO_PASS ? moe::kFormTwoPass
+                     : path == MOE_FP4_PATH_DECODE_SPLIT  ? moe::kFormSplit
+                                                          : moe::kFormAuto;
+    if (form != moe::kFormAuto) path = MOE_FP4_PATH_DECODE;
+    shape = moe::DecodeShape{tuning->fc1_chunks_per_wave, tuning->fc1_rows, tuning->fc2_rows, form};
+    if (!moe::valid_shape(L, shape)) return MOE_FP4_EINVAL;
+  }
+  if (prefill_routes(desc) > moe::kPrefillMaxRoutes ||
+      moe::prefill_max_workgroups(L, prefill_routes(desc)) >= ((int64_t)1 << 31))
+    return MOE_FP4_EUNSUPPORTED;
+  const int k = desc->top_k;
+  const bool decode_ok = k <= moe::kDecodeMaxSlots && M <= moe::decode_max_tokens(k);
+  if (path == MOE_FP4_PATH_AUTO) path = decode_ok ? MOE_FP4_PATH_DECODE : MOE_FP4_PATH_GROUPED;
+  if (path == MOE_FP4_PATH_DECODE && !decode_ok) return MOE_FP4_EUNSUPPORTED;
+  if (path == MOE_FP4_PATH_GROUPED && L.E > moe::kRouteMaxExperts) return MOE_FP4_EUNSUPPORTED;
+  if (path == MOE_FP4_PATH_DECODE) {
+    const moe::DecodeWs W = moe::decode_ws(L, decode_slots(desc));
+    if (!moe::resolve_shape(L, W, M < 1 ? 1 : M, (M < 1 ? 1 : M) * k, &shape)) return MOE_FP4_EUNSUPPORTED;
+    path = shape.form == moe::kFormSplit ? MOE_FP4_PATH_DECODE_SPLIT : MOE_FP4_PATH_DECODE_TWO_PASS;
+  }
+  plan->path = path;
+  plan->shape = shape;
+  return MOE_FP4_OK;
+}
+
 template <typename IdT>
 moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, const uint16_t* x,
                             int32_t M, const IdT* ids, const float* w, uint16_t* out,
@@ -85,33 +124,20 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
   if (!aligned(prepared, 256) || !aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, 256) ||
       !aligned(ids, sizeof(IdT)) || !aligned(w, 4))
     return MOE_FP4_EINVAL;
-  moe::DecodeShape shape{0, 0, 0};
-  int path = MOE_FP4_PATH_AUTO;
-  if (tuning) {
-    shape = moe::DecodeShape{tuning->fc1_chunks_per_wave, tuning->fc1_rows, tuning->fc2_rows};
-    path = tuning->path;
-    if (path < MOE_FP4_PATH_AUTO || path > MOE_FP4_PATH_GROUPED || !moe::valid_shape(L, shape))
-      return MOE_FP4_EINVAL;
-  }
   if (phases != 1 && phases != 2 && phases != 3 && phases != 4 && phases != 8) return MOE_FP4_EINVAL;
-  if (prefill_routes(desc) > moe::kPrefillMaxRoutes ||
-      moe::prefill_max_workgroups(L, prefill_routes(desc)) >= ((int64_t)1 << 31))
-    return MOE_FP4_EUNSUPPORTED;
-  const int k = desc->top_k;
-  const bool decode_ok = k <= moe::kDecodeMaxSlots && M <= moe::decode_max_tokens(k);
-  if (path == MOE_FP4_PATH_AUTO) path = decode_ok ? MOE_FP4_PATH_DECODE : MOE_FP4_PATH_GROUPED;
-  if (path == MOE_FP4_PATH_DECODE && !decode_ok) return MOE_FP4_EUNSUPPORTED;
-  if (path == MOE_FP4_PATH_GROUPED && L.E > moe::kRouteMaxExperts) return MOE_FP4_EUNSUPPORTED;
-  if (path == MOE_FP4_PATH_DECODE && phases > 3) return MOE_FP4_EINVAL;
+  Plan plan;
+  st = make_plan(desc, L, M, tuning, &plan);
+  if (st != MOE_FP4_OK) return st;
+  if (plan.path != MOE_FP4_PATH_GROUPED && phases > 3) return MOE_FP4_EINVAL;
   if ((int64_t)ws_bytes < workspace_total(L, desc)) return MOE_FP4_EWORKSPACE;
-  if (path == MOE_FP4_PATH_GROUPED)
+  const int k = desc->top_k;
+  if (plan.path == MOE_FP4_PATH_GROUPED)
     return from_hip(moe::launch_prefill<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
                                              (uint8_t*)workspace, prefill_layout(L, desc), phases,
                                              act_mxfp8(desc), (hipStream_t)stream));
   const moe::DecodeWs W = moe::decode_ws(L, decode_slots(desc));
-  shape = moe::resolve_shape(L, M * k, shape);
   return from_hip(moe::launch_decode<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
-                                          (uint8_t*)workspace, W, shape, phases, (hipStream_t)stream));
+                                          (uint8_t*)workspace, W, plan.shape, phases, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -203,6 +229,23 @@ moe_fp4_status moe_fp4_forward_ex(const moe_fp4_desc* desc, const void* prepared
                                   int32_t phases, void* stream) {
   return forward_impl<int32_t>(desc, prepared, x, M, topk_ids, topk_w, out, workspace,
                                workspace_bytes, tuning, phases, stream);
+}
+
+moe_fp4_status moe_fp4_plan(const moe_fp4_desc* desc, int32_t M, const moe_fp4_tuning* tuning,
+                            moe_fp4_tuning* plan) {
+  Layout L;
+  moe_fp4_status st = desc_layout(desc, &L);
+  if (st != MOE_FP4_OK) return st;
+  if (!plan || M < 0 || M > desc->max_tokens) return MOE_FP4_EINVAL;
+  Plan p;
+  st = make_plan(desc, L, M, tuning, &p);
+  if (st != MOE_FP4_OK) return st;
+  const bool grouped = p.path == MOE_FP4_PATH_GROUPED;
+  plan->fc1_chunks_per_wave = grouped ? 0 : p.shape.kl1;
+  plan->fc1_rows = grouped || p.path == MOE_FP4_PATH_DECODE_SPLIT ? 0 : p.shape.r1;
+  plan->fc2_rows = grouped || p.path == MOE_FP4_PATH_DECODE_SPLIT ? 0 : p.shape.r2;
+  plan->path = p.path;
+  return MOE_FP4_OK;
 }
 
 moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prepared,
