@@ -49,8 +49,6 @@ def parse():
     ap.add_argument("--no-check", action="store_true", help="skip the oracle check (profiling runs)")
     ap.add_argument("--shape", default=None,
                     help="launch shape kl1,r1,r2 (FC1 chunks per wave, FC1 rows, FC2 rows; 0 = built-in)")
-    ap.add_argument("--form", default="auto", choices=("auto", "two_pass", "split"),
-                    help="decode form: the library's choice, FC1 then FC2, or FC1 with FC2 partial sums then a reduce")
     ap.add_argument("--extra", action="store_true", help="also time warm-cache calls and a copy probe")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run 5 copies of a 256 MiB buffer (reference for profiler byte counters)")
@@ -174,15 +172,9 @@ def main():
     out = torch.empty((wl.M, wl.H), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     log("[bench] prepared")
-    form_path = {"auto": moe.PATH_AUTO, "two_pass": moe.PATH_DECODE_TWO_PASS,
-                 "split": moe.PATH_DECODE_SPLIT}[args.form]
-    tuning = None
-    if args.shape or form_path != moe.PATH_AUTO:
-        shape = [int(v) for v in args.shape.split(",")] if args.shape else [0, 0, 0]
-        tuning = moe.Tuning(*shape, form_path)
+    tuning = moe.Tuning(*[int(v) for v in args.shape.split(",")], 0) if args.shape else None
     plan = moe.plan(desc, wl.M, tuning)
-    split = plan.path == moe.PATH_DECODE_SPLIT
-    log(f"[bench] path {plan.path} ({'grouped' if plan.path == moe.PATH_GROUPED else ('decode, split form' if split else 'decode, two-pass form')}), "
+    log(f"[bench] {'grouped' if plan.path == moe.PATH_GROUPED else 'decode'} path, "
         f"shape kl1={plan.fc1_chunks_per_wave} r1={plan.fc1_rows} r2={plan.fc2_rows}")
 
     # the decode band of the library: M <= min(16, 64 / k); past it, the grouped path
@@ -275,7 +267,7 @@ def main():
     log(f"[bench] layer, cold rotation: {value:.3f} us/step")
     fc1_us, _, _ = region(phases=1)
     fc2_us, _, _ = region(phases=2)
-    log(f"[bench] first launch only {fc1_us:.3f} us, second launch only {fc2_us:.3f} us")
+    log(f"[bench] fc1 only {fc1_us:.3f} us/launch, fc2 only {fc2_us:.3f} us/launch")
     aux = {}
     if grouped:
         # the grouped halves also hold the routing (with FC1) and the combine
@@ -300,16 +292,11 @@ def main():
         dom, dom_work, dom_us = ("fc1_gemm" + sfx, f1, fc1_us) if f1 >= f2 else ("fc2_gemm" + sfx, f2, fc2_us)
         achieved = dom_work / (dom_us * 1e-6) / 1e12
         peak, unit, bound = (MFMA_FP8_PEAK_TFLOPS if a8 else MFMA_BF16_PEAK_TFLOPS), "TFLOP/s", "mfma"
-    elif split:
-        # the first launch streams every routed weight byte; the second reads none
-        dom, dom_work, dom_us = "fc12_kernel", b13 + b2, fc1_us
-        achieved = dom_work / (dom_us * 1e-6) / 1e9
-        peak, unit, bound = HBM_PEAK_GBPS, "GB/s", "hbm"
     else:
         dom, dom_work, dom_us = ("fc1_kernel", b13, fc1_us) if b13 >= b2 else ("fc2_kernel", b2, fc2_us)
         achieved = dom_work / (dom_us * 1e-6) / 1e9
         peak, unit, bound = HBM_PEAK_GBPS, "GB/s", "hbm"
-    prof = profsum.lookup(dom, wl.name) if args.shape is None and args.form == "auto" else None
+    prof = profsum.lookup(dom, wl.name) if args.shape is None else None
     traffic = prof["hbm_bytes_per_dispatch"] if prof else None
     extra = {}
     if args.extra:
@@ -379,12 +366,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "format": wl.fmt, "E": wl.E, "H": wl.H, "I": wl.I,
                    "M": wl.M, "top_k": wl.k, "unique_experts": U, "activations": "mxfp8" if a8 else "bf16",
-                   "path": ("grouped" if plan.path == moe.PATH_GROUPED else
-                            ("decode_split" if split else "decode_two_pass"))},
+                   "path": "grouped" if plan.path == moe.PATH_GROUPED else "decode"},
         "hbm_frac_layer": round(layer_bytes / (value * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "routed_bytes": {"fc1": b13, "fc2": b2},
-        "kernel_us": ({"fc12": round(fc1_us, 3), "reduce": round(fc2_us, 3)} if split else
-                      {"fc1": round(fc1_us, 3), "fc2": round(fc2_us, 3), **aux}),
+        "kernel_us": {"fc1": round(fc1_us, 3), "fc2": round(fc2_us, 3), **aux},
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": dom, ("algorithmic_flops" if grouped else "algorithmic_bytes"): dom_work,

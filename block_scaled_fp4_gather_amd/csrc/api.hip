@@ -71,8 +71,8 @@ int64_t workspace_total(const Layout& L, const moe_fp4_desc* d) {
 
 moe_fp4_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_FP4_OK : MOE_FP4_EHIP; }
 
-// The path and launch shape of a call: a moe_fp4_path (GROUPED, or one of
-// the decode forms) and the decode shape with every field resolved.
+// The path and launch shape of a call: MOE_FP4_PATH_GROUPED or
+// MOE_FP4_PATH_DECODE, and the decode shape with every field resolved.
 struct Plan {
   int path;
   moe::DecodeShape shape;
@@ -80,17 +80,13 @@ struct Plan {
 
 moe_fp4_status make_plan(const moe_fp4_desc* desc, const Layout& L, int32_t M,
                          const moe_fp4_tuning* tuning, Plan* plan) {
-  moe::DecodeShape shape{0, 0, 0, moe::kFormAuto};
+  moe::DecodeShape shape{0, 0, 0};
   int path = MOE_FP4_PATH_AUTO;
   if (tuning) {
+    shape = moe::DecodeShape{tuning->fc1_chunks_per_wave, tuning->fc1_rows, tuning->fc2_rows};
     path = tuning->path;
-    if (path < MOE_FP4_PATH_AUTO || path > MOE_FP4_PATH_DECODE_SPLIT) return MOE_FP4_EINVAL;
-    const int form = path == MOE_FP4_PATH_DECODE_TWO_PASS ? moe::kFormTwoPass
-                     : path == MOE_FP4_PATH_DECODE_SPLIT  ? moe::kFormSplit
-                                                          : moe::kFormAuto;
-    if (form != moe::kFormAuto) path = MOE_FP4_PATH_DECODE;
-    shape = moe::DecodeShape{tuning->fc1_chunks_per_wave, tuning->fc1_rows, tuning->fc2_rows, form};
-    if (!moe::valid_shape(L, shape)) return MOE_FP4_EINVAL;
+    if (path < MOE_FP4_PATH_AUTO || path > MOE_FP4_PATH_GROUPED || !moe::valid_shape(L, shape))
+      return MOE_FP4_EINVAL;
   }
   if (prefill_routes(desc) > moe::kPrefillMaxRoutes ||
       moe::prefill_max_workgroups(L, prefill_routes(desc)) >= ((int64_t)1 << 31))
@@ -100,11 +96,7 @@ moe_fp4_status make_plan(const moe_fp4_desc* desc, const Layout& L, int32_t M,
   if (path == MOE_FP4_PATH_AUTO) path = decode_ok ? MOE_FP4_PATH_DECODE : MOE_FP4_PATH_GROUPED;
   if (path == MOE_FP4_PATH_DECODE && !decode_ok) return MOE_FP4_EUNSUPPORTED;
   if (path == MOE_FP4_PATH_GROUPED && L.E > moe::kRouteMaxExperts) return MOE_FP4_EUNSUPPORTED;
-  if (path == MOE_FP4_PATH_DECODE) {
-    const moe::DecodeWs W = moe::decode_ws(L, decode_slots(desc));
-    if (!moe::resolve_shape(L, W, M < 1 ? 1 : M, (M < 1 ? 1 : M) * k, &shape)) return MOE_FP4_EUNSUPPORTED;
-    path = shape.form == moe::kFormSplit ? MOE_FP4_PATH_DECODE_SPLIT : MOE_FP4_PATH_DECODE_TWO_PASS;
-  }
+  if (path == MOE_FP4_PATH_DECODE) shape = moe::resolve_shape(L, (M < 1 ? 1 : M) * k, shape);
   plan->path = path;
   plan->shape = shape;
   return MOE_FP4_OK;
@@ -242,8 +234,8 @@ moe_fp4_status moe_fp4_plan(const moe_fp4_desc* desc, int32_t M, const moe_fp4_t
   if (st != MOE_FP4_OK) return st;
   const bool grouped = p.path == MOE_FP4_PATH_GROUPED;
   plan->fc1_chunks_per_wave = grouped ? 0 : p.shape.kl1;
-  plan->fc1_rows = grouped || p.path == MOE_FP4_PATH_DECODE_SPLIT ? 0 : p.shape.r1;
-  plan->fc2_rows = grouped || p.path == MOE_FP4_PATH_DECODE_SPLIT ? 0 : p.shape.r2;
+  plan->fc1_rows = grouped ? 0 : p.shape.r1;
+  plan->fc2_rows = grouped ? 0 : p.shape.r2;
   plan->path = p.path;
   return MOE_FP4_OK;
 }

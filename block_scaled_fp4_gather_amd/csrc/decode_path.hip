@@ -175,30 +175,6 @@ __device__ __forceinline__ float unit_dot2(const u32x4 q, const uint32_t* hi, co
   return fmaf(pa, sc.x, pb * sc.y);
 }
 
-// Dot product of half a unit (16 elements, 8 bytes) with 16 fp32
-// activations in LDS (every lane reads the same addresses: broadcast reads),
-// unscaled; the half is widened to fp32 pairs.
-__device__ __forceinline__ float half_unit_dot_f32(const u32x2 q, const float* a) {
-  const uint32_t w[2] = {q.x, q.y};
-  float acc = 0.0f;
-#pragma unroll
-  for (int d = 0; d < 2; ++d) {
-    f32x2_t wv[4];
-    fp4x8_to_f32(w[d], wv);  // elements 8d .. 8d+7
-    const f32x4 a0 = ((const f32x4*)a)[2 * d];
-    const f32x4 a1 = ((const f32x4*)a)[2 * d + 1];
-    acc = fmaf(wv[0].x, a0.x, acc);
-    acc = fmaf(wv[0].y, a0.y, acc);
-    acc = fmaf(wv[1].x, a0.z, acc);
-    acc = fmaf(wv[1].y, a0.w, acc);
-    acc = fmaf(wv[2].x, a1.x, acc);
-    acc = fmaf(wv[2].y, a1.y, acc);
-    acc = fmaf(wv[3].x, a1.z, acc);
-    acc = fmaf(wv[3].y, a1.w, acc);
-  }
-  return acc;
-}
-
 __device__ __forceinline__ void load_chunk16(const uint16_t* p, uint32_t* d) {
   const u32x4* q = (const u32x4*)p;
 #pragma unroll
@@ -430,242 +406,6 @@ __global__ void __launch_bounds__(64 * fc2_max_waves(KL))
   }
 }
 
-// Split form, first launch: one workgroup per (route slot, FC1 tile b, half
-// h2 of the tile).  Its FC1 part is fc1_kernel's with 32-row blocks: gate
-// rows 32b + 16 h2 + i and the matching up rows (relu2: the same rows of its
-// two halves), i < 16.  Instead of storing the activation, the workgroup
-// keeps its 16 intermediate values (relu2: 2 x 16) in LDS and multiplies
-// them into the matching 16 columns of W2 (the h2 half of each 32-element
-// unit of chunk b) for every row of H: FC2's partial sum over these columns,
-// stored in fp32 per (route slot, tile, half).  The W2 half-units (one per
-// lane and FC2 tile: row 64 hb + lane) are loaded right after the route
-// lookup, together with FC1's, so the two weight streams share one memory
-// latency.  Workgroup ids place the two halves of a tile 8 apart, so that
-// the round-robin dispatch over the 8 XCDs puts them on one XCD and the W2
-// lines they share are fetched once into its L2.
-template <int FMT, int KL, int NT2, int NCH, typename IdT>
-__global__ void __launch_bounds__(64 * kSplitMaxWaves)
-    fc12_kernel(const uint8_t* __restrict__ prep, const Layout L, const uint16_t* __restrict__ x,
-                const IdT* __restrict__ ids, const int M, const int k, float* __restrict__ part) {
-  constexpr int SPD = FMT == kMXFP4 ? 4 : 2;  // chunks per scale dword
-  constexpr int R = 32;                       // FC1 rows per workgroup
-  constexpr int RG = 64 / KL;                 // row groups of a wave
-  constexpr int T = R / RG;                   // rows per lane
-  extern __shared__ u32x4 lds_raw[];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int W = blockDim.x >> 6;
-  uint16_t* xs = (uint16_t*)lds_raw;               // [H] activations of token t0
-  float* psum = (float*)(xs + align_up(L.H, 64));  // [token index][W waves][32 rows]
-  float* acts = psum + M * W * R;                  // [token index][32] intermediate values
-  const int p = lane % KL, g = lane / KL;
-  const int h2 = (blockIdx.x >> 3) & 1;
-  const int u = (blockIdx.x >> 4) * 8 + (blockIdx.x & 7);  // (slot, tile) unit
-  if (u >= M * k * L.nB1) return;  // grid padding
-  const int b = u % L.nB1;
-  const int s = u / L.nB1;
-  const int t0 = s / k;
-  const int ngroups = (L.nC1 + W * KL - 1) / (W * KL);
-
-  stage_lds(x + (int64_t)t0 * L.H, xs, L.H / 8);
-  const Routes R_ = load_routes(ids, (const float*)nullptr, M * k, L.E);
-  uint64_t mask = 0;
-  const int e = slot_expert(R_, s, &mask);
-  if (e < 0) return;  // same decision in every wave of the workgroup
-  // Half h2 of W2 chunk b (relu2: also of chunk nB1 + b, the second half's
-  // columns) in FC2 tiles hb = wave + W j2; tiles past the last are clamped
-  // (loaded, not used).
-  u32x2 q2[NCH][NT2];
-  uint32_t s2[NCH][NT2];
-#pragma unroll
-  for (int j2 = 0; j2 < NT2; ++j2) {
-    const int hb = min(wave + W * j2, L.nB2 - 1);
-    const uint8_t* t2 = prep + fc2_tile_offset(L, e, hb);
-#pragma unroll
-    for (int ch = 0; ch < NCH; ++ch) {
-      const int c = b + ch * L.nB1;
-      q2[ch][j2] = __builtin_nontemporal_load((const u32x2*)(t2 + (int64_t)c * 1024 + lane * 16 + 8 * h2));
-      s2[ch][j2] = __builtin_nontemporal_load(
-          (const uint32_t*)(t2 + (int64_t)L.nC2 * 1024 + (c / SPD) * 256 + lane * 4));
-    }
-  }
-  const uint8_t* tile = prep + fc1_tile_offset(L, e, b);
-  const uint8_t* sbase = tile + (int64_t)L.nC1 * 1024;
-
-  int m = 0;
-  for (int t = 0; t < M; ++t) m += token_routes(mask, t, k) != 0;
-  for (int i = threadIdx.x; i < m * W * R; i += blockDim.x) psum[i] = 0.0f;
-  __syncthreads();
-
-  for (int grp = 0; grp < ngroups; ++grp) {
-    const int c = (grp * W + wave) * KL + p;
-    const bool cv = c < L.nC1;
-    const int cc = min(c, L.nC1 - 1);
-    u32x4 q[T];
-    uint32_t sd[T];
-#pragma unroll
-    for (int j = 0; j < T; ++j) {
-      const int qr = g + RG * j;  // block row: 16 gate rows, then 16 up rows
-      const int row = (qr < 16 ? 0 : 16) + 16 * h2 + qr;
-      q[j] = __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)cc * 1024 + row * 16));
-      sd[j] = __builtin_nontemporal_load((const uint32_t*)(sbase + (cc / SPD) * 256 + row * 4));
-    }
-    int ti = 0;
-    for (int t = 0; t < M; ++t) {
-      if (!token_routes(mask, t, k)) continue;
-      uint32_t xc[16];
-      if (t == t0)
-        lds_chunk16(xs + 32 * cc, xc);
-      else
-        load_chunk16(x + (int64_t)t * L.H + 32 * cc, xc);
-      float v[T];
-#pragma unroll
-      for (int j = 0; j < T; ++j) v[j] = cv ? unit_dot<FMT>(q[j], xc, chunk_scale<FMT>(sd[j], cc)) : 0.0f;
-      const float r = fold_rows<KL, T>(v, p);
-      if (p < T) psum[(ti * W + wave) * R + g + RG * p] += r;
-      ++ti;
-    }
-  }
-  __syncthreads();
-  const float g13 = FMT == kNVFP4 ? ((const float*)prep)[e] : 1.0f;
-  int ti = 0;
-  for (int t = 0; t < M; ++t) {
-    if (!token_routes(mask, t, k)) continue;
-    if (ti % W == wave && lane < 16) {
-      float gate = 0.0f, up = 0.0f;
-      for (int w = 0; w < W; ++w) {
-        gate += psum[(ti * W + w) * R + lane];
-        up += psum[(ti * W + w) * R + 16 + lane];
-      }
-      gate *= g13;
-      up *= g13;
-      if (L.act.kind == kActRelu2) {  // not gated: both halves are outputs
-        acts[ti * 32 + lane] = relu2(gate);
-        acts[ti * 32 + 16 + lane] = relu2(up);
-      } else {
-        acts[ti * 32 + lane] = gated_act(L.act, gate, up);
-      }
-    }
-    ++ti;
-  }
-  __syncthreads();
-  const float g2 = FMT == kNVFP4 ? ((const float*)prep)[L.E + e] : 1.0f;
-  const int nblk = 2 * L.nB1;
-  ti = 0;
-  for (int t = 0; t < M; ++t) {
-    const uint64_t tm = token_routes(mask, t, k);
-    if (!tm) continue;
-    const int r = t * k + __builtin_ctzll(tm);  // the token's first slot holding e
-    const float* a = acts + ti * 32;
-#pragma unroll
-    for (int j2 = 0; j2 < NT2; ++j2) {
-      const int hb = wave + W * j2;
-      float y = 0.0f;
-#pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
-        const f32x2_t sc = chunk_scale<FMT>(s2[ch][j2], b + ch * L.nB1);
-        y += half_unit_dot_f32(q2[ch][j2], a + 16 * ch) * (h2 ? sc.y : sc.x);
-      }
-      const int h = 64 * hb + lane;
-      if (hb < L.nB2 && h < L.H) part[((int64_t)r * nblk + 2 * b + h2) * L.H + h] = y * g2;
-    }
-    ++ti;
-  }
-}
-
-// Split form, second launch: out[t][h] = bf16(sum over the valid routes j
-// of token t of w[t][j] * sum_q part[f(j)][q][h]) over the 2 nB1 column
-// blocks q, where f(j) is the token's first slot holding the same expert
-// (duplicate routes share its partials).  One workgroup per (token, 64
-// columns of H); thread (sub, c) = (tid / 16, tid % 16) owns columns
-// 4c..4c+3 and the (route, block) pairs sub, sub + 64, ...; the 64 sums of
-// a column then meet in LDS in a fixed order, so results are
-// bit-reproducible.  The first pairs' rows are loaded before the route ids
-// arrive (the slot's own row, in bounds whatever it holds) and used only
-// when the route is valid and is the first of its expert; invalid routes
-// read nothing else and add nothing.
-template <typename IdT>
-__global__ void __launch_bounds__(1024)
-    fc2_reduce_kernel(const Layout L, const IdT* __restrict__ ids, const float* __restrict__ tw,
-                      const int M, const int k, const float* __restrict__ part,
-                      uint16_t* __restrict__ out) {
-  constexpr int PB = 4;  // pairs per thread loaded ahead of the route ids
-  __shared__ int rid[kDecodeMaxSlots];
-  __shared__ int rfirst[kDecodeMaxSlots];
-  __shared__ float rw[kDecodeMaxSlots];
-  __shared__ f32x4 red[64][16];
-  const int nhb = (L.H + 63) / 64;
-  const int t = blockIdx.x / nhb;
-  const int hcol = (blockIdx.x % nhb) * 64;
-  const int c = threadIdx.x & 15;
-  const int sub = threadIdx.x >> 4;
-  const int h0 = hcol + 4 * c;
-  const bool hv = h0 < L.H;  // H is a multiple of 32: all four columns or none
-  const int nblk = 2 * L.nB1;
-  const int np = k * nblk;
-  if ((int)threadIdx.x < k) {
-    const int64_t v = (int64_t)ids[t * k + threadIdx.x];
-    rid[threadIdx.x] = (v >= 0 && v < L.E) ? (int)v : -1;
-    rw[threadIdx.x] = tw[t * k + threadIdx.x];
-  }
-  f32x4 ahead[PB];
-#pragma unroll
-  for (int i = 0; i < PB; ++i) {
-    const int pi = sub + 64 * i;
-    const int j = pi / nblk, q = pi % nblk;
-    if (pi < np && hv)
-      ahead[i] = *(const f32x4*)(part + ((int64_t)(t * k + j) * nblk + q) * L.H + h0);
-    else
-      ahead[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < k) {
-    const int e = rid[threadIdx.x];
-    int f = e < 0 ? -1 : (int)threadIdx.x;
-    for (int j = 0; e >= 0 && j < (int)threadIdx.x; ++j)
-      if (rid[j] == e) {
-        f = j;
-        break;
-      }
-    rfirst[threadIdx.x] = f;
-  }
-  __syncthreads();
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto add = [&](int j, f32x4 v) {
-    const float w = rw[j];
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
-  };
-  if (hv) {
-#pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      const int pi = sub + 64 * i;
-      if (pi >= np) break;
-      const int j = pi / nblk, q = pi % nblk;
-      const int f = rfirst[j];
-      if (f < 0) continue;
-      add(j, f == j ? ahead[i] : *(const f32x4*)(part + ((int64_t)(t * k + f) * nblk + q) * L.H + h0));
-    }
-    for (int pi = sub + 64 * PB; pi < np; pi += 64) {
-      const int j = pi / nblk, q = pi % nblk;
-      const int f = rfirst[j];
-      if (f < 0) continue;
-      add(j, *(const f32x4*)(part + ((int64_t)(t * k + f) * nblk + q) * L.H + h0));
-    }
-  }
-  red[sub][c] = acc;
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int cc = threadIdx.x >> 2, comp = threadIdx.x & 3;
-    float v = 0.0f;
-    for (int i = 0; i < 64; ++i) v += red[i][cc][comp];
-    const int h = hcol + (int)threadIdx.x;
-    if (h < L.H) out[(int64_t)t * L.H + h] = f32_to_bf16_rne(v);
-  }
-}
-
 template <int FMT, int KL, typename IdT>
 hipError_t launch_fc1(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                       const IdT* ids, uint16_t* act_hi, uint16_t* act_lo, int R, hipStream_t st) {
@@ -713,52 +453,12 @@ hipError_t launch_fc2(const Layout& L, const uint8_t* prep, int M, int k, const 
   }
 }
 
-template <int FMT, int KL, int NT2, int NCH, typename IdT>
-hipError_t launch_fc12_t(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
-                         const IdT* ids, float* part, hipStream_t st) {
-  const int waves = fc1_waves(L, KL);
-  const int64_t units = (int64_t)M * k * L.nB1;  // (slot, tile) pairs, two halves each
-  const dim3 grid((unsigned)((units + 7) / 8 * 16)), block(64 * waves);
-  hipLaunchKernelGGL((fc12_kernel<FMT, KL, NT2, NCH, IdT>), grid, block, split_lds(L, M, waves), st, prep, L,
-                     x, ids, M, k, part);
-  return hipGetLastError();
-}
-
-template <int FMT, int KL, typename IdT>
-hipError_t launch_fc12(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
-                       const IdT* ids, float* part, hipStream_t st) {
-  const bool wide = split_tiles_per_wave(L, KL) == 8;
-  if (split_chunks(L) == 2)
-    return wide ? launch_fc12_t<FMT, KL, 8, 2, IdT>(L, prep, x, M, k, ids, part, st)
-                : launch_fc12_t<FMT, KL, 4, 2, IdT>(L, prep, x, M, k, ids, part, st);
-  if (wide) return launch_fc12_t<FMT, KL, 8, 1, IdT>(L, prep, x, M, k, ids, part, st);
-  return launch_fc12_t<FMT, KL, 4, 1, IdT>(L, prep, x, M, k, ids, part, st);
-}
-
-template <typename IdT>
-hipError_t launch_reduce(const Layout& L, int M, int k, const IdT* ids, const float* tw, const float* part,
-                         uint16_t* out, hipStream_t st) {
-  const dim3 grid((unsigned)(M * ((L.H + 63) / 64))), block(1024);
-  hipLaunchKernelGGL((fc2_reduce_kernel<IdT>), grid, block, 0, st, L, ids, tw, M, k, part, out);
-  return hipGetLastError();
-}
-
 template <int FMT, typename IdT>
 hipError_t launch_decode_fmt(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                              const IdT* ids, const float* tw, uint16_t* out, uint8_t* ws,
                              const DecodeWs& W, const DecodeShape& sh, int phases, hipStream_t st) {
   uint16_t* act_hi = (uint16_t*)(ws + W.act_hi);
   uint16_t* act_lo = (uint16_t*)(ws + W.act_lo);
-  if (sh.form == kFormSplit) {  // the caller checked split_usable
-    float* part = (float*)(ws + W.part);
-    if (phases & 1) {
-      const hipError_t err = sh.kl1 == 4 ? launch_fc12<FMT, 4, IdT>(L, prep, x, M, k, ids, part, st)
-                                         : launch_fc12<FMT, 8, IdT>(L, prep, x, M, k, ids, part, st);
-      if (err != hipSuccess) return err;
-    }
-    if (phases & 2) return launch_reduce<IdT>(L, M, k, ids, tw, part, out, st);
-    return hipSuccess;
-  }
   if (phases & 1) {
     hipError_t err;
     if (sh.kl1 == 4)

@@ -29,7 +29,7 @@ class MoeFp4Error(RuntimeError):
         self.status = status
 
 
-PATH_AUTO, PATH_DECODE, PATH_GROUPED, PATH_DECODE_TWO_PASS, PATH_DECODE_SPLIT = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
 
 ACT_BF16, ACT_MXFP8 = 0, 1
 ACT_FORMATS = {"bf16": ACT_BF16, "mxfp8": ACT_MXFP8}
@@ -40,8 +40,7 @@ ACT_FNS = {"silu": FN_SILU, "gelu_tanh": FN_GELU_TANH, "swigluoai": FN_SWIGLUOAI
 
 class Tuning(ctypes.Structure):
     """Launch shape of the decode kernels and the execution path (0 keeps the
-    built-in choice; path is PATH_AUTO, PATH_DECODE, PATH_GROUPED, or one of
-    the decode path's forms, PATH_DECODE_TWO_PASS or PATH_DECODE_SPLIT)."""
+    built-in choice; path is PATH_AUTO, PATH_DECODE or PATH_GROUPED)."""
     _fields_ = [("fc1_chunks_per_wave", ctypes.c_int32), ("fc1_rows", ctypes.c_int32),
                 ("fc2_rows", ctypes.c_int32), ("path", ctypes.c_int32)]
 
@@ -185,8 +184,7 @@ def forward(desc: Desc, prepared, x, ids, w, out, workspace, stream=None, tuning
 
 def plan(desc: Desc, M: int, tuning: Tuning | None = None) -> Tuning:
     """The path and launch shape a forward call with M tokens takes (every
-    field resolved; path is PATH_GROUPED, PATH_DECODE_TWO_PASS or
-    PATH_DECODE_SPLIT)."""
+    field resolved; path is PATH_DECODE or PATH_GROUPED)."""
     out = Tuning()
     _check("moe_fp4_plan", lib().moe_fp4_plan(ctypes.byref(desc.c()), M,
                                               ctypes.byref(tuning) if tuning is not None else None,

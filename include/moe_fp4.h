@@ -202,37 +202,20 @@ moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prep
                                       int32_t expert, int32_t which, float* out,
                                       void* stream);
 
-/* Execution path selector for moe_fp4_forward_ex.  The decode path has two
- * forms with the same results up to fp32 summation order:
- *   two-pass: FC1 writes SiLU(gate) * up for every route, FC2 reads it and
- *             writes the router-weighted sum per token;
- *   split:    the FC1 launch also streams, for each 32-column block of the
- *             intermediate that one FC1 workgroup computes, the matching 32
- *             columns of W2 and writes FC2's partial sums over them (fp32);
- *             a second launch, which reads no weights, sums a token's
- *             partials over blocks and routes (router-weighted, in a fixed
- *             order) and writes the bf16 output.  Both weight streams share
- *             one memory latency.  It needs the partial sums to fit the
- *             workspace (at most 64 MiB) and H and M small enough for its
- *             register and LDS budget; otherwise the two-pass form runs. */
+/* Execution path selector for moe_fp4_forward_ex. */
 typedef enum {
   MOE_FP4_PATH_AUTO = 0,    /* by M, as moe_fp4_forward */
-  MOE_FP4_PATH_DECODE = 1,  /* decode path, built-in form; MOE_FP4_EUNSUPPORTED when M is past its band */
-  MOE_FP4_PATH_GROUPED = 2, /* grouped path at any M */
-  MOE_FP4_PATH_DECODE_TWO_PASS = 3, /* decode path, two-pass form */
-  MOE_FP4_PATH_DECODE_SPLIT = 4     /* decode path, split form; MOE_FP4_EUNSUPPORTED where it cannot run */
+  MOE_FP4_PATH_DECODE = 1,  /* decode path; MOE_FP4_EUNSUPPORTED when M is past its band */
+  MOE_FP4_PATH_GROUPED = 2  /* grouped path at any M */
 } moe_fp4_path;
 
 /* Launch shape of the decode kernels and the path; 0 in a field keeps the
  * built-in choice.
- *   fc1_chunks_per_wave: 32-element K chunks per FC1 wave (4, 8 or 16; the
- *             split form takes 4 or 8)
- *   fc1_rows: FC1 rows per workgroup, half gate and half up (16 or 32;
- *             two-pass form, the split form's workgroups take whole 64-row
- *             tiles)
+ *   fc1_chunks_per_wave: 32-element K chunks per FC1 wave (4, 8 or 16)
+ *   fc1_rows: FC1 rows per workgroup, half gate and half up (16 or 32)
  *   fc2_rows: FC2 rows of H per workgroup (8, 16 or 32; at least 64 divided
  *             by FC2's chunk lanes, which is 4, 8 or 16 for I up to 128, 256
- *             or beyond; two-pass form)
+ *             or beyond)
  *   path: a moe_fp4_path */
 typedef struct {
   int32_t fc1_chunks_per_wave;
@@ -244,9 +227,8 @@ typedef struct {
 /* Measurement and test hook: moe_fp4_forward (int32 ids) with an explicit
  * launch shape and path (`tuning` may be NULL) and only part of the call
  * queued, so a caller can put events between the two halves: phases = 1
- * queues the first half (decode: FC1, or in the split form FC1 with FC2's
- * partial sums; grouped: routing and FC1), which fills the workspace's
- * activation or partial sums; 2 queues the second half (FC2 and the combine
+ * queues the first half (decode: FC1; grouped: routing and FC1), which fills
+ * the workspace's activation; 2 queues the second half (FC2 and the combine
  * into `out`; it must follow a phase-1 call with the same arguments on the
  * same stream); 3 queues both.  On the grouped path, 4 queues only its
  * routing (the grouping of the routes by expert) and 8 only its combine
@@ -260,10 +242,10 @@ moe_fp4_status moe_fp4_forward_ex(const moe_fp4_desc* desc, const void* prepared
 
 /* The path and launch shape that moe_fp4_forward_ex takes for M tokens with
  * `tuning` (NULL: moe_fp4_forward's choice), written to `plan` with every
- * field resolved: path is MOE_FP4_PATH_GROUPED, MOE_FP4_PATH_DECODE_TWO_PASS
- * or MOE_FP4_PATH_DECODE_SPLIT; the decode shape fields the chosen form does
- * not use are 0.  Returns what moe_fp4_forward_ex would return for an
- * invalid or unsupported request; launches nothing. */
+ * field resolved: path is MOE_FP4_PATH_DECODE or MOE_FP4_PATH_GROUPED, and
+ * the decode shape fields are 0 on the grouped path.  Returns what
+ * moe_fp4_forward_ex would return for an invalid or unsupported request;
+ * launches nothing. */
 moe_fp4_status moe_fp4_plan(const moe_fp4_desc* desc, int32_t M, const moe_fp4_tuning* tuning,
                             moe_fp4_tuning* plan);
 

@@ -111,9 +111,8 @@ def test_tuning_hook_rejects_bad_shapes(L):
     assert status(moe.Tuning(3, 0, 0, 0)) == 1      # chunks per wave not 4/8/16
     assert status(moe.Tuning(0, 24, 0, 0)) == 1     # FC1 rows not 16/32
     assert status(moe.Tuning(0, 0, 8, 0)) == 1      # 8 FC2 rows x 4 lanes < 64
-    assert status(moe.Tuning(0, 0, 0, 5)) == 1      # no such path
+    assert status(moe.Tuning(0, 0, 0, 3)) == 1      # no such path
     assert status(moe.Tuning(0, 0, 0, -1)) == 1
-    assert status(moe.Tuning(0, 0, 0, moe.PATH_DECODE_SPLIT), phases=4) == 1
     assert status(None, phases=0) == 1
     assert status(None, phases=5) == 1
     assert status(None, phases=4) == 1  # M = 1 takes the decode path: no routing-only phase
@@ -139,13 +138,10 @@ def test_workspace_sizes_do_not_depend_on_m(L):
     assert len(sizes) == 1
     size = sizes.pop()
     routes, H, I = 8 * 8, 4096, 512
-    # decode: two bf16 activation planes per route slot, and the split form's
-    # fp32 partial sums (one row of H per slot and 16 intermediate columns);
-    # grouped: two bf16 activation rows and an fp32 output row per route,
-    # plus routing tables
-    decode = 2 * 2 * routes * I + routes * (I // 16) * H * 4
-    grouped = routes * (4 * I + 4 * H)
-    assert max(decode, grouped) <= size <= max(decode, grouped) + 64 * 1024
+    # decode: two bf16 activation planes per route slot; grouped: two bf16
+    # activation rows and an fp32 output row per route, plus routing tables
+    assert size >= 2 * 2 * routes * I
+    assert routes * (4 * I + 4 * H) <= size <= routes * (4 * I + 4 * H) + 64 * 1024
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
@@ -228,40 +224,23 @@ def _plan(desc, M, tuning=None):
     return p.path, p.fc1_chunks_per_wave, p.fc1_rows, p.fc2_rows
 
 
-def test_plan_resolves_path_form_and_shape(L):
-    # the split decode form where its registers, LDS and partial sums fit, the
-    # two-pass form elsewhere, the grouped path past the band
-    assert _plan(moe.Desc("nvfp4", 512, 2560, 320, 10, 1), 1) == (moe.PATH_DECODE_SPLIT, 8, 0, 0)
-    assert _plan(moe.Desc("mxfp4", 8, 256, 128, 2, 1), 1)[0] in (moe.PATH_DECODE_SPLIT, moe.PATH_DECODE_TWO_PASS)
+def test_plan_resolves_path_and_shape(L):
+    # the decode band with its built-in launch shape, the grouped path past it
+    e512 = moe.Desc("nvfp4", 512, 2560, 320, 10, 1)
+    assert _plan(e512, 1) == (moe.PATH_DECODE, 8, 32, 16)
+    assert _plan(moe.Desc("mxfp4", 8, 256, 128, 2, 1), 1) == (moe.PATH_DECODE, 4, 16, 32)
+    assert _plan(moe.Desc("mxfp4", 256, 7168, 256, 8, 4), 4) == (moe.PATH_DECODE, 8, 32, 16)
     assert _plan(moe.Desc("mxfp4", 128, 4096, 1536, 8, 4096), 4096) == (moe.PATH_GROUPED, 0, 0, 0)
-    two = _plan(moe.Desc("nvfp4", 512, 2560, 320, 10, 1), 1, moe.Tuning(0, 0, 0, moe.PATH_DECODE_TWO_PASS))
-    assert two == (moe.PATH_DECODE_TWO_PASS, 8, 32, 16)
-    # forcing the split form where it cannot run: unsupported, nothing launched
-    wide_h = moe.Desc("mxfp4", 16, 16384, 256, 8, 1)       # 256 FC2 tiles > 16 waves x 8
-    huge_part = moe.Desc("mxfp4", 16, 8192, 4096, 8, 8)    # 537 MB of partial sums
-    for big in (wide_h, huge_part):
-        assert _plan(big, 1)[0] == moe.PATH_DECODE_TWO_PASS
+    # explicit fields are kept, the rest resolved; the grouped path at any M
+    assert _plan(e512, 1, moe.Tuning(16, 16, 0, 0)) == (moe.PATH_DECODE, 16, 16, 16)
+    assert _plan(e512, 1, moe.Tuning(0, 0, 0, moe.PATH_GROUPED)) == (moe.PATH_GROUPED, 0, 0, 0)
+    # rejected requests: the same status moe_fp4_forward_ex gives
+    for bad in (moe.Tuning(3, 0, 0, 0), moe.Tuning(0, 0, 0, 3)):
         with pytest.raises(moe.MoeFp4Error) as ei:
-            moe.plan(big, 1, moe.Tuning(0, 0, 0, moe.PATH_DECODE_SPLIT))
-        assert ei.value.status == 2
-        assert L.moe_fp4_forward_ex(ctypes.byref(big.c()), 256, 16, 1, 4, 4, 16, 256, 1 << 40,
-                                    ctypes.byref(moe.Tuning(0, 0, 0, moe.PATH_DECODE_SPLIT)), 3, None) == 2
-    # 16 chunks per wave: not a split shape
-    small = moe.Desc("nvfp4", 512, 2560, 320, 10, 1)
+            moe.plan(e512, 1, bad)
+        assert ei.value.status == 1
+    with pytest.raises(moe.MoeFp4Error) as ei:
+        moe.plan(moe.Desc("nvfp4", 512, 2560, 320, 10, 8), 7, moe.Tuning(0, 0, 0, moe.PATH_DECODE))
+    assert ei.value.status == 2  # 70 route slots: past the decode band
     with pytest.raises(moe.MoeFp4Error):
-        moe.plan(small, 1, moe.Tuning(16, 0, 0, moe.PATH_DECODE_SPLIT))
-    assert _plan(small, 1, moe.Tuning(16, 0, 0, 0))[0] == moe.PATH_DECODE_TWO_PASS
-    # relu2 holds two W2 half-units per lane and tile
-    assert _plan(moe.Desc("mxfp4", 8, 2560, 256, 8, 1, fn="relu2"), 1, moe.Tuning(0, 0, 0, moe.PATH_DECODE_SPLIT))[0] \
-        == moe.PATH_DECODE_SPLIT
-    with pytest.raises(moe.MoeFp4Error):
-        moe.plan(small, 2)  # M past max_tokens
-
-
-def test_split_workspace_holds_partial_sums(L):
-    # per route slot and 16 intermediate columns, one fp32 row of H partial sums
-    d = moe.Desc("nvfp4", 512, 2560, 320, 10, 6)
-    slots, H, I = 60, 2560, 320
-    size = moe.workspace_bytes(d, 1)
-    need = slots * (I // 16) * H * 4 + 2 * 2 * slots * I
-    assert need <= size <= need + 1024
+        moe.plan(e512, 2)  # M past max_tokens

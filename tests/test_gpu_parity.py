@@ -125,27 +125,15 @@ def test_forward_small_shapes(fmt, E, H, I, M, k, seed):
     layer = make_layer(fmt, d, k, M)
     compare(run_layer(layer, d), acc, f"{fmt} E{E} H{H} I{I} M{M} k{k}")
     compare(run_layer(layer, d, ids_dtype=torch.int64), acc, "int64 ids")
-    # every launch shape the tuning hook accepts gives a valid result, in
-    # both forms of the decode path
+    # every launch shape the tuning hook accepts gives a valid result
     kl2 = 4 if I <= 128 else (8 if I <= 256 else 16)
     for kl1 in (4, 8, 16):
         for r1 in (16, 32):
             for r2 in (8, 16, 32):
                 if r2 * kl2 < 64:
                     continue
-                t = moe.Tuning(kl1, r1, r2, moe.PATH_DECODE_TWO_PASS)
-                compare(run_layer(layer, d, tuning=t), acc, f"  two-pass kl1={kl1} r1={r1} r2={r2}")
-    split_runs = 0
-    for kl1 in (0, 4, 8):
-        t = moe.Tuning(kl1, 0, 0, moe.PATH_DECODE_SPLIT)
-        try:
-            moe.plan(layer.desc, M, t)
-        except moe.MoeFp4Error as err:
-            assert err.status == 2 and kl1 != 0, f"split kl1={kl1}: {err}"
-            continue
-        compare(run_layer(layer, d, tuning=t), acc, f"  split kl1={kl1}")
-        split_runs += 1
-    assert split_runs >= 1
+                t = moe.Tuning(kl1, r1, r2, 0)
+                compare(run_layer(layer, d, tuning=t), acc, f"  shape kl1={kl1} r1={r1} r2={r2}")
 
 
 @pytest.mark.parametrize("name", ["tiny_mxfp4", "nvfp4_decode_e512", "nvfp4_multi_e288",
@@ -157,15 +145,6 @@ def test_forward_workloads_full_size(name):
     acc, _ = oracle.forward_f32(wl.fmt, d)
     layer = make_layer(wl.fmt, d, wl.k, max(wl.M, 16))
     compare(run_layer(layer, d), acc, name)
-    say(f"  built-in form: path {moe.plan(layer.desc, wl.M).path}")
-    for path in (moe.PATH_DECODE_TWO_PASS, moe.PATH_DECODE_SPLIT):
-        t = moe.Tuning(0, 0, 0, path)
-        try:
-            moe.plan(layer.desc, wl.M, t)
-        except moe.MoeFp4Error as err:
-            assert err.status == 2 and path == moe.PATH_DECODE_SPLIT
-            continue
-        compare(run_layer(layer, d, tuning=t), acc, f"{name} path {path}")
     if wl.n_invalid:
         assert (d["ids"] < 0).any() and (d["ids"] >= wl.E).any()
 
@@ -220,16 +199,15 @@ def test_poisoned_scratch_and_output_deterministic_and_inputs_unchanged():
     ids = to_dev(d["ids"])
     w = to_dev(d["w"])
     snap = [t.clone() for t in (x, ids, w, layer.prepared)]
-    for path in (moe.PATH_DECODE_SPLIT, moe.PATH_DECODE_TWO_PASS):
-        results = []
-        for rep in range(3):
-            layer.workspace.fill_(0xFF)  # NaN in every scratch word
-            out = torch.full((1, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
-            layer(x, ids, w, out=out, tuning=moe.Tuning(0, 0, 0, path))
-            torch.cuda.synchronize()
-            results.append(out.view(torch.int16).cpu().numpy().view(np.uint16))
-        compare(results[0], acc, f"poisoned scratch, path {path}")
-        assert all(np.array_equal(results[0], r) for r in results[1:]), "not bit-reproducible"
+    results = []
+    for rep in range(3):
+        layer.workspace.fill_(0xFF)  # NaN in every scratch word
+        out = torch.full((1, wl.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+        layer(x, ids, w, out=out)
+        torch.cuda.synchronize()
+        results.append(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    compare(results[0], acc, "poisoned scratch")
+    assert all(np.array_equal(results[0], r) for r in results[1:]), "not bit-reproducible"
     for a, b in zip(snap, (x, ids, w, layer.prepared)):
         assert torch.equal(a, b), "an input was modified"
 
