@@ -229,7 +229,10 @@ def test_plan_resolves_path_and_shape(L):
     e512 = moe.Desc("nvfp4", 512, 2560, 320, 10, 1)
     assert _plan(e512, 1) == (moe.PATH_DECODE, 8, 32, 16)
     assert _plan(moe.Desc("mxfp4", 8, 256, 128, 2, 1), 1) == (moe.PATH_DECODE, 4, 16, 32)
-    assert _plan(moe.Desc("mxfp4", 256, 7168, 256, 8, 4), 4) == (moe.PATH_DECODE, 8, 32, 16)
+    shard = moe.Desc("mxfp4", 256, 7168, 256, 8, 4)
+    assert _plan(shard, 1) == (moe.PATH_DECODE, 8, 16, 32)
+    assert _plan(shard, 4) == (moe.PATH_DECODE, 4, 32, 32)
+    assert _plan(moe.Desc("nvfp4", 288, 4096, 512, 8, 5), 5) == (moe.PATH_DECODE, 4, 32, 16)
     assert _plan(moe.Desc("mxfp4", 128, 4096, 1536, 8, 4096), 4096) == (moe.PATH_GROUPED, 0, 0, 0)
     # explicit fields are kept, the rest resolved; the grouped path at any M
     assert _plan(e512, 1, moe.Tuning(16, 16, 0, 0)) == (moe.PATH_DECODE, 16, 16, 16)
