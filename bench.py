@@ -259,12 +259,34 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / K, (time.perf_counter() - t0) / K, K
 
+    def launch_floor():
+        """Per step, K steps of two trivial kernels (one-element adds) as
+        graph replays: the floor of any two-launch layer step."""
+        t = torch.zeros(1, dtype=torch.float32, device=dev)
+        g = torch.cuda.CUDAGraph()
+        n = min(K, 512)
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                t.add_(1.0)
+                t.add_(1.0)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(max(1, K // n)):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / (n * max(1, K // n))
+
     for i in range(W):
         call(groups[i % len(groups)])
     torch.cuda.synchronize()
     log("[bench] warm-up done")
     value, wall_step, K = region()
     log(f"[bench] layer, cold rotation: {value:.3f} us/step")
+    floor_us = launch_floor()
+    log(f"[bench] two trivial kernels per step: {floor_us:.3f} us/step")
     fc1_us, _, _ = region(phases=1)
     fc2_us, _, _ = region(phases=2)
     log(f"[bench] fc1 only {fc1_us:.3f} us/launch, fc2 only {fc2_us:.3f} us/launch")
@@ -370,6 +392,7 @@ def main():
         "hbm_frac_layer": round(layer_bytes / (value * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "routed_bytes": {"fc1": b13, "fc2": b2},
         "kernel_us": {"fc1": round(fc1_us, 3), "fc2": round(fc2_us, 3), **aux},
+        "two_kernel_graph_floor_us": round(floor_us, 3),
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": dom, ("algorithmic_flops" if grouped else "algorithmic_bytes"): dom_work,
