@@ -48,8 +48,14 @@ struct DecodeShape {
   int r2;   // FC2 rows per workgroup: 8, 16, 32
 };
 
-// FC2 chunk lanes: the smallest of 4, 8, 16 that covers I (longer I loops).
-inline int fc2_chunk_lanes(const Layout& L) { return L.nC2 <= 4 ? 4 : (L.nC2 <= 8 ? 8 : 16); }
+// FC2 chunk lanes: 4 up to 4 chunks of I, 8 up to 16 (two groups of 8
+// chunks, loaded together), else 16 (longer I loops).  With 8 lanes a load
+// instruction reads 8 consecutive rows of each chunk, whole 128-byte lines;
+// 16 lanes read 4 rows (half lines).
+inline int fc2_chunk_lanes(const Layout& L) { return L.nC2 <= 4 ? 4 : (L.nC2 <= 16 ? 8 : 16); }
+
+// Chunk groups an FC2 lane loads at once: 2 for 8 lanes over 9..16 chunks.
+inline int fc2_chunk_groups(const Layout& L) { return fc2_chunk_lanes(L) == 8 && L.nC2 > 8 ? 2 : 1; }
 
 inline bool valid_shape(const Layout& L, const DecodeShape& s) {
   if (s.kl1 != 0 && s.kl1 != 4 && s.kl1 != 8 && s.kl1 != 16) return false;
@@ -65,12 +71,14 @@ inline bool valid_shape(const Layout& L, const DecodeShape& s) {
 //  - FC1 takes 4 chunks per wave (2 rows per lane, waves loop over more
 //    chunk groups) for short K and from 16 route slots on, where it was
 //    13-26% faster than 8; with fewer slots 8 is as fast or faster;
-//  - FC2 takes 32-row blocks when it has at most 8 chunk lanes (I <= 256),
-//    24-27% faster than 16 rows from M = 2 on; with 16 chunk lanes 16 rows.
+//  - FC2 takes 32-row blocks when its lanes cover I in one group of at most
+//    8 chunks (I <= 256), 24-27% faster than 16 rows from M = 2 on; with two
+//    groups (I up to 512) or 16 chunk lanes, 16 rows (32 rows were 26-36%
+//    slower there, 8 rows 14-60%).
 inline DecodeShape resolve_shape(const Layout& L, int slots, DecodeShape s) {
   if (s.kl1 == 0) s.kl1 = (L.nC1 <= 8 || slots >= 16) ? 4 : 8;
   if (s.r1 == 0) s.r1 = (int64_t)slots * L.nB1 * 2 >= 160 ? 32 : 16;
-  if (s.r2 == 0) s.r2 = fc2_chunk_lanes(L) <= 8 ? 32 : 16;
+  if (s.r2 == 0) s.r2 = fc2_chunk_lanes(L) <= 8 && fc2_chunk_groups(L) == 1 ? 32 : 16;
   return s;
 }
 

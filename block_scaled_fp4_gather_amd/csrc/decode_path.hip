@@ -316,7 +316,7 @@ __global__ void __launch_bounds__(1024)
 // slots.  Lane (g, p) owns chunk c0 + p of the expert's block rows
 // q = g + RG*j, j < T.  With STAGE, the activations of every route slot are
 // staged in LDS while the route lookup is in flight.
-template <int FMT, int KL, int R, bool STAGE, typename IdT>
+template <int FMT, int KL, int R, int CI, bool STAGE, typename IdT>
 __global__ void __launch_bounds__(64 * fc2_max_waves(KL))
     fc2_kernel(const uint8_t* __restrict__ prep, const Layout L, const IdT* __restrict__ ids,
                const float* __restrict__ tw, const int M, const int k,
@@ -354,17 +354,19 @@ __global__ void __launch_bounds__(64 * fc2_max_waves(KL))
     const uint8_t* tile = prep + fc2_tile_offset(L, e, hb);
     const uint8_t* sbase = tile + (int64_t)L.nC2 * 1024;
     const float g2 = FMT == kNVFP4 ? ((const float*)prep)[L.E + e] : 1.0f;
-    for (int c0 = 0; c0 < L.nC2; c0 += KL) {
-      const int c = c0 + p;
-      const bool cv = c < L.nC2;
-      const int cc = min(c, L.nC2 - 1);
-      u32x4 q[T];
-      uint32_t sd[T];
+    // CI groups of KL chunks per pass, all their loads issued together
+    for (int c0 = 0; c0 < L.nC2; c0 += CI * KL) {
+      u32x4 q[CI][T];
+      uint32_t sd[CI][T];
 #pragma unroll
-      for (int j = 0; j < T; ++j) {
-        const int row = row0 % 64 + g + RG * j;  // tile rows past H are zero padding
-        q[j] = __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)cc * 1024 + row * 16));
-        sd[j] = __builtin_nontemporal_load((const uint32_t*)(sbase + (cc / SPD) * 256 + row * 4));
+      for (int ci = 0; ci < CI; ++ci) {
+        const int cc = min(c0 + ci * KL + p, L.nC2 - 1);
+#pragma unroll
+        for (int j = 0; j < T; ++j) {
+          const int row = row0 % 64 + g + RG * j;  // tile rows past H are zero padding
+          q[ci][j] = __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)cc * 1024 + row * 16));
+          sd[ci][j] = __builtin_nontemporal_load((const uint32_t*)(sbase + (cc / SPD) * 256 + row * 4));
+        }
       }
       for (int t = 0; t < M; ++t) {
         uint64_t tm = token_routes(mask, t, k);
@@ -376,19 +378,26 @@ __global__ void __launch_bounds__(64 * fc2_max_waves(KL))
           tm &= tm - 1;
           wsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(R_.w), t * k + j));
         }
-        uint32_t ah[16], al[16];
-        if (STAGE) {
-          lds_chunk16(as + (int64_t)r * 2 * L.I + 32 * cc, ah);
-          lds_chunk16(as + (int64_t)r * 2 * L.I + L.I + 32 * cc, al);
-        } else {
-          load_chunk16(act_hi + (int64_t)r * L.I + 32 * cc, ah);
-          load_chunk16(act_lo + (int64_t)r * L.I + 32 * cc, al);
-        }
         float v[T];
 #pragma unroll
-        for (int j = 0; j < T; ++j) {
-          const f32x2_t sc = chunk_scale<FMT>(sd[j], cc);
-          v[j] = cv ? unit_dot2<FMT>(q[j], ah, al, sc) : 0.0f;
+        for (int ci = 0; ci < CI; ++ci) {
+          const int c = c0 + ci * KL + p;
+          const bool cv = c < L.nC2;
+          const int cc = min(c, L.nC2 - 1);
+          uint32_t ah[16], al[16];
+          if (STAGE) {
+            lds_chunk16(as + (int64_t)r * 2 * L.I + 32 * cc, ah);
+            lds_chunk16(as + (int64_t)r * 2 * L.I + L.I + 32 * cc, al);
+          } else {
+            load_chunk16(act_hi + (int64_t)r * L.I + 32 * cc, ah);
+            load_chunk16(act_lo + (int64_t)r * L.I + 32 * cc, al);
+          }
+#pragma unroll
+          for (int j = 0; j < T; ++j) {
+            const f32x2_t sc = chunk_scale<FMT>(sd[ci][j], cc);
+            const float d = cv ? unit_dot2<FMT>(q[ci][j], ah, al, sc) : 0.0f;
+            v[j] = ci == 0 ? d : v[j] + d;
+          }
         }
         const float y = fold_rows<KL, T>(v, p);
         if (p < T) part[(t * 16 + wave) * R + g + RG * p] += (y * g2) * wsum;
@@ -422,10 +431,10 @@ hipError_t launch_fc1(const Layout& L, const uint8_t* prep, const uint16_t* x, i
   return hipGetLastError();
 }
 
-template <int FMT, int KL, int R, typename IdT>
-hipError_t launch_fc2_r(const Layout& L, const uint8_t* prep, int M, int k, const IdT* ids,
-                        const float* tw, const uint16_t* ah, const uint16_t* al, uint16_t* out,
-                        hipStream_t st) {
+template <int FMT, int KL, int R, int CI, typename IdT>
+hipError_t launch_fc2_ci(const Layout& L, const uint8_t* prep, int M, int k, const IdT* ids,
+                         const float* tw, const uint16_t* ah, const uint16_t* al, uint16_t* out,
+                         hipStream_t st) {
   const int slots = M * k;
   const int waves = slots < fc2_max_waves(KL) ? slots : fc2_max_waves(KL);
   const size_t act_bytes = (size_t)slots * L.I * 4;
@@ -434,10 +443,22 @@ hipError_t launch_fc2_r(const Layout& L, const uint8_t* prep, int M, int k, cons
   const size_t lds = part_bytes + (stage ? act_bytes : 0);
   const dim3 grid((unsigned)((L.H + R - 1) / R)), block(64 * waves);
   if (stage)
-    hipLaunchKernelGGL((fc2_kernel<FMT, KL, R, true, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, ah, al, out);
+    hipLaunchKernelGGL((fc2_kernel<FMT, KL, R, CI, true, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, ah,
+                       al, out);
   else
-    hipLaunchKernelGGL((fc2_kernel<FMT, KL, R, false, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, ah, al, out);
+    hipLaunchKernelGGL((fc2_kernel<FMT, KL, R, CI, false, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, ah,
+                       al, out);
   return hipGetLastError();
+}
+
+template <int FMT, int KL, int R, typename IdT>
+hipError_t launch_fc2_r(const Layout& L, const uint8_t* prep, int M, int k, const IdT* ids,
+                        const float* tw, const uint16_t* ah, const uint16_t* al, uint16_t* out,
+                        hipStream_t st) {
+  if constexpr (KL == 8) {
+    if (fc2_chunk_groups(L) == 2) return launch_fc2_ci<FMT, KL, R, 2, IdT>(L, prep, M, k, ids, tw, ah, al, out, st);
+  }
+  return launch_fc2_ci<FMT, KL, R, 1, IdT>(L, prep, M, k, ids, tw, ah, al, out, st);
 }
 
 template <int FMT, int KL, typename IdT>

@@ -108,6 +108,9 @@ SMALL = [
     ("mxfp4", 16, 1024, 256, 8, 4, 5),
     ("nvfp4", 12, 2560, 64, 16, 2, 6),
     ("mxfp4", 3, 1536, 544, 2, 2, 7),   # I = 17 chunks: two FC2 batches
+    ("nvfp4", 6, 512, 320, 3, 3, 8),    # I = 10 chunks: FC2's two groups of 8, the second ragged
+    ("mxfp4", 5, 256, 512, 2, 2, 9),    # I = 16 chunks: two full groups
+    ("mxfp4", 4, 128, 288, 1, 2, 10),   # I = 9 chunks: one chunk in the second group
 ]
 
 
@@ -126,7 +129,7 @@ def test_forward_small_shapes(fmt, E, H, I, M, k, seed):
     compare(run_layer(layer, d), acc, f"{fmt} E{E} H{H} I{I} M{M} k{k}")
     compare(run_layer(layer, d, ids_dtype=torch.int64), acc, "int64 ids")
     # every launch shape the tuning hook accepts gives a valid result
-    kl2 = 4 if I <= 128 else (8 if I <= 256 else 16)
+    kl2 = 4 if I <= 128 else (8 if I <= 512 else 16)
     for kl1 in (4, 8, 16):
         for r1 in (16, 32):
             for r2 in (8, 16, 32):
