@@ -177,9 +177,9 @@ def main():
     log(f"[bench] {'grouped' if plan.path == moe.PATH_GROUPED else 'decode'} path, "
         f"shape kl1={plan.fc1_chunks_per_wave} r1={plan.fc1_rows} r2={plan.fc2_rows}")
 
-    # the decode band of the library: M <= min(16, 64 / k); past it, the grouped path
+    # the library's choice of path for this M (moe_fp4_plan)
     grouped = plan.path == moe.PATH_GROUPED
-    a8 = grouped and args.act == "mxfp8"  # the decode band keeps bf16 activations
+    a8 = grouped and args.act == "mxfp8"  # the decode path keeps bf16 activations
     sample = np.arange(wl.M)
     if grouped:
         rs = np.random.default_rng(wl.seed & 0xFFFF)

@@ -92,11 +92,21 @@ moe_fp4_status make_plan(const moe_fp4_desc* desc, const Layout& L, int32_t M,
       moe::prefill_max_workgroups(L, prefill_routes(desc)) >= ((int64_t)1 << 31))
     return MOE_FP4_EUNSUPPORTED;
   const int k = desc->top_k;
-  const bool decode_ok = k <= moe::kDecodeMaxSlots && M <= moe::decode_max_tokens(k);
-  if (path == MOE_FP4_PATH_AUTO) path = decode_ok ? MOE_FP4_PATH_DECODE : MOE_FP4_PATH_GROUPED;
+  // The decode path takes any M in chunks of at most decode_max_tokens(k)
+  // tokens.  By default: up to kDecodeMaxChunks chunks with bf16
+  // activations, one chunk with MXFP8 activations (whose grouped path
+  // quantises them), the grouped path beyond; the decode path for any M when
+  // E is past what the grouped path's route grouping holds.
+  const bool decode_ok = k <= moe::kDecodeMaxSlots;
+  const int mc = decode_ok ? moe::decode_max_tokens(k) : 1;
+  const int64_t chunks = ((int64_t)(M < 1 ? 1 : M) + mc - 1) / mc;
+  const int64_t auto_chunks = act_mxfp8(desc) ? 1 : moe::kDecodeMaxChunks;
+  if (path == MOE_FP4_PATH_AUTO)
+    path = decode_ok && (chunks <= auto_chunks || L.E > moe::kRouteMaxExperts) ? MOE_FP4_PATH_DECODE
+                                                                               : MOE_FP4_PATH_GROUPED;
   if (path == MOE_FP4_PATH_DECODE && !decode_ok) return MOE_FP4_EUNSUPPORTED;
   if (path == MOE_FP4_PATH_GROUPED && L.E > moe::kRouteMaxExperts) return MOE_FP4_EUNSUPPORTED;
-  if (path == MOE_FP4_PATH_DECODE) shape = moe::resolve_shape(L, (M < 1 ? 1 : M) * k, shape);
+  if (path == MOE_FP4_PATH_DECODE) shape = moe::resolve_shape(L, (M < mc ? (M < 1 ? 1 : M) : mc) * k, shape);
   plan->path = path;
   plan->shape = shape;
   return MOE_FP4_OK;
@@ -120,16 +130,33 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
   Plan plan;
   st = make_plan(desc, L, M, tuning, &plan);
   if (st != MOE_FP4_OK) return st;
-  if (plan.path != MOE_FP4_PATH_GROUPED && phases > 3) return MOE_FP4_EINVAL;
-  if ((int64_t)ws_bytes < workspace_total(L, desc)) return MOE_FP4_EWORKSPACE;
   const int k = desc->top_k;
+  const int mc = plan.path == MOE_FP4_PATH_GROUPED ? M : moe::decode_max_tokens(k);
+  if (plan.path != MOE_FP4_PATH_GROUPED && (phases > 3 || (M > mc && phases != 3))) return MOE_FP4_EINVAL;
+  if ((int64_t)ws_bytes < workspace_total(L, desc)) return MOE_FP4_EWORKSPACE;
   if (plan.path == MOE_FP4_PATH_GROUPED)
     return from_hip(moe::launch_prefill<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
                                              (uint8_t*)workspace, prefill_layout(L, desc), phases,
                                              act_mxfp8(desc), (hipStream_t)stream));
+  // decode: consecutive chunks of at most mc tokens, in order on the stream,
+  // each one FC1 + FC2 over the same workspace (a chunk's FC1 follows the
+  // previous chunk's FC2); the last, shorter chunk gets its own shape
   const moe::DecodeWs W = moe::decode_ws(L, decode_slots(desc));
-  return from_hip(moe::launch_decode<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
-                                          (uint8_t*)workspace, W, plan.shape, phases, (hipStream_t)stream));
+  for (int t0 = 0; t0 < M; t0 += mc) {
+    const int m = M - t0 < mc ? M - t0 : mc;
+    moe::DecodeShape shape = plan.shape;
+    if (m != mc && M > mc) {
+      shape = tuning ? moe::DecodeShape{tuning->fc1_chunks_per_wave, tuning->fc1_rows, tuning->fc2_rows}
+                     : moe::DecodeShape{0, 0, 0};
+      shape = moe::resolve_shape(L, m * k, shape);
+    }
+    const hipError_t err = moe::launch_decode<IdT>(L, (const uint8_t*)prepared, x + (int64_t)t0 * L.H, m, k,
+                                                   ids + (int64_t)t0 * k, w + (int64_t)t0 * k,
+                                                   out + (int64_t)t0 * L.H, (uint8_t*)workspace, W, shape,
+                                                   phases, (hipStream_t)stream);
+    if (err != hipSuccess) return MOE_FP4_EHIP;
+  }
+  return MOE_FP4_OK;
 }
 
 }  // namespace

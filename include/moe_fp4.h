@@ -166,9 +166,12 @@ moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size
  * must be ordered on one stream.
  *
  * Two execution paths, chosen by M (both compute the layer above):
- *   decode  (M <= min(16, 64 / k)): FC1 and FC2 as streamed FP4 GEMVs, each
- *           routed expert's weights read once per call (b12x PR #22, What);
- *           results are bit-reproducible.
+ *   decode  FC1 and FC2 as streamed FP4 GEMVs over chunks of up to
+ *           C = min(16, 64 / k) tokens, one launch pair per chunk in order on
+ *           the stream, each routed expert's weights read once per chunk
+ *           (b12x PR #22, What); results are bit-reproducible.  Taken for
+ *           M <= 4C with bf16 activations, M <= C with MXFP8 activations,
+ *           and for every M when E > 8192.
  *   grouped (any other M): routes grouped by expert in route order, FC1 and
  *           FC2 as grouped GEMMs on the matrix cores over bf16 operands (FP4
  *           dequantised exactly) with fp32 accumulation, per-route fp32 rows
@@ -181,8 +184,8 @@ moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size
  *           FP8 x FP4 matrix instruction (the W4A8-MX variant above).
  *           Results are bit-reproducible.
  * The activation function (act_fn) is the same on both paths.
- * Returns MOE_FP4_EUNSUPPORTED when max_tokens * k > 2^22, or when the
- * grouped path is needed and E > 8192. */
+ * Returns MOE_FP4_EUNSUPPORTED when max_tokens * k > 2^22, or when k > 64
+ * and the grouped path cannot run (E > 8192). */
 moe_fp4_status moe_fp4_forward(const moe_fp4_desc* desc, const void* prepared,
                                const uint16_t* x, int32_t M, const int32_t* topk_ids,
                                const float* topk_w, uint16_t* out, void* workspace,
@@ -205,7 +208,7 @@ moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prep
 /* Execution path selector for moe_fp4_forward_ex. */
 typedef enum {
   MOE_FP4_PATH_AUTO = 0,    /* by M, as moe_fp4_forward */
-  MOE_FP4_PATH_DECODE = 1,  /* decode path; MOE_FP4_EUNSUPPORTED when M is past its band */
+  MOE_FP4_PATH_DECODE = 1,  /* decode path at any M (in chunks); MOE_FP4_EUNSUPPORTED when k > 64 */
   MOE_FP4_PATH_GROUPED = 2  /* grouped path at any M */
 } moe_fp4_path;
 
@@ -233,7 +236,8 @@ typedef struct {
  * same stream); 3 queues both.  On the grouped path, 4 queues only its
  * routing (the grouping of the routes by expert) and 8 only its combine
  * (which reads what a phase-2 call left), so the two GEMM launches can be
- * timed on their own; the decode path rejects 4 and 8. */
+ * timed on their own; the decode path rejects 4 and 8, and 1 and 2 when M
+ * takes more than one chunk. */
 moe_fp4_status moe_fp4_forward_ex(const moe_fp4_desc* desc, const void* prepared,
                                   const uint16_t* x, int32_t M, const int32_t* topk_ids,
                                   const float* topk_w, uint16_t* out, void* workspace,

@@ -118,18 +118,33 @@ def test_tuning_hook_rejects_bad_shapes(L):
     assert status(None, phases=4) == 1  # M = 1 takes the decode path: no routing-only phase
 
 
-def test_decode_path_rejects_past_its_band(L):
-    # forcing the decode path where M * k > 64 or M > 16: unsupported, nothing launched
-    wide = moe.Desc("nvfp4", 512, 2560, 320, 10, 8)
+def test_decode_path_past_one_launch_pair(L):
+    # past M * k = 64 route slots or M = 16 the decode path runs in chunks
+    # (chosen automatically up to 4 chunks with bf16 activations); the
+    # measurement hook's part-of-call phases need a single chunk
+    wide = moe.Desc("nvfp4", 512, 2560, 320, 10, 64)     # 6 tokens per chunk
     t = moe.Tuning(0, 0, 0, moe.PATH_DECODE)
-    assert L.moe_fp4_forward_ex(ctypes.byref(wide.c()), 256, 16, 7, 4, 4, 16, 256, 1 << 30,
-                                ctypes.byref(t), 3, None) == 2   # 70 route slots > 64
-    # the grouped path's expert grouping holds at most 8192 experts
+    assert _plan(wide, 7, t)[0] == moe.PATH_DECODE
+    assert _plan(wide, 24)[0] == moe.PATH_DECODE         # 4 chunks
+    assert _plan(wide, 25)[0] == moe.PATH_GROUPED        # 5
+    assert _plan(wide, 64, t)[0] == moe.PATH_DECODE
+    for ph in (1, 2):
+        assert L.moe_fp4_forward_ex(ctypes.byref(wide.c()), 256, 16, 7, 4, 4, 16, 256, 1 << 30,
+                                    ctypes.byref(t), ph, None) == 1
+    # MXFP8 activations: the decode path only within one chunk by default
+    a8 = moe.Desc("mxfp4", 256, 2048, 256, 8, 64, "mxfp8")
+    assert _plan(a8, 8)[0] == moe.PATH_DECODE
+    assert _plan(a8, 9)[0] == moe.PATH_GROUPED
+    assert _plan(moe.Desc("mxfp4", 256, 2048, 256, 8, 64), 9)[0] == moe.PATH_DECODE
+    # the grouped path's expert grouping holds at most 8192 experts; past it
+    # the decode path takes every M
     wide_e = moe.Desc("mxfp4", 9000, 64, 32, 8, 64)
-    assert _forward_status(L, wide_e, M=64) == 2
-    many = moe.Desc("mxfp4", 8, 256, 128, 1, 32)
-    assert L.moe_fp4_forward_ex(ctypes.byref(many.c()), 256, 16, 17, 4, 4, 16, 256, 1 << 30,
-                                ctypes.byref(t), 3, None) == 2   # 17 tokens > 16
+    assert _plan(wide_e, 64)[0] == moe.PATH_DECODE
+    with pytest.raises(moe.MoeFp4Error) as ei:
+        moe.plan(wide_e, 64, moe.Tuning(0, 0, 0, moe.PATH_GROUPED))
+    assert ei.value.status == 2
+    many = moe.Desc("mxfp4", 8, 256, 128, 1, 32)          # 16 tokens per chunk
+    assert _plan(many, 17, t)[0] == moe.PATH_DECODE
 
 
 def test_workspace_sizes_do_not_depend_on_m(L):
@@ -243,7 +258,7 @@ def test_plan_resolves_path_and_shape(L):
             moe.plan(e512, 1, bad)
         assert ei.value.status == 1
     with pytest.raises(moe.MoeFp4Error) as ei:
-        moe.plan(moe.Desc("nvfp4", 512, 2560, 320, 10, 8), 7, moe.Tuning(0, 0, 0, moe.PATH_DECODE))
-    assert ei.value.status == 2  # 70 route slots: past the decode band
+        moe.plan(moe.Desc("nvfp4", 512, 2560, 320, 65, 8), 1, moe.Tuning(0, 0, 0, moe.PATH_DECODE))
+    assert ei.value.status == 2  # k = 65: more route slots than one wave holds
     with pytest.raises(moe.MoeFp4Error):
         moe.plan(e512, 2)  # M past max_tokens

@@ -67,7 +67,7 @@ def test_grouped_small_shapes(fmt, E, H, I, M, k, seed, hot):
     got = run_layer(layer, d, tuning=GROUPED)
     compare(got, acc, label + " grouped")
     # the automatic choice gives the same bits when it picks the grouped path
-    if M > min(16, 64 // k):
+    if moe.plan(layer.desc, M).path == moe.PATH_GROUPED:
         assert np.array_equal(run_layer(layer, d), got)
         assert np.array_equal(run_layer(layer, d, ids_dtype=torch.int64), got), "int64 ids"
     # repeated calls are bit-identical
@@ -95,33 +95,36 @@ def test_grouped_token_outputs_do_not_depend_on_the_batch():
 def test_grouped_invalid_ids_with_nan_poisoned_expert_zero():
     for fmt, poison in (("mxfp4", 0xFF), ("nvfp4", 0x7F)):
         rng = np.random.default_rng(32)
-        d, _, _ = random_case(rng, fmt, 6, 512, 64, 40, 4)
-        d["ids"][:] = rng.integers(1, 6, size=(40, 4))
+        M = 80  # past the decode path's automatic range (4 chunks of 16 tokens)
+        d, _, _ = random_case(rng, fmt, 6, 512, 64, M, 4)
+        d["ids"][:] = rng.integers(1, 6, size=(M, 4))
         d["w13_scales"][0] = poison
         d["w2_scales"][0] = poison
-        d["ids"][:, 2] = np.resize(np.array([-1, 6, 2**31 - 1, -(2**31)], np.int32), 40)
+        d["ids"][:, 2] = np.resize(np.array([-1, 6, 2**31 - 1, -(2**31)], np.int32), M)
         acc, _ = oracle.forward_f32(fmt, d)
         assert np.isfinite(acc).all()
-        layer = make_layer(fmt, d, 4, 40)
+        layer = make_layer(fmt, d, 4, M)
+        assert moe.plan(layer.desc, M).path == moe.PATH_GROUPED
         compare(run_layer(layer, d), acc, f"{fmt} poisoned expert 0, grouped")
         d64 = dict(d)
         d64["ids"] = d["ids"].astype(np.int64)
-        d64["ids"][:, 2] = np.resize(np.array([-(2**40), 2**40, 2**62, 6], np.int64), 40)
+        d64["ids"][:, 2] = np.resize(np.array([-(2**40), 2**40, 2**62, 6], np.int64), M)
         compare(run_layer(layer, d64, ids_dtype=torch.int64), acc, f"{fmt} int64 out-of-range ids")
 
 
 def test_grouped_all_invalid_and_poisoned_workspace():
     rng = np.random.default_rng(33)
-    d, _, _ = random_case(rng, "nvfp4", 4, 256, 64, 30, 2)
+    d, _, _ = random_case(rng, "nvfp4", 4, 256, 64, 70, 2)   # 70 tokens: the grouped path
     d["ids"][:10] = np.array([-1, 4], np.int32)       # tokens 0..9: no valid route
-    layer = make_layer("nvfp4", d, 2, 30)
+    layer = make_layer("nvfp4", d, 2, 70)
+    assert moe.plan(layer.desc, 70).path == moe.PATH_GROUPED
     acc, _ = oracle.forward_f32("nvfp4", d)
     x = to_dev(d["x"]).view(torch.bfloat16)
     ids, w = to_dev(d["ids"]), to_dev(d["w"])
     outs = []
     for rep in range(2):
         layer.workspace.fill_(0xFF)
-        out = torch.full((30, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+        out = torch.full((70, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
         layer(x, ids, w, out=out)
         torch.cuda.synchronize()
         outs.append(out.view(torch.int16).cpu().numpy().view(np.uint16))
@@ -130,7 +133,7 @@ def test_grouped_all_invalid_and_poisoned_workspace():
     assert np.array_equal(outs[0], outs[1])
     # every route invalid
     d["ids"][:] = -1
-    out = torch.full((30, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((70, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
     layer(x, to_dev(d["ids"]), w, out=out)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), torch.zeros_like(out.view(torch.int16)))
@@ -212,23 +215,23 @@ def test_prefill_workload_full_size_sampled():
 
 @pytest.mark.parametrize("fmt,k", [("mxfp4", 4), ("nvfp4", 8)])
 def test_band_edge_both_paths(fmt, k):
-    """At the last M of the decode band and the first past it, the automatic
-    path and the forced other path (where it exists) both match the oracle."""
+    """Around the edges of one decode launch pair (M = min(16, 64/k)) and of
+    the decode path's automatic range (4 such chunks), the automatic path,
+    the forced decode path (in chunks past one) and the forced grouped path
+    all match the oracle."""
     edge = min(16, 64 // k)
-    for M in (edge, edge + 1):
+    for M in (edge, edge + 1, 4 * edge, 4 * edge + 1):
         rng = np.random.default_rng(40 + M)
         d, _, _ = random_case(rng, fmt, 16, 512, 128, M, k)
         d["ids"][0, 0] = -1
+        d["ids"][-1, -1] = 99
         acc, _ = oracle.forward_f32(fmt, d)
         layer = make_layer(fmt, d, k, M)
+        want = moe.PATH_DECODE if M <= 4 * edge else moe.PATH_GROUPED
+        assert moe.plan(layer.desc, M).path == want
         compare(run_layer(layer, d), acc, f"{fmt} k{k} M{M} auto")
         compare(run_layer(layer, d, tuning=GROUPED), acc, f"{fmt} k{k} M{M} grouped")
-        if M == edge:
-            compare(run_layer(layer, d, tuning=moe.Tuning(0, 0, 0, moe.PATH_DECODE)), acc,
-                    f"{fmt} k{k} M{M} decode")
-        else:
-            with pytest.raises(moe.MoeFp4Error):
-                run_layer(layer, d, tuning=moe.Tuning(0, 0, 0, moe.PATH_DECODE))
+        compare(run_layer(layer, d, tuning=moe.Tuning(0, 0, 0, moe.PATH_DECODE)), acc, f"{fmt} k{k} M{M} decode")
 
 
 def test_grouped_nvfp4_decode_geometry_many_tokens():
