@@ -17,6 +17,10 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Chunks of decode_max_tokens(k) tokens a call with bf16 activations takes
+// on the decode path by default; more tokens take the grouped path.
+constexpr int kDecodeMaxChunks = 4;
+
 moe_fp4_status desc_layout(const moe_fp4_desc* d, Layout* L) {
   if (!d) return MOE_FP4_EINVAL;
   if (d->format != MOE_FP4_MXFP4 && d->format != MOE_FP4_NVFP4) return MOE_FP4_EINVAL;
@@ -100,7 +104,7 @@ moe_fp4_status make_plan(const moe_fp4_desc* desc, const Layout& L, int32_t M,
   const bool decode_ok = k <= moe::kDecodeMaxSlots;
   const int mc = decode_ok ? moe::decode_max_tokens(k) : 1;
   const int64_t chunks = ((int64_t)(M < 1 ? 1 : M) + mc - 1) / mc;
-  const int64_t auto_chunks = act_mxfp8(desc) ? 1 : moe::kDecodeMaxChunks;
+  const int64_t auto_chunks = act_mxfp8(desc) ? 1 : kDecodeMaxChunks;
   if (path == MOE_FP4_PATH_AUTO)
     path = decode_ok && (chunks <= auto_chunks || L.E > moe::kRouteMaxExperts) ? MOE_FP4_PATH_DECODE
                                                                                : MOE_FP4_PATH_GROUPED;

@@ -35,10 +35,6 @@ inline DecodeWs decode_ws(const Layout& L, int slots) {
   return w;
 }
 
-// Chunks of decode_max_tokens tokens a call takes on the decode path by
-// default; more tokens take the grouped path.
-constexpr int kDecodeMaxChunks = 4;
-
 // Largest M one decode launch pair takes for top-k routing.
 inline int decode_max_tokens(int k) {
   const int m = kDecodeMaxSlots / k;
