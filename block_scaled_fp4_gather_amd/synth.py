@@ -134,6 +134,21 @@ WORKLOADS = {
     "mxfp4_prefill_e128": Workload(
         "mxfp4_prefill_e128", "mxfp4", E=128, H=4096, I=1536, M=4096, k=8, seed=SEED_BASE + 4,
         description="MXFP4 prefill E128/H4096/I1536, M=4096, top-8"),
+    # Extra sweep points (not configurations): the decoder-only geometries at
+    # the other routed-row counts of the pages' table (b12x #459, PR body:
+    # 10, 40 and 63 routed rows), as M tokens x top-k routes.
+    "nvfp4_e512_routed40": Workload(
+        "nvfp4_e512_routed40", "nvfp4", E=512, H=2560, I=320, M=4, k=10, seed=SEED_BASE + 100,
+        description="NVFP4 E512/H2560/I320, M=4, top-10 (40 routes)"),
+    "nvfp4_e512_routed63": Workload(
+        "nvfp4_e512_routed63", "nvfp4", E=512, H=2560, I=320, M=7, k=9, seed=SEED_BASE + 101,
+        description="NVFP4 E512/H2560/I320, M=7, top-9 (63 routes)"),
+    "nvfp4_e288_routed10": Workload(
+        "nvfp4_e288_routed10", "nvfp4", E=288, H=4096, I=512, M=1, k=10, seed=SEED_BASE + 102,
+        description="NVFP4 E288/H4096/I512, M=1, top-10 (10 routes)"),
+    "nvfp4_e288_routed63": Workload(
+        "nvfp4_e288_routed63", "nvfp4", E=288, H=4096, I=512, M=7, k=9, seed=SEED_BASE + 103,
+        description="NVFP4 E288/H4096/I512, M=7, top-9 (63 routes)"),
 }
 
 # Stream ids: one per drawn tensor, so that changing one shape leaves the

@@ -140,7 +140,9 @@ def test_forward_small_shapes(fmt, E, H, I, M, k, seed):
 
 
 @pytest.mark.parametrize("name", ["tiny_mxfp4", "nvfp4_decode_e512", "nvfp4_multi_e288",
-                                  "mxfp4_shard_e256_m1", "mxfp4_shard_e256_m2", "mxfp4_shard_e256_m4"])
+                                  "mxfp4_shard_e256_m1", "mxfp4_shard_e256_m2", "mxfp4_shard_e256_m4",
+                                  "nvfp4_e512_routed40", "nvfp4_e512_routed63", "nvfp4_e288_routed10",
+                                  "nvfp4_e288_routed63"])
 def test_forward_workloads_full_size(name):
     wl = synth.WORKLOADS[name]
     say(f"  generate {name}")
