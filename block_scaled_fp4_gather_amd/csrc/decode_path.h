@@ -69,14 +69,15 @@ inline bool valid_shape(const Layout& L, const DecodeShape& s) {
 // E512/H2560/I320 NVFP4 (M = 1), E288/H4096/I512 NVFP4 (M = 5) and
 // E256/H7168/I256 MXFP4 (M = 1, 2, 4) decode shapes:
 //  - FC1 takes 4 chunks per wave (2 rows per lane, waves loop over more
-//    chunk groups) for short K and from 16 route slots on, where it was
-//    13-26% faster than 8; with fewer slots 8 is as fast or faster;
+//    chunk groups) for K up to 128 chunks and from 16 route slots on, where
+//    it was 13-26% faster than 8 (21% on E288/H4096 at M = 1); with longer
+//    K (4 chunk groups per wave) and fewer slots 8 is faster;
 //  - FC2 takes 32-row blocks when its lanes cover I in one group of at most
 //    8 chunks (I <= 256), 24-27% faster than 16 rows from M = 2 on; with two
 //    groups (I up to 512) or 16 chunk lanes, 16 rows (32 rows were 26-36%
 //    slower there, 8 rows 14-60%).
 inline DecodeShape resolve_shape(const Layout& L, int slots, DecodeShape s) {
-  if (s.kl1 == 0) s.kl1 = (L.nC1 <= 8 || slots >= 16) ? 4 : 8;
+  if (s.kl1 == 0) s.kl1 = (L.nC1 <= 128 || slots >= 16) ? 4 : 8;
   if (s.r1 == 0) s.r1 = (int64_t)slots * L.nB1 * 2 >= 160 ? 32 : 16;
   if (s.r2 == 0) s.r2 = fc2_chunk_lanes(L) <= 8 && fc2_chunk_groups(L) == 1 ? 32 : 16;
   return s;

@@ -242,7 +242,7 @@ def _plan(desc, M, tuning=None):
 def test_plan_resolves_path_and_shape(L):
     # the decode band with its built-in launch shape, the grouped path past it
     e512 = moe.Desc("nvfp4", 512, 2560, 320, 10, 1)
-    assert _plan(e512, 1) == (moe.PATH_DECODE, 8, 32, 16)
+    assert _plan(e512, 1) == (moe.PATH_DECODE, 4, 32, 16)
     assert _plan(moe.Desc("mxfp4", 8, 256, 128, 2, 1), 1) == (moe.PATH_DECODE, 4, 16, 32)
     shard = moe.Desc("mxfp4", 256, 7168, 256, 8, 4)
     assert _plan(shard, 1) == (moe.PATH_DECODE, 8, 16, 32)
