@@ -20,7 +20,10 @@
 //        at most one route slot per wave); its waves split the group's route
 //        slots (experts); the weighted expert sums meet in LDS and are
 //        written to the output as bf16, overwriting it.
-// Experts are streamed once per call however many tokens route to them: a
+// FC1 streams each routed expert once per launch pair however many of its
+// tokens (at most min(16, 64/k); larger calls run in chunks) route to it,
+// FC2 once per token group (one group unless a wave would loop over 3 or
+// more route slots; an expert shared by two groups is read by both): a
 // slot works only if its id is valid and no earlier slot holds the same id
 // (b12x PR #22, Notes: re-reading weights per routed row is what limited the
 // prior kernel to M=1).  Invalid ids read nothing and add nothing (b12x PR
