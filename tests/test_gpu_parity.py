@@ -111,6 +111,8 @@ SMALL = [
     ("nvfp4", 6, 512, 320, 3, 3, 8),    # I = 10 chunks: FC2's two groups of 8, the second ragged
     ("mxfp4", 5, 256, 512, 2, 2, 9),    # I = 16 chunks: two full groups
     ("mxfp4", 4, 128, 288, 1, 2, 10),   # I = 9 chunks: one chunk in the second group
+    ("mxfp4", 24, 512, 64, 3, 20, 11),  # k = 20 > 16 waves: FC2 token groups of one token
+    ("nvfp4", 8, 5632, 64, 16, 4, 12),  # 64 slots, 352 FC2 row blocks: groups grown past 1280 workgroups
 ]
 
 
