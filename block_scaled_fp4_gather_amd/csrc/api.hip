@@ -19,7 +19,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Chunks of decode_max_tokens(k) tokens a call with bf16 activations takes
 // on the decode path by default; more tokens take the grouped path.
-constexpr int kDecodeMaxChunks = 4;
+constexpr int kDecodeMaxChunks = 6;
 
 moe_fp4_status desc_layout(const moe_fp4_desc* d, Layout* L) {
   if (!d) return MOE_FP4_EINVAL;
@@ -45,11 +45,11 @@ moe_fp4_status desc_layout(const moe_fp4_desc* d, Layout* L) {
   return MOE_FP4_OK;
 }
 
-// Route slots the workspace is sized for; it depends only on the descriptor.
+// Route slots the decode workspace is sized for (every route of max_tokens
+// tokens: the decode path keeps the activation rows of all its chunks); it
+// depends only on the descriptor.
 int decode_slots(const moe_fp4_desc* d) {
-  const int cap = moe::decode_max_tokens(d->top_k);
-  const int m = d->max_tokens < 1 ? 1 : (d->max_tokens > cap ? cap : d->max_tokens);
-  return m * d->top_k;
+  return (d->max_tokens < 1 ? 1 : d->max_tokens) * d->top_k;
 }
 
 // Routes the grouped path's workspace is sized for (desc capacity).
@@ -135,32 +135,17 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
   st = make_plan(desc, L, M, tuning, &plan);
   if (st != MOE_FP4_OK) return st;
   const int k = desc->top_k;
-  const int mc = plan.path == MOE_FP4_PATH_GROUPED ? M : moe::decode_max_tokens(k);
-  if (plan.path != MOE_FP4_PATH_GROUPED && (phases > 3 || (M > mc && phases != 3))) return MOE_FP4_EINVAL;
+  if (plan.path != MOE_FP4_PATH_GROUPED && phases > 3) return MOE_FP4_EINVAL;
   if ((int64_t)ws_bytes < workspace_total(L, desc)) return MOE_FP4_EWORKSPACE;
   if (plan.path == MOE_FP4_PATH_GROUPED)
     return from_hip(moe::launch_prefill<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
                                              (uint8_t*)workspace, prefill_layout(L, desc), phases,
                                              act_mxfp8(desc), (hipStream_t)stream));
-  // decode: consecutive chunks of at most mc tokens, in order on the stream,
-  // each one FC1 + FC2 over the same workspace (a chunk's FC1 follows the
-  // previous chunk's FC2); the last, shorter chunk gets its own shape
+  // decode: one FC1 launch over all chunks of decode_max_tokens(k) tokens
+  // (the grid's second dimension), one FC2 launch over all tokens
   const moe::DecodeWs W = moe::decode_ws(L, decode_slots(desc));
-  for (int t0 = 0; t0 < M; t0 += mc) {
-    const int m = M - t0 < mc ? M - t0 : mc;
-    moe::DecodeShape shape = plan.shape;
-    if (m != mc && M > mc) {
-      shape = tuning ? moe::DecodeShape{tuning->fc1_chunks_per_wave, tuning->fc1_rows, tuning->fc2_rows}
-                     : moe::DecodeShape{0, 0, 0};
-      shape = moe::resolve_shape(L, m * k, shape);
-    }
-    const hipError_t err = moe::launch_decode<IdT>(L, (const uint8_t*)prepared, x + (int64_t)t0 * L.H, m, k,
-                                                   ids + (int64_t)t0 * k, w + (int64_t)t0 * k,
-                                                   out + (int64_t)t0 * L.H, (uint8_t*)workspace, W, shape,
-                                                   phases, (hipStream_t)stream);
-    if (err != hipSuccess) return MOE_FP4_EHIP;
-  }
-  return MOE_FP4_OK;
+  return from_hip(moe::launch_decode<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
+                                          (uint8_t*)workspace, W, plan.shape, phases, (hipStream_t)stream));
 }
 
 }  // namespace

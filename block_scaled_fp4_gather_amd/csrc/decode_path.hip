@@ -20,10 +20,11 @@
 //        at most one route slot per wave); its waves split the group's route
 //        slots (experts); the weighted expert sums meet in LDS and are
 //        written to the output as bf16, overwriting it.
-// FC1 streams each routed expert once per launch pair however many of its
-// tokens (at most min(16, 64/k); larger calls run in chunks) route to it,
-// FC2 once per token group (one group unless a wave would loop over 3 or
-// more route slots; an expert shared by two groups is read by both): a
+// FC1 streams each routed expert once per token chunk (at most min(16,
+// 64/k) tokens, the chunks on the grid's second dimension) however many of
+// the chunk's tokens route to it, FC2 once per token group (one group unless
+// a wave would loop over 3 or more route slots; an expert shared by two
+// groups is read by both): a
 // slot works only if its id is valid and no earlier slot holds the same id
 // (b12x PR #22, Notes: re-reading weights per routed row is what limited the
 // prior kernel to M=1).  Invalid ids read nothing and add nothing (b12x PR
@@ -221,13 +222,23 @@ __device__ __forceinline__ void lds_chunk16(const uint16_t* p, uint32_t* d) {
 template <int FMT, int KL, int R, typename IdT>
 __global__ void __launch_bounds__(1024)
     fc1_kernel(const uint8_t* __restrict__ prep, const Layout L, const uint16_t* __restrict__ x,
-               const IdT* __restrict__ ids, const int M, const int k,
+               const IdT* __restrict__ ids, const int M_all, const int k, const int mc,
                uint16_t* __restrict__ act_hi, uint16_t* __restrict__ act_lo) {
   constexpr int SPD = FMT == kMXFP4 ? 4 : 2;  // chunks per scale dword
   constexpr int RG = 64 / KL;                 // row groups of a wave
   constexpr int T = R / RG;                   // rows per lane
   constexpr int NB = 64 / R;                  // blocks per tile
   extern __shared__ u32x4 lds_raw[];
+  // Token chunk blockIdx.y: tokens c0 .. c0 + M - 1 (mc per chunk, at most 64
+  // route slots, one per lane of the route table), whose activations, route
+  // slots and activation rows are contiguous; experts are deduplicated
+  // within the chunk.
+  const int c0 = blockIdx.y * mc;
+  const int M = min(mc, M_all - c0);
+  x += (int64_t)c0 * L.H;
+  ids += (int64_t)c0 * k;
+  act_hi += (int64_t)c0 * k * L.I;
+  act_lo += (int64_t)c0 * k * L.I;
   uint16_t* xs = (uint16_t*)lds_raw;                // [H] activations of token t0
   float* part = (float*)(xs + align_up(L.H, 64));  // [token index][16 waves][R rows]
   const int lane = threadIdx.x & 63;
@@ -237,6 +248,7 @@ __global__ void __launch_bounds__(1024)
   const int blk = blockIdx.x % NB;
   const int b = (blockIdx.x / NB) % L.nB1;
   const int s = (blockIdx.x / NB) / L.nB1;
+  if (s >= M * k) return;  // a slot past the last chunk's tokens
   const int t0 = s / k;  // the slot's own token routes to the slot's expert
   const int ngroups = (L.nC1 + W * KL - 1) / (W * KL);
 
@@ -433,16 +445,20 @@ __global__ void __launch_bounds__(64 * fc2_max_waves(KL))
 template <int FMT, int KL, typename IdT>
 hipError_t launch_fc1(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                       const IdT* ids, uint16_t* act_hi, uint16_t* act_lo, int R, hipStream_t st) {
-  const int slots = M * k;
+  const int mc = M < decode_max_tokens(k) ? M : decode_max_tokens(k);  // tokens per chunk
+  const int slots = mc * k;
   const int groups = (L.nC1 + KL - 1) / KL;
   const int waves = groups < kMaxWaves ? groups : kMaxWaves;
   const bool big = R == 32;
-  const size_t lds = 2 * (size_t)align_up(L.H, 64) + (size_t)M * 16 * R * sizeof(float);
-  const dim3 grid((unsigned)((int64_t)slots * L.nB1 * (64 / R))), block(64 * waves);
+  const size_t lds = 2 * (size_t)align_up(L.H, 64) + (size_t)mc * 16 * R * sizeof(float);
+  const dim3 grid((unsigned)((int64_t)slots * L.nB1 * (64 / R)), (unsigned)((M + mc - 1) / mc)),
+      block(64 * waves);
   if (big)
-    hipLaunchKernelGGL((fc1_kernel<FMT, KL, 32, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, act_hi, act_lo);
+    hipLaunchKernelGGL((fc1_kernel<FMT, KL, 32, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, mc, act_hi,
+                       act_lo);
   else
-    hipLaunchKernelGGL((fc1_kernel<FMT, KL, 16, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, act_hi, act_lo);
+    hipLaunchKernelGGL((fc1_kernel<FMT, KL, 16, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, mc, act_hi,
+                       act_lo);
   return hipGetLastError();
 }
 
@@ -458,11 +474,12 @@ hipError_t launch_fc2_ci(const Layout& L, const uint8_t* prep, int M, int k, con
   // E288 at M = 5; 2 slots per wave stay faster in one group.
   const int maxw = fc2_max_waves(KL);
   const int64_t nhb = (L.H + R - 1) / R;
-  int tg = M;
-  if ((int64_t)M * k > 2 * maxw) {
+  const int mc = decode_max_tokens(k);  // a group's route table fits one wave
+  int tg = M < mc ? M : mc;
+  if ((int64_t)tg * k > 2 * maxw) {
     const int tg0 = k >= maxw ? 1 : maxw / k;
     tg = tg0;
-    while (tg < M && nhb * ((M + tg - 1) / tg) > 1280) tg += tg0;
+    while (tg < M && tg + tg0 <= mc && nhb * ((M + tg - 1) / tg) > 1280) tg += tg0;
     if (tg > M) tg = M;
   }
   const int slots = tg * k;

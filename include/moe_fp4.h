@@ -166,12 +166,12 @@ moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size
  * must be ordered on one stream.
  *
  * Two execution paths, chosen by M (both compute the layer above):
- *   decode  FC1 and FC2 as streamed FP4 GEMVs over chunks of up to
- *           C = min(16, 64 / k) tokens, one launch pair per chunk in order on
- *           the stream, each routed expert's weights read once per chunk
- *           (b12x PR #22, What); results are bit-reproducible.  Taken for
- *           M <= 4C with bf16 activations, M <= C with MXFP8 activations,
- *           and for every M when E > 8192.
+ *   decode  FC1 and FC2 as streamed FP4 GEMVs in one launch each, FC1
+ *           over chunks of up to C = min(16, 64 / k) tokens, each routed
+ *           expert's weights read once per chunk (b12x PR #22, What);
+ *           results are bit-reproducible.  Taken for M <= 6C with bf16
+ *           activations, M <= C with MXFP8 activations, and for every M when
+ *           E > 8192.
  *   grouped (any other M): routes grouped by expert in route order, FC1 and
  *           FC2 as grouped GEMMs on the matrix cores over bf16 operands (FP4
  *           dequantised exactly) with fp32 accumulation, per-route fp32 rows
@@ -236,8 +236,7 @@ typedef struct {
  * same stream); 3 queues both.  On the grouped path, 4 queues only its
  * routing (the grouping of the routes by expert) and 8 only its combine
  * (which reads what a phase-2 call left), so the two GEMM launches can be
- * timed on their own; the decode path rejects 4 and 8, and 1 and 2 when M
- * takes more than one chunk. */
+ * timed on their own; the decode path rejects 4 and 8. */
 moe_fp4_status moe_fp4_forward_ex(const moe_fp4_desc* desc, const void* prepared,
                                   const uint16_t* x, int32_t M, const int32_t* topk_ids,
                                   const float* topk_w, uint16_t* out, void* workspace,

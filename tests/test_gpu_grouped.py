@@ -95,7 +95,7 @@ def test_grouped_token_outputs_do_not_depend_on_the_batch():
 def test_grouped_invalid_ids_with_nan_poisoned_expert_zero():
     for fmt, poison in (("mxfp4", 0xFF), ("nvfp4", 0x7F)):
         rng = np.random.default_rng(32)
-        M = 80  # past the decode path's automatic range (4 chunks of 16 tokens)
+        M = 112  # past the decode path's automatic range (6 chunks of 16 tokens)
         d, _, _ = random_case(rng, fmt, 6, 512, 64, M, 4)
         d["ids"][:] = rng.integers(1, 6, size=(M, 4))
         d["w13_scales"][0] = poison
@@ -114,17 +114,17 @@ def test_grouped_invalid_ids_with_nan_poisoned_expert_zero():
 
 def test_grouped_all_invalid_and_poisoned_workspace():
     rng = np.random.default_rng(33)
-    d, _, _ = random_case(rng, "nvfp4", 4, 256, 64, 70, 2)   # 70 tokens: the grouped path
+    d, _, _ = random_case(rng, "nvfp4", 4, 256, 64, 100, 2)   # 100 tokens: the grouped path
     d["ids"][:10] = np.array([-1, 4], np.int32)       # tokens 0..9: no valid route
-    layer = make_layer("nvfp4", d, 2, 70)
-    assert moe.plan(layer.desc, 70).path == moe.PATH_GROUPED
+    layer = make_layer("nvfp4", d, 2, 100)
+    assert moe.plan(layer.desc, 100).path == moe.PATH_GROUPED
     acc, _ = oracle.forward_f32("nvfp4", d)
     x = to_dev(d["x"]).view(torch.bfloat16)
     ids, w = to_dev(d["ids"]), to_dev(d["w"])
     outs = []
     for rep in range(2):
         layer.workspace.fill_(0xFF)
-        out = torch.full((70, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+        out = torch.full((100, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
         layer(x, ids, w, out=out)
         torch.cuda.synchronize()
         outs.append(out.view(torch.int16).cpu().numpy().view(np.uint16))
@@ -133,7 +133,7 @@ def test_grouped_all_invalid_and_poisoned_workspace():
     assert np.array_equal(outs[0], outs[1])
     # every route invalid
     d["ids"][:] = -1
-    out = torch.full((70, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
+    out = torch.full((100, 256), float("nan"), dtype=torch.bfloat16, device="cuda")
     layer(x, to_dev(d["ids"]), w, out=out)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), torch.zeros_like(out.view(torch.int16)))
@@ -216,18 +216,18 @@ def test_prefill_workload_full_size_sampled():
 @pytest.mark.parametrize("fmt,k", [("mxfp4", 4), ("nvfp4", 8)])
 def test_band_edge_both_paths(fmt, k):
     """Around the edges of one decode launch pair (M = min(16, 64/k)) and of
-    the decode path's automatic range (4 such chunks), the automatic path,
+    the decode path's automatic range (6 such chunks), the automatic path,
     the forced decode path (in chunks past one) and the forced grouped path
     all match the oracle."""
     edge = min(16, 64 // k)
-    for M in (edge, edge + 1, 4 * edge, 4 * edge + 1):
+    for M in (edge, edge + 1, 6 * edge, 6 * edge + 1):
         rng = np.random.default_rng(40 + M)
         d, _, _ = random_case(rng, fmt, 16, 512, 128, M, k)
         d["ids"][0, 0] = -1
         d["ids"][-1, -1] = 99
         acc, _ = oracle.forward_f32(fmt, d)
         layer = make_layer(fmt, d, k, M)
-        want = moe.PATH_DECODE if M <= 4 * edge else moe.PATH_GROUPED
+        want = moe.PATH_DECODE if M <= 6 * edge else moe.PATH_GROUPED
         assert moe.plan(layer.desc, M).path == want
         compare(run_layer(layer, d), acc, f"{fmt} k{k} M{M} auto")
         compare(run_layer(layer, d, tuning=GROUPED), acc, f"{fmt} k{k} M{M} grouped")
