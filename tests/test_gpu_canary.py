@@ -36,7 +36,8 @@ def _bands_intact(big, nbytes, fill):
 
 
 @pytest.mark.parametrize("fmt,act,M", [("mxfp4", "bf16", 2), ("nvfp4", "bf16", 3), ("mxfp4", "bf16", 300),
-                                       ("nvfp4", "bf16", 130), ("mxfp4", "mxfp8", 300), ("mxfp4", "mxfp8", 37)])
+                                       ("nvfp4", "bf16", 130), ("mxfp4", "mxfp8", 300), ("mxfp4", "mxfp8", 37),
+                                       ("nvfp4", "bf16", 40), ("mxfp4", "bf16", 96)])
 def test_layer_writes_stay_inside_out_and_workspace(fmt, act, M):
     rng = np.random.default_rng(70 + M)
     E, H, I, k = 12, 288, 96, 4
@@ -49,7 +50,9 @@ def test_layer_writes_stay_inside_out_and_workspace(fmt, act, M):
     out = ob.view(torch.bfloat16).view(M, H)
     x = to_dev(d["x"]).view(torch.bfloat16)
     ids, w = to_dev(d["ids"]), to_dev(d["w"])
-    for tuning in (None, moe.Tuning(0, 0, 0, moe.PATH_GROUPED)):
+    # the automatic path, then the grouped and the decode path forced (the
+    # decode path in chunks of 16 tokens past M = 16)
+    for tuning in (None, moe.Tuning(0, 0, 0, moe.PATH_GROUPED), moe.Tuning(0, 0, 0, moe.PATH_DECODE)):
         moe.forward(layer.desc, layer.prepared, x, ids, w, out, ws, tuning=tuning)
         assert _bands_intact(wbig, ws_n, 0xA5), f"{fmt} {act} M{M}: write outside the workspace"
         assert _bands_intact(obig, M * H * 2, 0x5A), f"{fmt} {act} M{M}: write outside the output"
