@@ -48,8 +48,9 @@ def test_activation_decode_and_grouped(fmt, fn, alpha, beta, limit):
         layer = _layer(fmt, d, k, M)
         label = f"{fmt} {fn}({alpha},{beta},{limit}) M{M} k{k}"
         compare(run_layer(layer, d), acc, label + " auto")
-        if M <= 16:
-            compare(run_layer(layer, d, tuning=GROUPED), acc, label + " grouped")
+        compare(run_layer(layer, d, tuning=GROUPED), acc, label + " grouped")
+        # the decode path forced (M = 70: five chunks of 16 tokens)
+        compare(run_layer(layer, d, tuning=moe.Tuning(0, 0, 0, moe.PATH_DECODE)), acc, label + " decode")
 
 
 @pytest.mark.parametrize("fn,alpha,beta,limit", FNS)
