@@ -109,6 +109,9 @@ moe_fp4_status make_plan(const moe_fp4_desc* desc, const Layout& L, int32_t M,
     path = decode_ok && (chunks <= auto_chunks || L.E > moe::kRouteMaxExperts) ? MOE_FP4_PATH_DECODE
                                                                                : MOE_FP4_PATH_GROUPED;
   if (path == MOE_FP4_PATH_DECODE && !decode_ok) return MOE_FP4_EUNSUPPORTED;
+  // the decode launches put token chunks and groups (at most M of them) on
+  // the grid's second dimension, which holds at most 65535 workgroups
+  if (path == MOE_FP4_PATH_DECODE && M > 65535) return MOE_FP4_EUNSUPPORTED;
   if (path == MOE_FP4_PATH_GROUPED && L.E > moe::kRouteMaxExperts) return MOE_FP4_EUNSUPPORTED;
   if (path == MOE_FP4_PATH_DECODE) shape = moe::resolve_shape(L, (M < mc ? (M < 1 ? 1 : M) : mc) * k, shape);
   plan->path = path;

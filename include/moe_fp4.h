@@ -184,8 +184,9 @@ moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size
  *           FP8 x FP4 matrix instruction (the W4A8-MX variant above).
  *           Results are bit-reproducible.
  * The activation function (act_fn) is the same on both paths.
- * Returns MOE_FP4_EUNSUPPORTED when max_tokens * k > 2^22, or when k > 64
- * and the grouped path cannot run (E > 8192). */
+ * Returns MOE_FP4_EUNSUPPORTED when max_tokens * k > 2^22, or when the path
+ * the call needs cannot run it: the grouped path with E > 8192, the decode
+ * path with k > 64 or M > 65535. */
 moe_fp4_status moe_fp4_forward(const moe_fp4_desc* desc, const void* prepared,
                                const uint16_t* x, int32_t M, const int32_t* topk_ids,
                                const float* topk_w, uint16_t* out, void* workspace,
@@ -208,7 +209,7 @@ moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prep
 /* Execution path selector for moe_fp4_forward_ex. */
 typedef enum {
   MOE_FP4_PATH_AUTO = 0,    /* by M, as moe_fp4_forward */
-  MOE_FP4_PATH_DECODE = 1,  /* decode path at any M (in chunks); MOE_FP4_EUNSUPPORTED when k > 64 */
+  MOE_FP4_PATH_DECODE = 1,  /* decode path (in chunks); MOE_FP4_EUNSUPPORTED when k > 64 or M > 65535 */
   MOE_FP4_PATH_GROUPED = 2  /* grouped path at any M */
 } moe_fp4_path;
 

@@ -141,6 +141,13 @@ def test_decode_path_past_one_launch_pair(L):
     assert ei.value.status == 2
     many = moe.Desc("mxfp4", 8, 256, 128, 1, 32)          # 16 tokens per chunk
     assert _plan(many, 17, t)[0] == moe.PATH_DECODE
+    # the decode launches' second grid dimension holds at most 65535 chunks or groups
+    huge_m = moe.Desc("mxfp4", 9000, 64, 32, 1, 70000)
+    assert _plan(huge_m, 65535)[0] == moe.PATH_DECODE
+    for bad in (None, t):
+        with pytest.raises(moe.MoeFp4Error) as ei:
+            moe.plan(huge_m, 65536, bad)
+        assert ei.value.status == 2
 
 
 def test_workspace_sizes_do_not_depend_on_m(L):
