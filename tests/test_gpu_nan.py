@@ -38,7 +38,7 @@ def test_nan_propagates(fmt, nan_scale, M):
     want_nan = np.isnan(acc)
     assert want_nan[1].all() and want_nan[M - 1, 5] and want_nan.sum() == H + 1 - (M - 1 == 1)
     layer = make_layer(fmt, d, k, M)
-    for label, tuning in (("auto", None), ("grouped", GROUPED)):
+    for label, tuning in (("auto", None), ("grouped", GROUPED), ("decode", moe.Tuning(0, 0, 0, moe.PATH_DECODE))):
         got = run_layer(layer, d, tuning=tuning)
         g = oracle.bf16_bits_to_f32(got)
         assert np.array_equal(np.isnan(g), want_nan), f"{fmt} M{M} {label}: NaN positions"
