@@ -123,7 +123,18 @@ moe_fp4_status make_plan(const moe_fp4_desc* desc, const Layout& L, int32_t M,
   // the grid's second dimension, which holds at most 65535 workgroups
   if (path == MOE_FP4_PATH_DECODE && M > 65535) return MOE_FP4_EUNSUPPORTED;
   if (path == MOE_FP4_PATH_GROUPED && L.E > moe::kRouteMaxExperts) return MOE_FP4_EUNSUPPORTED;
-  if (path == MOE_FP4_PATH_DECODE) shape = moe::resolve_shape(L, (M < mc ? (M < 1 ? 1 : M) : mc) * k, shape);
+  if (path == MOE_FP4_PATH_DECODE) {
+    const int mc_call = M < mc ? (M < 1 ? 1 : M) : mc;
+    shape = moe::resolve_shape(L, mc_call * k, shape);
+    // FC1 stages a token's H activations in LDS: past what a workgroup may
+    // allocate, the decode path cannot run this layer
+    if (moe::fc1_lds_bytes(L, mc_call, shape.r1) > moe::kMaxLdsBytes) {
+      const bool auto_path = !tuning || tuning->path == MOE_FP4_PATH_AUTO;
+      if (!auto_path || L.E > moe::kRouteMaxExperts) return MOE_FP4_EUNSUPPORTED;
+      path = MOE_FP4_PATH_GROUPED;
+      shape = moe::DecodeShape{0, 0, 0};
+    }
+  }
   plan->path = path;
   plan->shape = shape;
   return MOE_FP4_OK;

@@ -83,6 +83,12 @@ inline DecodeShape resolve_shape(const Layout& L, int slots, DecodeShape s) {
   return s;
 }
 
+// Dynamic LDS of an FC1 workgroup: the token's H activations (bf16) and the
+// per-wave partial sums of mc tokens x 16 waves x r1 rows (fp32).
+inline int64_t fc1_lds_bytes(const Layout& L, int mc, int r1) {
+  return 2 * align_up(L.H, 64) + (int64_t)mc * kMaxWaves * r1 * 4;
+}
+
 template <typename IdT>
 hipError_t launch_decode(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k,
                          const IdT* ids, const float* tw, uint16_t* out, uint8_t* ws,

@@ -6,16 +6,20 @@
 // epilogue into the bf16 output, and no grid barrier (its Notes section records
 // the grid-barrier variant deadlocking).
 //
-// On gfx950 the lanes of a wave own rows instead of K-slices: every lane reads
-// the same 32-element K chunk of its own row, so the activation chunk is
-// wave-uniform and arrives through scalar loads into SGPRs, each wave load of
-// codes is one contiguous KiB of the resident layout, and no cross-lane
-// reduction is needed.  All cross-wave sums stay inside a workgroup, in LDS
-// and in a fixed order: no workgroup ever waits for or signals another one,
-// and results are bit-reproducible.
-//   FC1: one workgroup per (route slot, 64-row tile); its waves split K into
-//        slabs; the slab sums meet in LDS, then SiLU(gate)*up is written to
-//        the workspace activation.
+// On gfx950 a wave's 64 lanes are split as lane = (g, p) = (lane / KL,
+// lane % KL): lane p of a group owns 32-element K chunk p of the wave's KL
+// chunks, for the rows g + RG*j (RG = 64 / KL row groups, j < T rows per
+// lane).  One load instruction then covers KL chunks x 8 consecutive rows of
+// the resident layout, whole 128-byte lines, and a lane's activation chunk
+// (32 bf16, from LDS where it is staged, else from global memory) is read
+// once and reused for its T rows.  The KL partial sums of a row are reduced
+// across lanes by a transposing DPP fold inside 16-lane rows (fold_rows),
+// which leaves one row sum per lane.  All cross-wave sums stay inside a
+// workgroup, in LDS and in a fixed order: no workgroup ever waits for or
+// signals another one, and results are bit-reproducible.
+//   FC1: one workgroup per (route slot, 64-row tile, block of R rows); its
+//        waves split K into slabs; the slab sums meet in LDS, then
+//        SiLU(gate)*up is written to the workspace activation.
 //   FC2: one workgroup per (block of rows of H, group of whole tokens with
 //        at most one route slot per wave); its waves split the group's route
 //        slots (experts); the weighted expert sums meet in LDS and are
@@ -450,7 +454,7 @@ hipError_t launch_fc1(const Layout& L, const uint8_t* prep, const uint16_t* x, i
   const int groups = (L.nC1 + KL - 1) / KL;
   const int waves = groups < kMaxWaves ? groups : kMaxWaves;
   const bool big = R == 32;
-  const size_t lds = 2 * (size_t)align_up(L.H, 64) + (size_t)mc * 16 * R * sizeof(float);
+  const size_t lds = (size_t)fc1_lds_bytes(L, mc, R);
   const dim3 grid((unsigned)((int64_t)slots * L.nB1 * (64 / R)), (unsigned)((M + mc - 1) / mc)),
       block(64 * waves);
   if (big)

@@ -124,12 +124,15 @@ typedef struct {
   float act_limit;
 } moe_fp4_desc;
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string).  A diagnostic hook
+ * of this library's own; no page defines one. */
 const char* moe_fp4_status_string(moe_fp4_status s);
 
 /* Bytes of the prepared (resident) weight buffer for `desc`.  It holds the
  * same codes, scale bytes and fp32 globals as the logical tensors, reordered,
- * plus zero padding to whole tiles. */
+ * plus zero padding to whole tiles (b12x PR #459, "Reduce NVFP4-CSF scale
+ * reconstruction overhead", commit messages: preparation keeps checkpoint
+ * bytes and prepared memory sizes). */
 moe_fp4_status moe_fp4_prepared_bytes(const moe_fp4_desc* desc, size_t* bytes);
 
 /* Weight preparation, once per layer at load time (b12x PR #459, "Reduce
@@ -152,7 +155,10 @@ moe_fp4_status moe_fp4_unprepare(const moe_fp4_desc* desc, const void* prepared,
 
 /* Workspace bytes for forward calls on `desc` (device scratch, 256-byte
  * aligned, caller-owned).  The size depends only on the descriptor, so one
- * workspace serves every M <= max_tokens; `M` is checked against max_tokens.
+ * workspace serves every M <= max_tokens; `M` is checked against max_tokens
+ * (b12x PR #311, review comment on the intermediate_cache13 sizing: a
+ * workspace must hold the largest requirement over every token count the
+ * caller plans, or a smaller launch under-allocates).
  * The grouped path needs about 4I + 4H bytes per route (max_tokens * k
  * routes) with bf16 activations, and about I + 4H per route plus H per
  * token with MXFP8 activations.  Its contents on entry do not matter and
@@ -192,16 +198,23 @@ moe_fp4_status moe_fp4_forward(const moe_fp4_desc* desc, const void* prepared,
                                const float* topk_w, uint16_t* out, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* Same, with int64 route ids (any int64 value outside [0, E) is invalid). */
+/* Same, with int64 route ids (any int64 value outside [0, E) is invalid).
+ * Both id widths are served (b12x PR #459, "Reduce NVFP4-CSF scale
+ * reconstruction overhead", commit messages: programs kept for both routing
+ * integer types). */
 moe_fp4_status moe_fp4_forward_i64(const moe_fp4_desc* desc, const void* prepared,
                                    const uint16_t* x, int32_t M, const int64_t* topk_ids,
                                    const float* topk_w, uint16_t* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
-/* Test hook: dequantise one expert matrix from the prepared buffer with the
- * same decode instructions the forward kernels use, into fp32 row-major
- * `out` ([2I][H] for which = 0 (W13), [H][I] for which = 1 (W2)).  Each value
- * is (E2M1 code * block scale) rounded to fp32, times the global (NVFP4). */
+/* Test hook of this library's own: dequantise one expert matrix from the
+ * prepared buffer with the same decode instructions the forward kernels use,
+ * into fp32 row-major `out` ([2I][H] for which = 0 (W13), [H][I] for
+ * which = 1 (W2); device, 4-byte aligned, caller-owned).  Each value is
+ * (E2M1 code * block scale) rounded to fp32, times the global (NVFP4), so
+ * the tests can compare every prepared byte with the oracle's dequantisation
+ * bit for bit (b12x PR #459, PR body: every arm is checked against an exact
+ * byte oracle). */
 moe_fp4_status moe_fp4_dequant_export(const moe_fp4_desc* desc, const void* prepared,
                                       int32_t expert, int32_t which, float* out,
                                       void* stream);

@@ -2,6 +2,7 @@
 through the C-ABI, and compare with the CPU oracle."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
@@ -69,22 +70,35 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return oracle.bf16_bits_to_f32(bits).astype(np.float64)
 
 
-def compare(gpu_bits: np.ndarray, acc: np.ndarray, label: str = "", maxabs: float = MAXABS_REL_RMS) -> dict:
+# Every compare() call of the session, for the summary table the suite prints
+# at its end (tests/conftest.py).
+RECORDS: list[dict] = []
+
+
+def compare(gpu_bits: np.ndarray, acc: np.ndarray, label: str = "", bar: float = MAXABS_REL_RMS) -> dict:
+    """Checks a bf16 layer output against the oracle's fp32 sums: cosine >=
+    COS_MIN and max |gpu - oracle| beyond half a bf16 ulp of the oracle value
+    <= bar * RMS(oracle), both in fp64 over every value."""
     g = bf16_to_f64(gpu_bits).ravel()
     r = acc.astype(np.float64).ravel()
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
     if rms == 0.0:
         assert np.array_equal(gpu_bits, np.zeros_like(gpu_bits)), f"{label}: expected +0 everywhere"
-        return dict(cos=1.0, maxabs_rel=0.0)
+        rec = dict(test=test, label=label, n=int(r.size), cos=1.0, maxabs_rel=0.0, excess_rel=0.0, bar=bar)
+        RECORDS.append(rec)
+        return rec
     assert np.isfinite(g).all(), f"{label}: non-finite GPU output"
     cos = float(g @ r / (np.linalg.norm(g) * np.linalg.norm(r)))
     err = np.abs(g - r)
-    maxabs = float(err.max()) / rms
-    excess = float(np.max(err - bf16_half_ulp(r))) / rms
-    say(f"  {label}: cos={cos:.8f} maxabs/rms={maxabs:.3e} beyond-rounding/rms={excess:.3e}")
-    assert cos >= COS_MIN, f"{label}: cosine {cos}"
-    assert excess <= maxabs, f"{label}: max-abs/RMS beyond bf16 rounding {excess}"
-    return dict(cos=cos, maxabs_rel=maxabs, excess_rel=excess)
+    maxabs_rel = float(err.max()) / rms
+    excess_rel = float(np.max(err - bf16_half_ulp(r))) / rms
+    say(f"  {label}: cos={cos:.8f} maxabs/rms={maxabs_rel:.3e} beyond-rounding/rms={excess_rel:.3e} (bar {bar})")
+    rec = dict(test=test, label=label, n=int(r.size), cos=cos, maxabs_rel=maxabs_rel, excess_rel=excess_rel, bar=bar)
+    RECORDS.append(rec)
+    assert cos >= COS_MIN, f"{label}: cosine {cos} < {COS_MIN}"
+    assert excess_rel <= bar, f"{label}: max-abs/RMS beyond bf16 rounding {excess_rel} > {bar}"
+    return rec
 
 
 def workload_inputs(name: str, seed=None) -> tuple[synth.Workload, dict]:

@@ -272,3 +272,16 @@ def test_plan_resolves_path_and_shape(L):
     assert ei.value.status == 2  # k = 65: more route slots than one wave holds
     with pytest.raises(moe.MoeFp4Error):
         moe.plan(e512, 2)  # M past max_tokens
+
+
+def test_plan_rejects_decode_past_the_lds_limit(L):
+    """FC1 of the decode path stages a token's H activations in LDS; a layer
+    whose staging exceeds what a workgroup may allocate takes the grouped
+    path by default and is rejected on the decode path before any launch."""
+    wide = moe.Desc("mxfp4", 8, 131072, 32, 2, 1)
+    assert _plan(wide, 1)[0] == moe.PATH_GROUPED
+    with pytest.raises(moe.MoeFp4Error) as ei:
+        moe.plan(wide, 1, moe.Tuning(0, 0, 0, moe.PATH_DECODE))
+    assert ei.value.status == 2
+    # the widest H whose staging still fits keeps the decode path
+    assert _plan(moe.Desc("mxfp4", 8, 16384, 32, 2, 1), 1)[0] == moe.PATH_DECODE

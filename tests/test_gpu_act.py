@@ -57,7 +57,7 @@ def test_activation_decode_and_grouped(fmt, fn, alpha, beta, limit):
 def test_activation_w4a8(fn, alpha, beta, limit):
     d = _case(400 + len(fn), "mxfp4", 10, 448, 224, 150, 4, fn, alpha, beta, limit)
     layer = _layer("mxfp4", d, 4, 150, act="mxfp8")
-    compare(run_layer(layer, d), oracle.forward_w4a8("mxfp4", d), f"w4a8 {fn}", maxabs=W4A8_MAXABS_REL_RMS)
+    compare(run_layer(layer, d), oracle.forward_w4a8("mxfp4", d), f"w4a8 {fn}", bar=W4A8_MAXABS_REL_RMS)
 
 
 def _relu2_case(seed, fmt, E, H, I, M, k):
@@ -98,7 +98,7 @@ def test_relu2_w4a8_and_prepare_round_trip():
     import torch
     d = _relu2_case(600, "mxfp4", 10, 448, 256, 150, 4)
     layer = _relu2_layer("mxfp4", d, 4, 150, act="mxfp8")
-    compare(run_layer(layer, d), oracle.forward_w4a8("mxfp4", d), "w4a8 relu2", maxabs=W4A8_MAXABS_REL_RMS)
+    compare(run_layer(layer, d), oracle.forward_w4a8("mxfp4", d), "w4a8 relu2", bar=W4A8_MAXABS_REL_RMS)
     # the prepared buffer holds exactly the I-row W13 and comes back unchanged
     from gpu_util import to_dev
     src = [to_dev(d[kk]) for kk in ("w13_codes", "w13_scales", "w2_codes", "w2_scales")]
@@ -138,4 +138,4 @@ def test_activations_at_full_sizes_sampled():
             compare(got, oracle.forward_f32(wl.fmt, sub)[0], "H7168/I256 M96 swigluoai, grouped bf16")
         else:
             compare(got, oracle.forward_w4a8(wl.fmt, sub), "H7168/I256 M96 swigluoai, grouped mxfp8",
-                    maxabs=W4A8_MAXABS_REL_RMS)
+                    bar=W4A8_MAXABS_REL_RMS)

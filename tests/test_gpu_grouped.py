@@ -271,7 +271,7 @@ def test_grouped_at_the_route_limit(act):
         compare(got[sample], oracle.forward_f32("mxfp4", sub)[0], "2^22 routes, bf16")
     else:
         from gpu_util import W4A8_MAXABS_REL_RMS
-        compare(got[sample], oracle.forward_w4a8("mxfp4", sub), "2^22 routes, mxfp8", maxabs=W4A8_MAXABS_REL_RMS)
+        compare(got[sample], oracle.forward_w4a8("mxfp4", sub), "2^22 routes, mxfp8", bar=W4A8_MAXABS_REL_RMS)
 
 
 def test_grouped_with_8192_experts():

@@ -71,7 +71,7 @@ def test_sizes_eager_and_graph_with_poison(act):
         got = eager.cpu().numpy().view(np.uint16)[sample]
         grouped = M > min(16, 64 // k)
         if act == "mxfp8" and grouped:
-            compare(got, oracle.forward_w4a8("mxfp4", sub), f"{act} M{M}", maxabs=W4A8_MAXABS_REL_RMS)
+            compare(got, oracle.forward_w4a8("mxfp4", sub), f"{act} M{M}", bar=W4A8_MAXABS_REL_RMS)
         else:
             compare(got, oracle.forward_f32("mxfp4", sub)[0], f"{act} M{M}")
         del g

@@ -23,7 +23,7 @@ GROUPED = moe.Tuning(0, 0, 0, moe.PATH_GROUPED)
 
 
 def compare(gpu_bits, acc, label=""):
-    return _compare(gpu_bits, acc, label, maxabs=W4A8_MAXABS_REL_RMS)
+    return _compare(gpu_bits, acc, label, bar=W4A8_MAXABS_REL_RMS)
 
 
 @pytest.fixture(autouse=True)
