@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "../../include/moe_fp4.h"
 #include "decode_path.h"
@@ -140,11 +141,12 @@ moe_fp4_status make_plan(const moe_fp4_desc* desc, const Layout& L, int32_t M,
   return MOE_FP4_OK;
 }
 
+// With check_only, every check runs and nothing is launched.
 template <typename IdT>
 moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, const uint16_t* x,
                             int32_t M, const IdT* ids, const float* w, uint16_t* out,
                             void* workspace, size_t ws_bytes, const moe_fp4_tuning* tuning,
-                            int32_t phases, void* stream) {
+                            int32_t phases, void* stream, bool check_only = false) {
   Layout L;
   moe_fp4_status st = desc_layout(desc, &L);
   if (st != MOE_FP4_OK) return st;
@@ -161,6 +163,7 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
   const int k = desc->top_k;
   if (plan.path != MOE_FP4_PATH_GROUPED && phases > 3) return MOE_FP4_EINVAL;
   if ((int64_t)ws_bytes < workspace_total(L, desc)) return MOE_FP4_EWORKSPACE;
+  if (check_only) return MOE_FP4_OK;
   if (plan.path == MOE_FP4_PATH_GROUPED)
     return from_hip(moe::launch_prefill<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
                                              (uint8_t*)workspace, prefill_layout(L, desc), phases,
@@ -170,6 +173,33 @@ moe_fp4_status forward_impl(const moe_fp4_desc* desc, const void* prepared, cons
   const moe::DecodeWs W = moe::decode_ws(L, decode_slots(desc));
   return from_hip(moe::launch_decode<IdT>(L, (const uint8_t*)prepared, x, M, k, ids, w, out,
                                           (uint8_t*)workspace, W, plan.shape, phases, (hipStream_t)stream));
+}
+
+// The workspace of moe_fp4_forward_noalloc: device memory the library holds
+// for callers that cannot allocate, one copy per GPU the library runs on
+// (it lives until the process ends).  Host code never passes the array's
+// name to a kernel: it stands for a host-side stand-in, not the device
+// address, which scratch_address() looks up once per device.
+constexpr int64_t kNoAllocScratchBytes = (int64_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with that device current).
+moe_fp4_status scratch_address(void** addr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_FP4_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_FP4_EHIP;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return MOE_FP4_OK;
 }
 
 }  // namespace
@@ -252,6 +282,27 @@ moe_fp4_status moe_fp4_forward_i64(const moe_fp4_desc* desc, const void* prepare
                                    size_t workspace_bytes, void* stream) {
   return forward_impl<int64_t>(desc, prepared, x, M, topk_ids, topk_w, out, workspace,
                                workspace_bytes, nullptr, 3, stream);
+}
+
+moe_fp4_status moe_fp4_forward_noalloc(const moe_fp4_desc* desc, const void* prepared,
+                                       const uint16_t* x, int32_t M, const int32_t* topk_ids,
+                                       const float* topk_w, uint16_t* out, void* stream) {
+  Layout L;
+  moe_fp4_status st = desc_layout(desc, &L);
+  if (st != MOE_FP4_OK) return st;
+  if (prefill_routes(desc) > moe::kPrefillMaxRoutes) return MOE_FP4_EUNSUPPORTED;
+  const int64_t need = workspace_total(L, desc);
+  if (need > kNoAllocScratchBytes) return MOE_FP4_EWORKSPACE;
+  // every check of moe_fp4_forward, before any HIP call (an aligned stand-in
+  // for the workspace pointer; nothing is launched)
+  st = forward_impl<int32_t>(desc, prepared, x, M, topk_ids, topk_w, out, (void*)(uintptr_t)256,
+                             (size_t)need, nullptr, 3, stream, true);
+  if (st != MOE_FP4_OK || M == 0) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MOE_FP4_OK) return st;
+  return forward_impl<int32_t>(desc, prepared, x, M, topk_ids, topk_w, out, ws, (size_t)need, nullptr, 3,
+                               stream);
 }
 
 moe_fp4_status moe_fp4_forward_ex(const moe_fp4_desc* desc, const void* prepared,

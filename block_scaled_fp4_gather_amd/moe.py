@@ -92,6 +92,7 @@ _SIGS = {
     "moe_fp4_workspace_bytes": ([ctypes.POINTER(_Desc), _I32, ctypes.POINTER(_SZ)], ctypes.c_int),
     "moe_fp4_forward": ([ctypes.POINTER(_Desc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
     "moe_fp4_forward_i64": ([ctypes.POINTER(_Desc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ, _VP], ctypes.c_int),
+    "moe_fp4_forward_noalloc": ([ctypes.POINTER(_Desc), _VP, _VP, _I32, _VP, _VP, _VP, _VP], ctypes.c_int),
     "moe_fp4_forward_ex": ([ctypes.POINTER(_Desc), _VP, _VP, _I32, _VP, _VP, _VP, _VP, _SZ,
                             ctypes.POINTER(Tuning), _I32, _VP], ctypes.c_int),
     "moe_fp4_plan": ([ctypes.POINTER(_Desc), _I32, ctypes.POINTER(Tuning), ctypes.POINTER(Tuning)], ctypes.c_int),
@@ -180,6 +181,15 @@ def forward(desc: Desc, prepared, x, ids, w, out, workspace, stream=None, tuning
     else:
         assert ids.dtype == torch.int32
         _check("moe_fp4_forward", lib().moe_fp4_forward(*args, _stream(stream)))
+
+
+def forward_noalloc(desc: Desc, prepared, x, ids, w, out, stream=None):
+    """moe_fp4_forward with the library's own 64 MiB workspace (int32 ids):
+    the entry point for callers that cannot allocate."""
+    assert ids.dtype == torch.int32
+    _check("moe_fp4_forward_noalloc", lib().moe_fp4_forward_noalloc(
+        ctypes.byref(desc.c()), _ptr(prepared), _ptr(x), x.shape[0], _ptr(ids), _ptr(w), _ptr(out),
+        _stream(stream)))
 
 
 def plan(desc: Desc, M: int, tuning: Tuning | None = None) -> Tuning:

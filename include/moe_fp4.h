@@ -29,8 +29,9 @@
  *
  * Conventions for every entry point:
  *   - Device pointers are caller-owned device memory; the library allocates
- *     nothing, keeps no global state and never synchronises.  Work is queued
- *     on `stream` (a hipStream_t; NULL is the default stream).
+ *     nothing, keeps no global state (except moe_fp4_forward_noalloc's
+ *     workspace, below) and never synchronises.  Work is queued on `stream`
+ *     (a hipStream_t; NULL is the default stream).
  *   - Inputs are never written.  Arguments are checked before any launch; a
  *     rejected call launches nothing.  A failed launch returns MOE_FP4_EHIP.
  *   - Data conditions are not errors: invalid ids contribute zero; NaN or Inf
@@ -206,6 +207,22 @@ moe_fp4_status moe_fp4_forward_i64(const moe_fp4_desc* desc, const void* prepare
                                    const uint16_t* x, int32_t M, const int64_t* topk_ids,
                                    const float* topk_w, uint16_t* out, void* workspace,
                                    size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): moe_fp4_forward
+ * (int32 ids) without a workspace argument.  The workspace is a block of
+ * 64 MiB of device memory that the library itself holds, one per GPU it
+ * runs on, from the first call on that GPU until the process ends; the call
+ * allocates nothing.  `desc` must need at most that much workspace
+ * (moe_fp4_workspace_bytes <= 64 MiB), else MOE_FP4_EWORKSPACE; other
+ * arguments, checks and results are those of moe_fp4_forward.  The stream
+ * must belong to the current device.  All calls on one GPU share that
+ * GPU's block: calls that overlap on one GPU (other streams, other host
+ * threads without ordering) race on it and give wrong results; calls
+ * ordered on one stream are safe.  Its contents on entry do not matter. */
+moe_fp4_status moe_fp4_forward_noalloc(const moe_fp4_desc* desc, const void* prepared,
+                                       const uint16_t* x, int32_t M, const int32_t* topk_ids,
+                                       const float* topk_w, uint16_t* out, void* stream);
 
 /* Test hook of this library's own: dequantise one expert matrix from the
  * prepared buffer with the same decode instructions the forward kernels use,

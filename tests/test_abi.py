@@ -285,3 +285,21 @@ def test_plan_rejects_decode_past_the_lds_limit(L):
     assert ei.value.status == 2
     # the widest H whose staging still fits keeps the decode path
     assert _plan(moe.Desc("mxfp4", 8, 16384, 32, 2, 1), 1)[0] == moe.PATH_DECODE
+
+
+def test_noalloc_forward_rejects_before_any_hip_call(L):
+    """moe_fp4_forward_noalloc checks its arguments and the workspace the
+    descriptor needs (at most the library's 64 MiB) before any HIP call."""
+    fn = L.moe_fp4_forward_noalloc
+    small = moe.Desc("mxfp4", 8, 256, 128, 2, 4)
+    assert moe.workspace_bytes(small, 4) <= 64 << 20
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: every call below is rejected or has M = 0
+    args = lambda d, M, p=fake: (ctypes.byref(d.c()), p, p, M, p, p, p, None)
+    assert fn(*args(small, 0)) == 0             # M = 0: nothing to do
+    assert fn(*args(small, 1, nul)) == 1        # null pointers
+    assert fn(*args(small, 5)) == 1             # M past max_tokens
+    big = moe.Desc("mxfp4", 128, 4096, 1536, 8, 4096)  # the prefill layer needs ~700 MiB of workspace
+    assert moe.workspace_bytes(big, 1) > 64 << 20
+    assert fn(*args(big, 1)) == 3               # MOE_FP4_EWORKSPACE
+    assert fn(*args(moe.Desc("mxfp4", 8, 250, 128, 2, 4), 1)) == 1  # H not whole scale blocks
