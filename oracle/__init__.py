@@ -77,6 +77,10 @@ def lib():
         L.oracle_activation.argtypes = [i] + [ctypes.c_double] * 5
         L.oracle_activation.restype = ctypes.c_double
         L.oracle_forward_w4a8.restype = i
+        L.oracle_csf_encode.argtypes = [i, u8p, i, u8p, u8p]
+        L.oracle_csf_encode.restype = i
+        L.oracle_csf_decode.argtypes = [i, ctypes.c_uint8, u8p, u8p, i, u8p]
+        L.oracle_csf_decode.restype = i
         _lib = L
     return _lib
 
@@ -203,3 +207,29 @@ def forward_w4a8(fmt: str, d: dict, quant_act: bool = True) -> np.ndarray:
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to fp32 (a bit shift, no rounding)."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def csf_encode(fmt: str, scales: np.ndarray) -> tuple[int, np.ndarray, bool]:
+    """Compressed-scale encoding of one row of scale bytes: (base byte,
+    offsets one per block, compressed?); an exception row has base 255."""
+    sc = np.ascontiguousarray(scales, dtype=np.uint8)
+    base = np.zeros(1, dtype=np.uint8)
+    off = np.zeros(sc.size, dtype=np.uint8)
+    rc = lib().oracle_csf_encode(FMT[fmt], _p(sc, ctypes.c_uint8), sc.size, _p(base, ctypes.c_uint8),
+                                 _p(off, ctypes.c_uint8))
+    if rc < 0:
+        raise ValueError("oracle_csf_encode rejected its arguments")
+    return int(base[0]), off, bool(rc)
+
+
+def csf_decode(fmt: str, base: int, offsets: np.ndarray, plain: np.ndarray) -> np.ndarray:
+    """A row's scale bytes from its base and offsets (an exception row, base
+    255, from `plain`)."""
+    off = np.ascontiguousarray(offsets, dtype=np.uint8)
+    pl = np.ascontiguousarray(plain, dtype=np.uint8)
+    out = np.empty(off.size, dtype=np.uint8)
+    rc = lib().oracle_csf_decode(FMT[fmt], base, _p(off, ctypes.c_uint8), _p(pl, ctypes.c_uint8), off.size,
+                                 _p(out, ctypes.c_uint8))
+    if rc:
+        raise ValueError("oracle_csf_decode rejected its arguments")
+    return out

@@ -68,6 +68,19 @@
 //    survey's reading): W13 then has I rows, h_n = x . W13[n], and
 //    a_n = max(h_n, 0)^2, a NaN passing through.
 //
+// Compressed scales (b12x PR #459, "Reduce NVFP4-CSF scale reconstruction
+// overhead", commit messages: one-bit MXFP4 and four-bit NVFP4 offsets from a
+// row base byte; the scale reconstruction does an exception lookup).  The
+// pages give no more than that sentence; the reading here, lossless:
+//  * A weight row's scale bytes s[0..n) (one per block along K) are stored
+//    as a base byte b and one offset per block, s[j] = b + o[j] as an
+//    integer on the byte (UE8M0 exponents for MXFP4, E4M3 codes for NVFP4),
+//    with o[j] in [0, 1] (MXFP4, one bit) or [0, 15] (NVFP4, four bits).
+//  * b is the smallest byte of the row.  A row whose bytes span more than
+//    the offsets reach, or whose smallest byte is 255, is an exception: its
+//    base byte is 255 and its offsets 0, and the reader takes its bytes
+//    from the uncompressed scales instead.
+//
 // Build: g++ -O2 -ffp-contract=off -shared -fPIC (no fast-math, no FMA
 // contraction, so every product and sum is one IEEE fp32 rounding in the
 // order written).
@@ -241,9 +254,51 @@ bool valid_act(int kind) {
 // Rows of W13: 2I for the gated activations, I for relu2.
 int w13_rows(int act, int I) { return act == ACT_RELU2 ? I : 2 * I; }
 
+// Offset reach of a compressed scale row: 1 (one bit, MXFP4) or 15 (four
+// bits, NVFP4).
+uint32_t csf_reach(int fmt) { return fmt == FMT_MXFP4 ? 1u : 15u; }
+
 }  // namespace
 
 extern "C" {
+
+// Compressed-scale encoding of one row of n scale bytes: writes the base byte
+// and n offsets (one per block, unpacked) and returns 1, or marks the row an
+// exception (base 255, offsets 0) and returns 0.  Returns -1 on bad
+// arguments.
+int oracle_csf_encode(int fmt, const uint8_t* scales, int n, uint8_t* base, uint8_t* offsets) {
+  if ((fmt != FMT_MXFP4 && fmt != FMT_NVFP4) || n <= 0 || !scales || !base || !offsets) return -1;
+  uint32_t lo = 255u, hi = 0u;
+  for (int j = 0; j < n; ++j) {
+    if (scales[j] < lo) lo = scales[j];
+    if (scales[j] > hi) hi = scales[j];
+  }
+  if (lo == 255u || hi - lo > csf_reach(fmt)) {
+    *base = 255u;
+    for (int j = 0; j < n; ++j) offsets[j] = 0u;
+    return 0;
+  }
+  *base = (uint8_t)lo;
+  for (int j = 0; j < n; ++j) offsets[j] = (uint8_t)(scales[j] - lo);
+  return 1;
+}
+
+// The row's scale bytes back from its base and offsets; an exception row
+// (base 255) takes them from `plain` (its uncompressed bytes).
+int oracle_csf_decode(int fmt, uint8_t base, const uint8_t* offsets, const uint8_t* plain, int n,
+                      uint8_t* scales) {
+  if ((fmt != FMT_MXFP4 && fmt != FMT_NVFP4) || n <= 0 || !offsets || !plain || !scales) return -1;
+  for (int j = 0; j < n; ++j) {
+    if (base == 255u) {
+      scales[j] = plain[j];
+    } else {
+      if (offsets[j] > csf_reach(fmt)) return -1;
+      scales[j] = (uint8_t)(base + offsets[j]);
+    }
+  }
+  return 0;
+}
+
 
 float oracle_e2m1(uint32_t nibble) { return e2m1(nibble); }
 float oracle_ue8m0(uint32_t b) { return ue8m0(b); }
