@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--workload", default="mxfp4_shard_e256_m1")
     ap.add_argument("--act", default="bf16", choices=("bf16", "mxfp8"),
                     help="activation format of the grouped path (mxfp8: W4A8-MX, MXFP4 weights)")
+    ap.add_argument("--scales", default=None, choices=("plain", "csf"),
+                    help="resident scale format (default: the workload's; csf = compressed scales)")
     ap.add_argument("--rounds", type=int, default=7,
                     help="timed rounds per region, each after a cache scrub; the median is reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -83,17 +85,33 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def routed_bytes(wl, ids):
-    """Unique valid experts and their algorithmic weight bytes (codes + scales)."""
+def routed_bytes(wl, ids, d=None, csf=False):
+    """Unique valid experts and their algorithmic weight bytes: codes plus
+    scales.  With compressed scales (csf) a row's scales cost its CSF words
+    (4 bytes per 24 chunks of 32 elements for MXFP4, per 3 chunks for NVFP4:
+    the base byte and the offsets), and an exception row its plain scale
+    bytes too."""
     import numpy as np
     flat = ids.reshape(-1).astype(np.int64)
     uniq = np.unique(flat[(flat >= 0) & (flat < wl.E)])
     G = wl.G
-    w13 = 2 * wl.I * (wl.H // 2 + wl.H // G)
-    w2 = wl.H * (wl.I // 2 + wl.I // G)
     glob = 4 if wl.fmt == "nvfp4" else 0
     U = len(uniq)
-    return U, U * (w13 + glob), U * (w2 + glob)
+    if not csf:
+        w13 = 2 * wl.I * (wl.H // 2 + wl.H // G)
+        w2 = wl.H * (wl.I // 2 + wl.I // G)
+        return U, U * (w13 + glob), U * (w2 + glob)
+    reach = 1 if wl.fmt == "mxfp4" else 15
+    out = []
+    for key, K in (("w13_scales", wl.H), ("w2_scales", wl.I)):
+        sc = d[key][uniq].astype(np.int32)
+        rows = sc.shape[0] * sc.shape[1]
+        lo, hi = sc.min(axis=2), sc.max(axis=2)
+        exc = int(np.count_nonzero((lo == 255) | (hi - lo > reach)))
+        nC = K // 32
+        per_row = K // 2 + 4 * -(-nC // (24 if wl.fmt == "mxfp4" else 3))
+        out.append(rows * per_row + exc * (K // G) + U * glob)
+    return U, out[0], out[1]
 
 
 def cold_groups(wl, d, dev):
@@ -166,7 +184,8 @@ def main():
     d = synth.generate(wl)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    desc = moe.Desc(wl.fmt, wl.E, wl.H, wl.I, wl.k, max(wl.M, 1), args.act)
+    scales = args.scales or wl.scales
+    desc = moe.Desc(wl.fmt, wl.E, wl.H, wl.I, wl.k, max(wl.M, 1), args.act, scales=scales)
 
     def dt(a):
         a = np.ascontiguousarray(a)
@@ -337,7 +356,8 @@ def main():
         log(f"[bench] routing {route_us:.3f} us, combine {comb_us:.3f} us; "
             f"fc1_gemm {fc1_us:.3f} us, fc2_gemm {fc2_us:.3f} us")
 
-    U, b13, b2 = routed_bytes(wl, groups[0][0].cpu().numpy())
+    csf = scales == "csf" and not grouped  # the grouped path reads the plain scales
+    U, b13, b2 = routed_bytes(wl, groups[0][0].cpu().numpy(), d, csf)
     layer_bytes = b13 + b2
     from block_scaled_fp4_gather_amd import profsum
     if grouped:
@@ -353,7 +373,7 @@ def main():
         dom, dom_work, dom_us = ("fc1_kernel", b13, fc1_us) if b13 >= b2 else ("fc2_kernel", b2, fc2_us)
         achieved = dom_work / (dom_us * 1e-6) / 1e9
         peak, unit, bound = HBM_PEAK_GBPS, "GB/s", "hbm"
-    prof = profsum.lookup(dom, wl.name) if args.shape is None else None
+    prof = profsum.lookup(dom, wl.name) if args.shape is None and scales == wl.scales else None
     traffic = prof["hbm_bytes_per_dispatch"] if prof else None
     # `achieved` from the rocprofv3 mean duration of the kernel (the summary
     # of this same command in profiles/, while its HIP sources are
@@ -430,6 +450,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "format": wl.fmt, "E": wl.E, "H": wl.H, "I": wl.I,
                    "M": wl.M, "top_k": wl.k, "unique_experts": U, "activations": "mxfp8" if a8 else "bf16",
+                   "scales": scales,
                    "path": "grouped" if plan.path == moe.PATH_GROUPED else "decode"},
         "hbm_frac_layer": round(layer_bytes / (value * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
         "routed_bytes": {"fc1": b13, "fc2": b2},

@@ -49,7 +49,10 @@ moe_fp4_status desc_layout(const moe_fp4_desc* d, Layout* L) {
   if (d->act_fn == MOE_FP4_FN_SWIGLUOAI &&
       (!std::isfinite(d->act_alpha) || !std::isfinite(d->act_beta) || !(d->act_limit > 0.0f)))
     return MOE_FP4_EINVAL;
-  if (!moe::make_layout(d->format, d->num_experts, d->hidden, d->inter, L, gated)) return MOE_FP4_EINVAL;
+  if (d->scale_format != MOE_FP4_SCALES_PLAIN && d->scale_format != MOE_FP4_SCALES_CSF) return MOE_FP4_EINVAL;
+  if (!moe::make_layout(d->format, d->num_experts, d->hidden, d->inter, L, gated,
+                        d->scale_format == MOE_FP4_SCALES_CSF))
+    return MOE_FP4_EINVAL;
   L->act = moe::ActParams{d->act_fn, d->act_alpha, d->act_beta, d->act_limit};
   return MOE_FP4_OK;
 }

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "layout.h"
+
 namespace moe {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -60,6 +62,36 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 // MXFP4: byte c%4 of dword c/4.  NVFP4: bytes 2(c%2), 2(c%2)+1 of dword c/2.
 __device__ __forceinline__ float mx_scale(uint32_t dword, int c) {
   return ue8m0_to_f32(dword >> (8 * (c & 3)));
+}
+
+// Compressed scales (the CSF block of a tile, layout.h).  The CSF word of
+// chunk c of a lane's row: base byte and the offsets of c's group of chunks.
+template <int FMT>
+__device__ __forceinline__ uint32_t csf_load(const uint8_t* csf, int lane, int c) {
+  return __builtin_nontemporal_load((const uint32_t*)(csf + 256 * (c / (FMT == kMXFP4 ? 24 : 3)) + 4 * lane));
+}
+
+// Chunk c's scale bytes from its CSF word, placed where the plain scale word
+// holds them (so mx_scale / e4m3x2_to_f32 read them alike): MXFP4 byte c %
+// 4; NVFP4 bytes 2 (c % 2) and 2 (c % 2) + 1.  Not for exception rows.
+template <int FMT>
+__device__ __forceinline__ uint32_t csf_word(uint32_t w, int c) {
+  const uint32_t base = w & 0xFFu;
+  if (FMT == kMXFP4) return ((base + ((w >> (8 + c % 24)) & 1u)) & 0xFFu) << (8 * (c & 3));
+  const uint32_t ob = (w >> (8 + 8 * (c % 3))) & 0xFFu;
+  const uint32_t s = ((base + (ob & 15u)) & 0xFFu) | (((base + (ob >> 4)) & 0xFFu) << 8);
+  return (c & 1) ? s << 16 : s;
+}
+
+// Whether a CSF word belongs to an exception row (base byte 255).
+__device__ __forceinline__ bool csf_exception(uint32_t w) { return (w & 0xFFu) == 255u; }
+
+// The scale word of chunk c of a lane's row from the CSF block, or the
+// plain word for an exception row.
+template <int FMT>
+__device__ __forceinline__ uint32_t csf_scale_word(const uint8_t* csf, int lane, int c, uint32_t plain) {
+  const uint32_t w = csf_load<FMT>(csf, lane, c);
+  return csf_exception(w) ? plain : csf_word<FMT>(w, c);
 }
 
 }  // namespace moe

@@ -57,7 +57,15 @@ inline int fc2_chunk_lanes(const Layout& L) { return L.nC2 <= 4 ? 4 : (L.nC2 <= 
 // Chunk groups an FC2 lane loads at once: 2 for 8 lanes over 9..16 chunks.
 inline int fc2_chunk_groups(const Layout& L) { return fc2_chunk_lanes(L) == 8 && L.nC2 > 8 ? 2 : 1; }
 
+// Decode kernels with compressed scales keep each row's base byte and offsets
+// in registers: FC1 with 16 chunk lanes and 32 rows (8 rows per lane), and
+// FC2 with 32 rows over two chunk groups (8 units per lane), would spill,
+// so those shapes are not taken for layouts with compressed scales.
+constexpr bool csf_shape_ok(int fc2_kl, int r2, int fc2_ci) { return !(fc2_ci == 2 && r2 * fc2_kl / 64 * fc2_ci > 4); }
+
 inline bool valid_shape(const Layout& L, const DecodeShape& s) {
+  if (L.csf && s.kl1 == 16 && s.r1 == 32) return false;
+  if (L.csf && s.r2 != 0 && !csf_shape_ok(fc2_chunk_lanes(L), s.r2, fc2_chunk_groups(L))) return false;
   if (s.kl1 != 0 && s.kl1 != 4 && s.kl1 != 8 && s.kl1 != 16) return false;
   if (s.r1 != 0 && s.r1 != 16 && s.r1 != 32) return false;
   if (s.r2 != 0 && s.r2 != 8 && s.r2 != 16 && s.r2 != 32) return false;

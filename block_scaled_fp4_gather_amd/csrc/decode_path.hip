@@ -223,7 +223,7 @@ __device__ __forceinline__ void lds_chunk16(const uint16_t* p, uint32_t* d) {
 // its activation chunk is read once and reused for T rows.  The activations
 // of the slot's own token are staged in LDS while the route lookup is in
 // flight.
-template <int FMT, int KL, int R, typename IdT>
+template <int FMT, int KL, int R, bool CSF, typename IdT>
 __global__ void __launch_bounds__(1024)
     fc1_kernel(const uint8_t* __restrict__ prep, const Layout L, const uint16_t* __restrict__ x,
                const IdT* __restrict__ ids, const int M_all, const int k, const int mc,
@@ -263,6 +263,7 @@ __global__ void __launch_bounds__(1024)
   if (e < 0) return;  // same decision in every wave of the workgroup
   const uint8_t* tile = prep + fc1_tile_offset(L, e, b);
   const uint8_t* sbase = tile + (int64_t)L.nC1 * 1024;
+  const uint8_t* csf = tile + L.csf1;  // compressed scales (CSF block)
 
   int m = 0;
   for (int t = 0; t < M; ++t) m += token_routes(mask, t, k) != 0;
@@ -280,8 +281,20 @@ __global__ void __launch_bounds__(1024)
       const int qr = g + RG * j;  // block row: R/2 gate rows, then R/2 up rows
       const int row = (qr < R / 2 ? 0 : 32 - R / 2) + blk * (R / 2) + qr;
       q[j] = __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)cc * 1024 + row * 16));
-      sd[j] = __builtin_nontemporal_load((const uint32_t*)(sbase + (cc / SPD) * 256 + row * 4));
+      if (CSF)
+        sd[j] = csf_load<FMT>(csf, row, cc);
+      else
+        sd[j] = __builtin_nontemporal_load((const uint32_t*)(sbase + (cc / SPD) * 256 + row * 4));
     }
+    // The chunk scale word of row j: the plain word, or rebuilt from the CSF
+    // word where it is used (an exception row, base 255, reads its plain word).
+    auto sword = [&](int j) -> uint32_t {
+      if (!CSF) return sd[j];
+      if (!csf_exception(sd[j])) return csf_word<FMT>(sd[j], cc);
+      const int qr = g + RG * j;
+      const int row = (qr < R / 2 ? 0 : 32 - R / 2) + blk * (R / 2) + qr;
+      return *(const uint32_t*)(sbase + (cc / SPD) * 256 + row * 4);
+    };
     int ti = 0;
     for (int t = 0; t < M; ++t) {
       if (!token_routes(mask, t, k)) continue;
@@ -292,7 +305,7 @@ __global__ void __launch_bounds__(1024)
         load_chunk16(x + (int64_t)t * L.H + 32 * cc, xc);
       float v[T];
 #pragma unroll
-      for (int j = 0; j < T; ++j) v[j] = cv ? unit_dot<FMT>(q[j], xc, chunk_scale<FMT>(sd[j], cc)) : 0.0f;
+      for (int j = 0; j < T; ++j) v[j] = cv ? unit_dot<FMT>(q[j], xc, chunk_scale<FMT>(sword(j), cc)) : 0.0f;
       const float r = fold_rows<KL, T>(v, p);
       if (p < T) part[(ti * 16 + wave) * R + g + RG * p] += r;
       ++ti;
@@ -337,7 +350,7 @@ __global__ void __launch_bounds__(1024)
 // expert's block rows q = g + RG*j, j < T.  With STAGE, the activations of
 // every route slot of the group are staged in LDS while the route lookup is
 // in flight.
-template <int FMT, int KL, int R, int CI, bool STAGE, typename IdT>
+template <int FMT, int KL, int R, int CI, bool STAGE, bool CSF, typename IdT>
 __global__ void __launch_bounds__(64 * fc2_max_waves(KL))
     fc2_kernel(const uint8_t* __restrict__ prep, const Layout L, const IdT* __restrict__ ids,
                const float* __restrict__ tw, const int M_all, const int k, const int tg,
@@ -384,6 +397,7 @@ __global__ void __launch_bounds__(64 * fc2_max_waves(KL))
     if (e < 0) continue;
     const uint8_t* tile = prep + fc2_tile_offset(L, e, hb);
     const uint8_t* sbase = tile + (int64_t)L.nC2 * 1024;
+    const uint8_t* csf = tile + L.csf2;  // compressed scales (CSF block)
     const float g2 = FMT == kNVFP4 ? ((const float*)prep)[L.E + e] : 1.0f;
     // CI groups of KL chunks per pass, all their loads issued together
     for (int c0 = 0; c0 < L.nC2; c0 += CI * KL) {
@@ -396,7 +410,10 @@ __global__ void __launch_bounds__(64 * fc2_max_waves(KL))
         for (int j = 0; j < T; ++j) {
           const int row = row0 % 64 + g + RG * j;  // tile rows past H are zero padding
           q[ci][j] = __builtin_nontemporal_load((const u32x4*)(tile + (int64_t)cc * 1024 + row * 16));
-          sd[ci][j] = __builtin_nontemporal_load((const uint32_t*)(sbase + (cc / SPD) * 256 + row * 4));
+          if (CSF)
+            sd[ci][j] = csf_load<FMT>(csf, row, cc);
+          else
+            sd[ci][j] = __builtin_nontemporal_load((const uint32_t*)(sbase + (cc / SPD) * 256 + row * 4));
         }
       }
       for (int t = 0; t < M; ++t) {
@@ -425,7 +442,13 @@ __global__ void __launch_bounds__(64 * fc2_max_waves(KL))
           }
 #pragma unroll
           for (int j = 0; j < T; ++j) {
-            const f32x2_t sc = chunk_scale<FMT>(sd[ci][j], cc);
+            // the chunk scale word: plain, or rebuilt from the CSF word (an
+            // exception row, base 255, reads its plain word here)
+            uint32_t word = sd[ci][j];
+            if (CSF)
+              word = !csf_exception(word) ? csf_word<FMT>(word, cc)
+                                          : *(const uint32_t*)(sbase + (cc / SPD) * 256 + (row0 % 64 + g + RG * j) * 4);
+            const f32x2_t sc = chunk_scale<FMT>(word, cc);
             const float d = cv ? unit_dot2<FMT>(q[ci][j], ah, al, sc) : 0.0f;
             v[j] = ci == 0 ? d : v[j] + d;
           }
@@ -457,12 +480,26 @@ hipError_t launch_fc1(const Layout& L, const uint8_t* prep, const uint16_t* x, i
   const size_t lds = (size_t)fc1_lds_bytes(L, mc, R);
   const dim3 grid((unsigned)((int64_t)slots * L.nB1 * (64 / R)), (unsigned)((M + mc - 1) / mc)),
       block(64 * waves);
-  if (big)
-    hipLaunchKernelGGL((fc1_kernel<FMT, KL, 32, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, mc, act_hi,
-                       act_lo);
-  else
-    hipLaunchKernelGGL((fc1_kernel<FMT, KL, 16, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, mc, act_hi,
-                       act_lo);
+#define MOE_FC1(RR, CC)                                                                                     \
+  hipLaunchKernelGGL((fc1_kernel<FMT, KL, RR, CC, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, mc, act_hi, \
+                     act_lo)
+  if (big) {
+    if constexpr (KL == 16) {  // 8 rows per lane: no registers left for compressed scales
+      if (L.csf) return hipErrorInvalidValue;  // valid_shape rejects this shape first
+      MOE_FC1(32, false);
+    } else {
+      if (L.csf)
+        MOE_FC1(32, true);
+      else
+        MOE_FC1(32, false);
+    }
+  } else {
+    if (L.csf)
+      MOE_FC1(16, true);
+    else
+      MOE_FC1(16, false);
+  }
+#undef MOE_FC1
   return hipGetLastError();
 }
 
@@ -493,12 +530,23 @@ hipError_t launch_fc2_ci(const Layout& L, const uint8_t* prep, int M, int k, con
   const bool stage = act_bytes <= kStageActBytes && part_bytes + act_bytes <= kMaxLdsBytes;
   const size_t lds = part_bytes + (stage ? act_bytes : 0);
   const dim3 grid((unsigned)((L.H + R - 1) / R), (unsigned)((M + tg - 1) / tg)), block(64 * waves);
-  if (stage)
-    hipLaunchKernelGGL((fc2_kernel<FMT, KL, R, CI, true, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, tg,
-                       ah, al, out);
-  else
-    hipLaunchKernelGGL((fc2_kernel<FMT, KL, R, CI, false, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, tg,
-                       ah, al, out);
+#define MOE_FC2(SS, CC)                                                                                  \
+  hipLaunchKernelGGL((fc2_kernel<FMT, KL, R, CI, SS, CC, IdT>), grid, block, lds, st, prep, L, ids, tw, M, k, tg, \
+                     ah, al, out)
+  constexpr bool csf_ok = csf_shape_ok(KL, R, CI);
+  if (L.csf && !csf_ok) return hipErrorInvalidValue;  // valid_shape rejects this shape first
+  if (stage) {
+    if constexpr (csf_ok) {
+      if (L.csf) MOE_FC2(true, true);
+    }
+    if (!L.csf) MOE_FC2(true, false);
+  } else {
+    if constexpr (csf_ok) {
+      if (L.csf) MOE_FC2(false, true);
+    }
+    if (!L.csf) MOE_FC2(false, false);
+  }
+#undef MOE_FC2
   return hipGetLastError();
 }
 

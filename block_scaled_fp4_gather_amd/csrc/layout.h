@@ -24,6 +24,23 @@
 //
 // Buffer: [NVFP4 globals g13[E], g2[E], padded to 256 B] then E experts, each
 // [FC1 tiles][FC2 tiles], expert stride a multiple of 256 B.
+//
+// Compressed scales (b12x PR #459, "Reduce NVFP4-CSF scale reconstruction
+// overhead", commit messages: one-bit MXFP4 and four-bit NVFP4 offsets from
+// a row base byte).  With the compressed scale format every tile also holds,
+// after its plain scale words, a CSF block of its 64 rows:
+//   [group g][lane l][4 B]   one word per row and group of chunks: byte 0 the
+//                            row's base byte (its smallest scale byte, or 255:
+//                            the row is an exception and its plain scale words
+//                            hold its scales), then the offsets of the group's
+//                            chunks: MXFP4 24 chunks, bit 8+j the offset (0/1)
+//                            of chunk 24g+j; NVFP4 3 chunks, byte 1+j those of
+//                            chunk 3g+j (low nibble: its first 16 elements,
+//                            high nibble: the second 16)
+// so that a chunk's scale byte is base + offset, and a lane reads one word per
+// row and chunk, as with the plain words.  The decode kernels read the CSF
+// block; the grouped GEMMs and the inverse preparation read the plain scale
+// words, which stay in place.
 #pragma once
 
 #include <stddef.h>
@@ -60,14 +77,29 @@ struct Layout {
   int64_t expert;   // expert stride
   int64_t globals;  // bytes of the globals header
   int64_t total;    // whole prepared buffer
+  int32_t csf;      // tiles carry a CSF block (compressed scale format)
+  int64_t csf1;     // offset of the CSF block in an FC1 tile (0 without)
+  int64_t csf2;     // offset of the CSF block in an FC2 tile (0 without)
   ActParams act;    // the layer's activation (not part of the byte layout)
 };
 
 MOE_HD inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
+// Chunks whose offsets one CSF word holds: 24 (MXFP4), 3 (NVFP4).
+MOE_HD inline int32_t csf_chunks_per_word(int32_t fmt) { return fmt == kMXFP4 ? 24 : 3; }
+
+// Bytes of the CSF block of a tile with nC chunks per row: 256 B (64 words)
+// per group of chunks.
+MOE_HD inline int64_t csf_block_bytes(int32_t fmt, int32_t nC) {
+  const int32_t cw = csf_chunks_per_word(fmt);
+  return 256 * (int64_t)((nC + cw - 1) / cw);
+}
+
 // Returns false when the shape is outside what the layout supports.  W13
-// has 2I rows when `gated`, I rows (I a multiple of 64) otherwise.
-MOE_HD inline bool make_layout(int32_t fmt, int32_t E, int32_t H, int32_t I, Layout* L, bool gated = true) {
+// has 2I rows when `gated`, I rows (I a multiple of 64) otherwise; `csf`
+// adds the compressed scale blocks.
+MOE_HD inline bool make_layout(int32_t fmt, int32_t E, int32_t H, int32_t I, Layout* L, bool gated = true,
+                               bool csf = false) {
   if (fmt != kMXFP4 && fmt != kNVFP4) return false;
   if (E <= 0 || H <= 0 || I <= 0 || H % 32 || I % 32) return false;
   if (!gated && I % 64) return false;
@@ -83,8 +115,11 @@ MOE_HD inline bool make_layout(int32_t fmt, int32_t E, int32_t H, int32_t I, Lay
   L->nB2 = (H + 63) / 64;
   L->nQ1 = (H / L->G + 3) / 4;
   L->nQ2 = (I / L->G + 3) / 4;
-  L->tile1 = (int64_t)L->nC1 * 1024 + (int64_t)L->nQ1 * 256;
-  L->tile2 = (int64_t)L->nC2 * 1024 + (int64_t)L->nQ2 * 256;
+  L->csf = csf ? 1 : 0;
+  L->csf1 = csf ? (int64_t)L->nC1 * 1024 + (int64_t)L->nQ1 * 256 : 0;
+  L->csf2 = csf ? (int64_t)L->nC2 * 1024 + (int64_t)L->nQ2 * 256 : 0;
+  L->tile1 = (int64_t)L->nC1 * 1024 + (int64_t)L->nQ1 * 256 + (csf ? csf_block_bytes(fmt, L->nC1) : 0);
+  L->tile2 = (int64_t)L->nC2 * 1024 + (int64_t)L->nQ2 * 256 + (csf ? csf_block_bytes(fmt, L->nC2) : 0);
   L->w13 = L->tile1 * L->nB1;
   L->expert = align_up(L->w13 + L->tile2 * L->nB2, 256);
   L->globals = fmt == kNVFP4 ? align_up(8 * (int64_t)E, 256) : 0;

@@ -74,6 +74,53 @@ __global__ void __launch_bounds__(256) repack_kernel(Layout L, PrepShape P, int 
   }
 }
 
+// CSF blocks (layout.h): one thread per (expert, tile, lane) of every FC1 and
+// FC2 tile.  The lane's logical row of scale bytes gives its base byte (the
+// smallest byte, or 255 for an exception row: bytes spanning more than the
+// offsets reach (1 MXFP4, 15 NVFP4), or a smallest byte of 255) and its
+// offsets (0 for exception and padding rows), written as one word per group
+// of chunks.
+__global__ void __launch_bounds__(256) csf_kernel(Layout L, const uint8_t* __restrict__ w13s,
+                                                  const uint8_t* __restrict__ w2s, uint8_t* __restrict__ prep) {
+  const int64_t per_e = 64 * (int64_t)(L.nB1 + L.nB2);
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= per_e * L.E) return;
+  const int e = (int)(idx / per_e);
+  const int r = (int)(idx % per_e);
+  const int tile = r / 64, lane = r % 64;
+  const bool fc1 = tile < L.nB1;
+  const int t = fc1 ? tile : tile - L.nB1;
+  const int rows = fc1 ? 2 * L.Ip : L.H;
+  const int row = fc1 ? fc1_row(L, t, lane) : t * 64 + lane;
+  const int nC = fc1 ? L.nC1 : L.nC2;
+  const int nsc = (fc1 ? L.H : L.I) / L.G;  // scale bytes per row
+  uint8_t* blk = prep + (fc1 ? fc1_tile_offset(L, e, t) + L.csf1 : fc2_tile_offset(L, e, t) + L.csf2);
+  const uint8_t* src = (fc1 ? w13s : w2s) + ((int64_t)e * rows + row) * nsc;
+  const uint32_t reach = L.fmt == kMXFP4 ? 1u : 15u;
+  uint32_t base = 0u;
+  if (row < rows) {
+    uint32_t lo = 255u, hi = 0u;
+    for (int j = 0; j < nsc; ++j) {
+      lo = src[j] < lo ? src[j] : lo;
+      hi = src[j] > hi ? src[j] : hi;
+    }
+    base = (lo == 255u || hi - lo > reach) ? 255u : lo;
+  }
+  const bool packed = row < rows && base != 255u;
+  const int cw = csf_chunks_per_word(L.fmt);
+  for (int g = 0; g < (nC + cw - 1) / cw; ++g) {
+    uint32_t w = base;
+    for (int j = 0; j < cw && packed && cw * g + j < nC; ++j) {
+      const int c = cw * g + j;
+      if (L.fmt == kMXFP4)
+        w |= ((uint32_t)src[c] - base) << (8 + j);
+      else
+        w |= (((uint32_t)src[2 * c] - base) | (((uint32_t)src[2 * c + 1] - base) << 4)) << (8 + 8 * j);
+    }
+    *(uint32_t*)(blk + 256 * g + 4 * lane) = w;
+  }
+}
+
 // Globals header: words [0, E) = g13, [E, 2E) = g2, the rest zero padding.
 __global__ void globals_kernel(int E, int words, int dir, float* g13, float* g2,
                                float* prep_globals) {
@@ -131,10 +178,13 @@ __global__ void __launch_bounds__(256) export_kernel(Layout L, int e, int which,
     }
   }
   float s0, s1;
+  const uint8_t* csf = L.csf ? prep + toff + (fc1 ? L.csf1 : L.csf2) : nullptr;
   if (L.fmt == kMXFP4) {
-    s0 = s1 = mx_scale(sw[64 * (c / 4)], c);
+    const uint32_t word = csf ? csf_scale_word<kMXFP4>(csf, lane, c, sw[64 * (c / 4)]) : sw[64 * (c / 4)];
+    s0 = s1 = mx_scale(word, c);
   } else {
-    const f32x2_t s = e4m3x2_to_f32(sw[64 * (c / 2)], c & 1);
+    const uint32_t word = csf ? csf_scale_word<kNVFP4>(csf, lane, c, sw[64 * (c / 2)]) : sw[64 * (c / 2)];
+    const f32x2_t s = e4m3x2_to_f32(word, c & 1);
     s0 = s.x;
     s1 = s.y;
   }
@@ -157,6 +207,12 @@ hipError_t launch_repack(const Layout& L, int dir, uint8_t* w13c, uint8_t* w13s,
                      w2c, w2s, prep);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (L.csf && dir == 0) {
+    const int64_t m = 64 * (int64_t)(L.nB1 + L.nB2) * L.E;
+    hipLaunchKernelGGL(csf_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, st, L, w13s, w2s, prep);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   if (L.fmt == kNVFP4) {
     const int words = (int)(L.globals / 4);
     hipLaunchKernelGGL(globals_kernel, dim3((words + 255) / 256), dim3(256), 0, st, L.E, words, dir,

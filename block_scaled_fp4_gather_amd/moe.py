@@ -34,6 +34,9 @@ PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
 ACT_BF16, ACT_MXFP8 = 0, 1
 ACT_FORMATS = {"bf16": ACT_BF16, "mxfp8": ACT_MXFP8}
 
+SCALES_PLAIN, SCALES_CSF = 0, 1
+SCALE_FORMATS = {"plain": SCALES_PLAIN, "csf": SCALES_CSF}
+
 FN_SILU, FN_GELU_TANH, FN_SWIGLUOAI, FN_RELU2 = 0, 1, 2, 3
 ACT_FNS = {"silu": FN_SILU, "gelu_tanh": FN_GELU_TANH, "swigluoai": FN_SWIGLUOAI, "relu2": FN_RELU2}
 
@@ -50,7 +53,8 @@ class _Desc(ctypes.Structure):
                 ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
                 ("act_format", ctypes.c_int32), ("act_fn", ctypes.c_int32),
-                ("act_alpha", ctypes.c_float), ("act_beta", ctypes.c_float), ("act_limit", ctypes.c_float)]
+                ("act_alpha", ctypes.c_float), ("act_beta", ctypes.c_float), ("act_limit", ctypes.c_float),
+                ("scale_format", ctypes.c_int32)]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -58,7 +62,8 @@ class Desc:
     """Layer shape; `act` is "bf16" or "mxfp8" (the W4A8-MX variant of the
     grouped path, MXFP4 weights only); `fn` the activation ("silu",
     "gelu_tanh", "swigluoai" with alpha, beta and limit, or the non-gated
-    "relu2", whose W13 has I rows)."""
+    "relu2", whose W13 has I rows); `scales` "plain" or "csf" (the
+    compressed scale format, read by the decode path)."""
     fmt: str
     E: int
     H: int
@@ -70,13 +75,15 @@ class Desc:
     alpha: float = 0.0
     beta: float = 0.0
     limit: float = 0.0
+    scales: str = "plain"
 
     def c(self) -> _Desc:
         act = ACT_FORMATS.get(self.act, self.act) if isinstance(self.act, str) else self.act
         fn = ACT_FNS.get(self.fn, self.fn) if isinstance(self.fn, str) else self.fn
         return _Desc(FORMATS.get(self.fmt, self.fmt) if isinstance(self.fmt, str) else self.fmt,
                      self.E, self.H, self.I, self.k, self.max_tokens, act, fn,
-                     self.alpha, self.beta, self.limit)
+                     self.alpha, self.beta, self.limit, SCALE_FORMATS.get(self.scales, self.scales)
+                     if isinstance(self.scales, str) else self.scales)
 
 
 _lib = None

@@ -93,6 +93,8 @@ class Workload:
     seed: int
     n_invalid: int = 0  # route slots overwritten with out-of-range ids
     description: str = ""
+    scales: str = "plain"  # "csf": rows whose scales fit the compressed scale format, 1 in csf_plain_rows not
+    csf_plain_rows: int = 64  # with scales="csf": 1 in this many rows drawn plain (0: none)
 
     @property
     def G(self) -> int:
@@ -146,6 +148,16 @@ WORKLOADS = {
     "nvfp4_e288_routed10": Workload(
         "nvfp4_e288_routed10", "nvfp4", E=288, H=4096, I=512, M=1, k=10, seed=SEED_BASE + 102,
         description="NVFP4 E288/H4096/I512, M=1, top-10 (10 routes)"),
+    # The compressed-scale format (b12x #459: one-bit MXFP4 and four-bit
+    # NVFP4 offsets from a row base byte) on the M = 1 geometries of the
+    # metric and of the E512 decoder table row, with scales drawn so that
+    # rows fit it (1 in 64 rows does not).
+    "mxfp4_csf_shard_e256_m1": Workload(
+        "mxfp4_csf_shard_e256_m1", "mxfp4", E=256, H=7168, I=256, M=1, k=8, seed=SEED_BASE + 200,
+        scales="csf", description="MXFP4 shard E256/H7168/I256, M=1, top-8, compressed scales"),
+    "nvfp4_csf_decode_e512": Workload(
+        "nvfp4_csf_decode_e512", "nvfp4", E=512, H=2560, I=320, M=1, k=10, seed=SEED_BASE + 201,
+        scales="csf", description="NVFP4 decode E512/H2560/I320, M=1, top-10, compressed scales"),
     "nvfp4_e288_routed63": Workload(
         "nvfp4_e288_routed63", "nvfp4", E=288, H=4096, I=512, M=7, k=9, seed=SEED_BASE + 103,
         description="NVFP4 E288/H4096/I512, M=7, top-9 (63 routes)"),
@@ -175,15 +187,41 @@ def scales(wl: Workload, stream: Stream, n: int) -> np.ndarray:
     return _e4m3_bits(v.astype(np.float32))
 
 
+def csf_scales(wl: Workload, stream: Stream, rows: int, n: int) -> np.ndarray:
+    """Block-scale bytes [rows][n] whose rows mostly fit the compressed scale
+    format: per row a base byte and an offset per block, the byte being
+    base + offset (MXFP4: base uniform in [118, 125], offset 0 or 1, so the
+    bytes stay in [118, 126]; NVFP4: base the E4M3 code of min(|N(0,1)| * 64,
+    448) capped at 0x6F, offset uniform in [0, 15], so codes stay at or
+    below 0x7E = 448).  One row in wl.csf_plain_rows (uniformly chosen) is
+    drawn by the plain recipe instead and mostly does not fit."""
+    if wl.fmt == "mxfp4":
+        base = stream.integers(118, 125, rows).astype(np.int64)
+        off = stream.integers(0, 1, rows * n).reshape(rows, n)
+    else:
+        b = _e4m3_bits(np.minimum(np.abs(stream.normal(rows)) * 64.0, 448.0).astype(np.float32))
+        base = np.minimum(b.astype(np.int64), 0x6F)
+        off = stream.integers(0, 15, rows * n).reshape(rows, n)
+    out = (base[:, None] + off).astype(np.uint8)
+    plain = stream.uniform(rows) < (1.0 / wl.csf_plain_rows if wl.csf_plain_rows else 0.0)
+    if plain.any():
+        out[plain] = scales(wl, stream, int(plain.sum()) * n).reshape(-1, n)
+    return out
+
+
 def weights(wl: Workload) -> dict:
     """Expert weights in the logical layout: W13 codes [E][2I][H/2], W13
     scales [E][2I][H/G], W2 codes [E][H][I/2], W2 scales [E][H][I/G]; the
     element at column c of a row sits in byte c/2, low nibble for even c."""
     E, H, I, G = wl.E, wl.H, wl.I, wl.G
     w13c = Stream(wl.seed, _S_W13C).bytes(E * 2 * I * H // 2).reshape(E, 2 * I, H // 2)
-    w13s = scales(wl, Stream(wl.seed, _S_W13S), E * 2 * I * H // G).reshape(E, 2 * I, H // G)
     w2c = Stream(wl.seed, _S_W2C).bytes(E * H * I // 2).reshape(E, H, I // 2)
-    w2s = scales(wl, Stream(wl.seed, _S_W2S), E * H * I // G).reshape(E, H, I // G)
+    if wl.scales == "csf":
+        w13s = csf_scales(wl, Stream(wl.seed, _S_W13S), E * 2 * I, H // G).reshape(E, 2 * I, H // G)
+        w2s = csf_scales(wl, Stream(wl.seed, _S_W2S), E * H, I // G).reshape(E, H, I // G)
+    else:
+        w13s = scales(wl, Stream(wl.seed, _S_W13S), E * 2 * I * H // G).reshape(E, 2 * I, H // G)
+        w2s = scales(wl, Stream(wl.seed, _S_W2S), E * H * I // G).reshape(E, H, I // G)
     if wl.fmt == "nvfp4":
         g13 = np.full(E, 1.0 / 512.0, dtype=np.float32)
         g2 = np.full(E, 1.0 / 512.0, dtype=np.float32)

@@ -105,12 +105,35 @@ typedef enum {
   MOE_FP4_FN_RELU2 = 3
 } moe_fp4_act_fn;
 
+/* Resident form of the block scales (scale_format in moe_fp4_desc).
+ *   PLAIN: the scale bytes as given.
+ *   CSF:   in addition, each weight row's scale bytes compressed as a row
+ *          base byte plus an offset per block, one bit (MXFP4, offset 0 or
+ *          1) or four bits (NVFP4, 0..15), the byte being base + offset
+ *          (b12x PR #459, "Reduce NVFP4-CSF scale reconstruction overhead",
+ *          commit messages: one-bit MXFP4 and four-bit NVFP4 offsets from a
+ *          row base byte).  The base is the row's smallest byte; a row whose
+ *          bytes span more than the offsets reach, or whose smallest byte is
+ *          255, is an exception read from the plain bytes.  Lossless: every
+ *          result equals the PLAIN one bit for bit.  The decode path reads
+ *          the compressed scales (one 4-byte word of base byte and offsets
+ *          per row and 24 (MXFP4) or 3 (NVFP4) chunks of 32 weights, against
+ *          1 or 2 plain bytes per chunk) and the plain bytes of exception
+ *          rows only; the grouped path and moe_fp4_unprepare read the plain
+ *          bytes.  The prepared buffer grows by the compressed blocks
+ *          (moe_fp4_prepared_bytes). */
+typedef enum {
+  MOE_FP4_SCALES_PLAIN = 0,
+  MOE_FP4_SCALES_CSF = 1
+} moe_fp4_scale_format;
+
 /* Shape of one MoE layer.  H and I must be multiples of 32 for both formats
  * (the kernels work in 32-element units); max_tokens is the largest M that
  * later forward calls will pass, used only to size the workspace.
  * act_format is a moe_fp4_act_format (0 keeps bf16 activations); MXFP8 with
  * NVFP4 weights returns MOE_FP4_EUNSUPPORTED.  act_fn and its parameters
- * choose the gated activation (0 and zeros: SiLU). */
+ * choose the gated activation (0 and zeros: SiLU).  scale_format is a
+ * moe_fp4_scale_format (0: plain). */
 typedef struct {
   int32_t format;      /* moe_fp4_format */
   int32_t num_experts; /* E, resident experts; ids outside [0, E) are invalid */
@@ -123,6 +146,7 @@ typedef struct {
   float act_alpha;     /* SWIGLUOAI only, else ignored */
   float act_beta;
   float act_limit;
+  int32_t scale_format; /* moe_fp4_scale_format */
 } moe_fp4_desc;
 
 /* Human-readable name of a status code (static string).  A diagnostic hook

@@ -303,3 +303,40 @@ def test_noalloc_forward_rejects_before_any_hip_call(L):
     assert moe.workspace_bytes(big, 1) > 64 << 20
     assert fn(*args(big, 1)) == 3               # MOE_FP4_EWORKSPACE
     assert fn(*args(moe.Desc("mxfp4", 8, 250, 128, 2, 4), 1)) == 1  # H not whole scale blocks
+
+
+def test_csf_prepared_bytes_and_validation(L):
+    """The compressed scale format adds one CSF block per tile (a 256-byte
+    group of one word per row for every 24 (MXFP4) or 3 (NVFP4) chunks) to the
+    plain layout; any other scale format is rejected."""
+    for fmt, G in (("mxfp4", 32), ("nvfp4", 16)):
+        for E, H, I in ((8, 256, 128), (256, 7168, 256), (512, 2560, 320), (3, 96, 64)):
+            plain = moe.prepared_bytes(moe.Desc(fmt, E, H, I, 2, 1))
+            csf = moe.prepared_bytes(moe.Desc(fmt, E, H, I, 2, 1, scales="csf"))
+            nC1, nC2 = H // 32, I // 32
+
+            def block(nC):  # 256 bytes per group of 24 (MXFP4) or 3 (NVFP4) chunks
+                return 256 * -(-nC // (24 if fmt == "mxfp4" else 3))
+            tiles1, tiles2 = (2 * I) // 64, -(-H // 64)
+            grow = E * (tiles1 * block(nC1) + tiles2 * block(nC2))
+            # the expert stride stays a multiple of 256 bytes, so the growth is exact
+            assert csf - plain == grow, (fmt, E, H, I)
+    bad = moe.Desc("mxfp4", 8, 256, 128, 2, 1, scales=2)
+    with pytest.raises(moe.MoeFp4Error) as ei:
+        moe.prepared_bytes(bad)
+    assert ei.value.status == 1
+
+
+def test_csf_rejects_the_shapes_it_does_not_run(L):
+    """With compressed scales the decode kernels keep each row's base byte
+    and offsets in registers; the two launch shapes that would spill are
+    rejected before any launch."""
+    desc = moe.Desc("mxfp4", 4, 512, 320, 2, 1, scales="csf")
+    assert _plan(desc, 1)[0] == moe.PATH_DECODE
+    for t in (moe.Tuning(16, 32, 0, moe.PATH_DECODE),   # 8 FC1 rows per lane
+              moe.Tuning(0, 0, 32, moe.PATH_DECODE)):   # 32 FC2 rows over two chunk groups (I = 320)
+        with pytest.raises(moe.MoeFp4Error) as ei:
+            moe.plan(desc, 1, t)
+        assert ei.value.status == 1
+    plain = moe.Desc("mxfp4", 4, 512, 320, 2, 1)
+    assert _plan(plain, 1, moe.Tuning(16, 32, 32, moe.PATH_DECODE))[0] == moe.PATH_DECODE
