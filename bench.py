@@ -350,7 +350,7 @@ def main():
         # (with FC2): time those alone and take them out of the GEMM figures
         route_us, _, _ = region(phases=4)
         comb_us, _, _ = region(phases=8)
-        aux = {"route_build": round(route_us, 3), "combine": round(comb_us, 3),
+        aux = {"routing": round(route_us, 3), "combine": round(comb_us, 3),
                "fc1_half": round(fc1_us, 3), "fc2_half": round(fc2_us, 3)}
         fc1_us, fc2_us = fc1_us - route_us, fc2_us - comb_us
         log(f"[bench] routing {route_us:.3f} us, combine {comb_us:.3f} us; "

@@ -16,6 +16,7 @@ struct PrefillWs {
   int64_t counts;      // int32 [E]   valid routes per expert
   int64_t grp_start;   // int32 [E]   first grouped row of each expert
   int64_t tile_start;  // int32 [E+1] first m-tile of each expert; [E] = total tiles
+  int64_t fill;        // int32 [E]   grouped rows handed out per expert (routing)
   int64_t perm;        // int32 [R]   grouped row -> route index t*k + j
   int64_t rpos;        // int32 [R]   route index -> grouped row (valid routes)
   // bf16 activations:
@@ -41,7 +42,8 @@ inline PrefillWs prefill_ws(const Layout& L, int64_t routes, int64_t tokens, boo
   w.counts = 0;
   w.grp_start = align_up(4 * (int64_t)L.E, 256);
   w.tile_start = w.grp_start + align_up(4 * (int64_t)L.E, 256);
-  w.perm = w.tile_start + align_up(4 * ((int64_t)L.E + 1), 256);
+  w.fill = w.tile_start + align_up(4 * ((int64_t)L.E + 1), 256);
+  w.perm = w.fill + align_up(4 * (int64_t)L.E, 256);
   w.rpos = w.perm + align_up(4 * routes, 256);
   int64_t o = w.rpos + align_up(4 * routes, 256);
   w.act = w.xq = w.xs = w.aq = w.as = o;

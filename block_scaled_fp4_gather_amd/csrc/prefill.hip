@@ -6,9 +6,9 @@
 // large tile (flashinfer #4285, description: MoEDynamicKernel with tiles
 // smaller than 128 rows), and reduces the routed outputs into fp32 before one
 // cast (b12x #311, commit on the prefill fused-sum epilogue).  Here:
-//   route_build  groups the valid routes by expert in route order
-//                (deterministic) and numbers the 128-row m-tiles of every
-//                expert;
+//   routing    groups the valid routes by expert (route_one, or route_zero,
+//              route_count and route_place for many routes) and numbers the
+//              128-row m-tiles of every expert;
 //   fc1_gemm   x rows gathered into LDS, FP4 weight tiles dequantised to
 //              bf16 into LDS (exact: E2M1 times a UE8M0 or E4M3 block scale
 //              has at most 6 significant bits), v_mfma_f32_32x32x16_bf16 with
@@ -40,81 +40,166 @@ __device__ __forceinline__ int route_expert(const IdT* __restrict__ ids, int r, 
   return (v >= 0 && v < E) ? (int)v : -1;
 }
 
-__device__ __forceinline__ int wave_sum(int v) {
+// Routing: the valid routes grouped by expert.  Expert e's routes take the
+// grouped rows [grp_start[e], grp_start[e] + counts[e]) and its m-tiles
+// [tile_start[e], tile_start[e + 1]); perm maps a grouped row to its route,
+// rpos a route to its grouped row.  The order of an expert's routes within
+// its rows is whatever the atomics hand out: every grouped row is computed
+// from its own route alone and the combine sums a token's routes in route
+// order through rpos, so the layer's output does not depend on it.  Ids are
+// checked before they index anything (b12x PR #311, review of dynamic.py:
+// unchecked top-k ids index the per-expert counters out of bounds).
+constexpr int kRouteBlock = 4096;  // routes per workgroup of the routing kernels
+
+// Exclusive prefix over the E counters cnt (in LDS, E <= kRouteMaxExperts)
+// by the 1024 threads of a workgroup: counts[e], grp_start[e] and
+// tile_start[e] (m-tiles of kGemmBM rows; tile_start[E] the total) are
+// written to global memory when `out` is set, and cnt[e] becomes
+// grp_start[e].  Ends with a barrier.
+__device__ void route_prefix(int* cnt, int E, bool out, int* __restrict__ counts, int* __restrict__ grp_start,
+                             int* __restrict__ tile_start) {
+  __shared__ int wpart[2][16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  constexpr int PER = kRouteMaxExperts / 1024;  // counters per thread
+  const int e0 = t * PER;
+  int c[PER], rsum = 0, tsum = 0;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
+  for (int i = 0; i < PER; ++i) {
+    c[i] = e0 + i < E ? cnt[e0 + i] : 0;
+    rsum += c[i];
+    tsum += (c[i] + kGemmBM - 1) / kGemmBM;
+  }
+  // inclusive scans of the per-thread sums over the wave, then over the waves
+  int ri = rsum, ti = tsum;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int rv = __shfl_up(ri, m), tv = __shfl_up(ti, m);
+    if (lane >= m) {
+      ri += rv;
+      ti += tv;
+    }
+  }
+  if (lane == 63) {
+    wpart[0][wave] = ri;
+    wpart[1][wave] = ti;
+  }
+  __syncthreads();
+  int rb = ri - rsum, tb = ti - tsum;  // exclusive within the wave
+  for (int w = 0; w < wave; ++w) {
+    rb += wpart[0][w];
+    tb += wpart[1][w];
+  }
+  int ttot = 0;
+  for (int w = 0; w < 16; ++w) ttot += wpart[1][w];
+  __syncthreads();  // every thread has read cnt before it is overwritten
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = e0 + i;
+    if (e < E) {
+      if (out) {
+        counts[e] = c[i];
+        grp_start[e] = rb;
+        tile_start[e] = tb;
+      }
+      cnt[e] = rb;
+    }
+    rb += c[i];
+    tb += (c[i] + kGemmBM - 1) / kGemmBM;
+  }
+  if (out && t == 0) tile_start[E] = ttot;
+  __syncthreads();
 }
 
-// One workgroup per expert e.  Every workgroup builds the histogram of
-// valid routes over all experts in LDS (so no workgroup waits for another),
-// derives e's group start and m-tile start from it, and places e's routes at
-// consecutive grouped rows in route order: each wave takes a contiguous
-// slice of the routes, counts its matches with ballots, and after a prefix
-// over the waves writes perm (grouped row -> route) and rpos (route ->
-// grouped row).  Workgroup e also writes counts[e], and the last one the
-// total m-tile count tile_start[E].
+// All of the routing in one workgroup (R <= kRouteBlock): an LDS histogram,
+// its prefix, then every route takes its grouped row from an LDS counter.
 template <typename IdT>
 __global__ void __launch_bounds__(1024)
-    route_build(const IdT* __restrict__ ids, int R, int E, int* __restrict__ counts,
-                int* __restrict__ grp_start, int* __restrict__ tile_start, int* __restrict__ perm,
-                int* __restrict__ rpos) {
-  __shared__ int hist[kRouteMaxExperts];
-  __shared__ int part[3][16];
-  const int e = blockIdx.x;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  for (int q = t; q < E; q += 1024) hist[q] = 0;
+    route_one(const IdT* __restrict__ ids, int R, int E, int* __restrict__ counts, int* __restrict__ grp_start,
+              int* __restrict__ tile_start, int* __restrict__ perm, int* __restrict__ rpos) {
+  __shared__ int cnt[kRouteMaxExperts];
+  const int t = threadIdx.x;
+  for (int q = t; q < E; q += 1024) cnt[q] = 0;
   __syncthreads();
-  for (int r = t; r < R; r += 1024) {
-    const int x = route_expert(ids, r, R, E);
-    if (x >= 0) atomicAdd(&hist[x], 1);
-  }
-  __syncthreads();
-  int off = 0, toff = 0;
-  for (int q = t; q < e; q += 1024) {
-    const int c = hist[q];
-    off += c;
-    toff += (c + kGemmBM - 1) / kGemmBM;
-  }
-  off = wave_sum(off);
-  toff = wave_sum(toff);
-  // this wave's slice of the routes, in whole ballots
-  const int slice = ((R + 15) / 16 + 63) / 64 * 64;
-  const int r0 = wave * slice, r1 = min(R, r0 + slice);
-  int mine = 0;
-  for (int base = r0; base < r1; base += 64) mine += __popcll(__ballot(route_expert(ids, base + lane, r1, E) == e));
-  if (lane == 0) {
-    part[0][wave] = off;
-    part[1][wave] = toff;
-    part[2][wave] = mine;
-  }
-  __syncthreads();
-  int goff = 0, gtoff = 0, pos = 0;
+  int ex[kRouteBlock / 1024];
 #pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    goff += part[0][w];
-    gtoff += part[1][w];
-    pos += w < wave ? part[2][w] : 0;
+  for (int i = 0; i < kRouteBlock / 1024; ++i) {
+    ex[i] = route_expert(ids, t + 1024 * i, R, E);
+    if (ex[i] >= 0) atomicAdd(&cnt[ex[i]], 1);
   }
-  if (t == 0) {
-    const int ce = hist[e];
-    counts[e] = ce;
-    grp_start[e] = goff;
-    tile_start[e] = gtoff;
-    if (e == E - 1) tile_start[E] = gtoff + (ce + kGemmBM - 1) / kGemmBM;
+  __syncthreads();
+  route_prefix(cnt, E, true, counts, grp_start, tile_start);
+#pragma unroll
+  for (int i = 0; i < kRouteBlock / 1024; ++i) {
+    if (ex[i] < 0) continue;
+    const int r = t + 1024 * i;
+    const int p = atomicAdd(&cnt[ex[i]], 1);
+    perm[p] = r;
+    rpos[r] = p;
   }
-  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  pos += goff;
-  for (int base = r0; base < r1; base += 64) {
-    const int r = base + lane;
-    const bool hit = route_expert(ids, r, r1, E) == e;
-    const uint64_t m = __ballot(hit);
-    if (hit) {
-      const int p = pos + __popcll(m & below);
-      perm[p] = r;
-      rpos[r] = p;
-    }
-    pos += __popcll(m);
+}
+
+// Routing of more routes, in three launches.  route_zero clears the
+// counters; route_count adds each block's LDS histogram to counts (one
+// global add per block and expert); route_place takes the prefix of
+// counts, reserves each expert's range for the block (one global add per
+// block and expert on fill) and hands out the rows within it from LDS.
+__global__ void route_zero(int E, int* __restrict__ counts, int* __restrict__ fill) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e < E) {
+    counts[e] = 0;
+    fill[e] = 0;
+  }
+}
+
+template <typename IdT>
+__global__ void __launch_bounds__(1024)
+    route_count(const IdT* __restrict__ ids, int R, int E, int* __restrict__ counts) {
+  __shared__ int cnt[kRouteMaxExperts];
+  const int t = threadIdx.x;
+  const int r0 = blockIdx.x * kRouteBlock;
+  for (int q = t; q < E; q += 1024) cnt[q] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRouteBlock / 1024; ++i) {
+    const int e = route_expert(ids, r0 + t + 1024 * i, R, E);
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int q = t; q < E; q += 1024)
+    if (cnt[q]) atomicAdd(&counts[q], cnt[q]);
+}
+
+template <typename IdT>
+__global__ void __launch_bounds__(1024)
+    route_place(const IdT* __restrict__ ids, int R, int E, int* __restrict__ counts, int* __restrict__ grp_start,
+                int* __restrict__ tile_start, int* __restrict__ fill, int* __restrict__ perm, int* __restrict__ rpos) {
+  __shared__ int cnt[kRouteMaxExperts];  // counts, then grp_start, then the block's next row per expert
+  __shared__ int mine[kRouteMaxExperts];  // the block's routes per expert
+  const int t = threadIdx.x;
+  const int r0 = blockIdx.x * kRouteBlock;
+  for (int q = t; q < E; q += 1024) {
+    cnt[q] = counts[q];
+    mine[q] = 0;
+  }
+  __syncthreads();
+  route_prefix(cnt, E, blockIdx.x == 0, counts, grp_start, tile_start);
+  int ex[kRouteBlock / 1024];
+#pragma unroll
+  for (int i = 0; i < kRouteBlock / 1024; ++i) {
+    ex[i] = route_expert(ids, r0 + t + 1024 * i, R, E);
+    if (ex[i] >= 0) atomicAdd(&mine[ex[i]], 1);
+  }
+  __syncthreads();
+  for (int q = t; q < E; q += 1024)
+    if (mine[q]) cnt[q] += atomicAdd(&fill[q], mine[q]);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRouteBlock / 1024; ++i) {
+    if (ex[i] < 0) continue;
+    const int r = r0 + t + 1024 * i;
+    const int p = atomicAdd(&cnt[ex[i]], 1);
+    perm[p] = r;
+    rpos[r] = p;
   }
 }
 
@@ -508,8 +593,17 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   // m-tiles: at most one partial tile per expert beyond R / 128 full ones
   const unsigned mt = (unsigned)((R + kGemmBM - 1) / kGemmBM + L.E);
   if (phases & 5) {
-    hipLaunchKernelGGL((route_build<IdT>), dim3(L.E), dim3(1024), 0, st, ids, R, L.E, counts, grp_start,
-                       tile_start, perm, rpos);
+    if (R <= kRouteBlock) {
+      hipLaunchKernelGGL((route_one<IdT>), dim3(1), dim3(1024), 0, st, ids, R, L.E, counts, grp_start, tile_start,
+                         perm, rpos);
+    } else {
+      int* fill = (int*)(ws + W.fill);
+      const unsigned nb = (unsigned)((R + kRouteBlock - 1) / kRouteBlock);
+      hipLaunchKernelGGL(route_zero, dim3((L.E + 255) / 256), dim3(256), 0, st, L.E, counts, fill);
+      hipLaunchKernelGGL((route_count<IdT>), dim3(nb), dim3(1024), 0, st, ids, R, L.E, counts);
+      hipLaunchKernelGGL((route_place<IdT>), dim3(nb), dim3(1024), 0, st, ids, R, L.E, counts, grp_start,
+                         tile_start, fill, perm, rpos);
+    }
   }
   const unsigned grid1 = grid8((int64_t)mt * fc1_blocks(L)), grid2 = grid8((int64_t)mt * fc2_blocks(L));
   if ((phases & 1) && a8) {

@@ -29,7 +29,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 256 * 1024 * 1024  # bench.py --copy-probe: bytes read and written per dispatch
 # (more specific names first: a kernel is named by the first entry its symbol contains)
 KERNELS = ("fc1_kernel", "fc2_kernel", "fc1_gemm_a8", "fc2_gemm_a8", "mxfp8_quantize", "fc1_gemm", "fc2_gemm",
-           "route_build", "combine")
+           "route_one", "route_count", "route_place", "route_zero", "combine")
 
 
 # HIP sources each kernel is built from: a summary stays valid while their
@@ -38,7 +38,8 @@ _DECODE_SRC = ("decode_path.hip", "decode_path.h", "decode.h", "act.h", "layout.
 _GROUPED_SRC = ("prefill.hip", "prefill.h", "gemm_util.h", "decode.h", "act.h", "layout.h")
 _A8_SRC = ("prefill_a8.hip", "prefill.h", "gemm_util.h", "mxfp8.h", "act.h", "layout.h")
 SOURCES = {"fc1_kernel": _DECODE_SRC, "fc2_kernel": _DECODE_SRC, "fc1_gemm": _GROUPED_SRC,
-           "fc2_gemm": _GROUPED_SRC, "route_build": _GROUPED_SRC, "combine": _GROUPED_SRC,
+           "fc2_gemm": _GROUPED_SRC, "route_one": _GROUPED_SRC, "route_count": _GROUPED_SRC,
+           "route_place": _GROUPED_SRC, "route_zero": _GROUPED_SRC, "combine": _GROUPED_SRC,
            "fc1_gemm_a8": _A8_SRC, "fc2_gemm_a8": _A8_SRC, "mxfp8_quantize": ("mxfp8.hip", "mxfp8.h")}
 
 
