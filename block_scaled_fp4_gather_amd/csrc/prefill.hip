@@ -244,16 +244,18 @@ __device__ __forceinline__ bf16x8_t lds_frag(const __bf16* p) {
   return __builtin_bit_cast(bf16x8_t, *(const u32x4*)p);
 }
 
-// LDS of a grouped GEMM workgroup: an A ring of 2 slots x 128 rows x 128
+// LDS of a grouped GEMM workgroup: an A ring of 3 slots x 128 rows x 128
 // bytes (64 bf16 per row, unpadded; the 16-byte chunk c of row r sits at
 // position c ^ swz(r)), and a weight ring of 3 slots x 4 waves x (2 x 1 KiB
-// codes + 2 x 256 B scales).
+// codes + 2 x 256 B scales): 78 KiB, two workgroups per CU.
 constexpr int kARow = kBK * 2;                    // bytes of one A row of a step
 constexpr int kAPlane = kGemmBM * kARow;          // 16 KiB
 constexpr int kBWave = 2 * 1024 + 2 * 256;        // one wave's weights of a step
 constexpr int kBSlot = 4 * kBWave;
 constexpr int kBSlots = 3;
-constexpr int kGemmLds = 2 * kAPlane + kBSlots * kBSlot;
+constexpr int kASlots = 3;
+constexpr int kADist = kASlots - 1;  // steps ahead that A is copied (the weights: kBSlots - 1)
+constexpr int kGemmLds = kASlots * kAPlane + kBSlots * kBSlot;
 
 // Grouped GEMM main loop for one 128-row x 256-column output tile, followed
 // by `epilogue(acc)`.  K runs over nU units of 32 values in steps of two; unit
@@ -272,30 +274,35 @@ constexpr int kGemmLds = 2 * kAPlane + kBSlots * kBSlot;
 // 4h + q of its A row.
 //
 // A rows (bf16, K contiguous; pass p at `plane` elements past pass 0) are
-// copied into the A ring one step ahead: wave w copies rows 32w..32w+31,
-// eight rows (1 KiB) per copy, from `rowp[blk]` (row 32w + 8 blk + lane / 8).
-// Per step: wait until this step's copies have landed, one barrier, then
-// widen and multiply, with the copies of A for step s + 1 and of the weights
-// for step s + 2 issued between the MFMA groups (each copy occupies the
-// address unit for a while; issued between MFMAs that wait hides behind
-// them).  Copies past the last step are clamped to it (never used); with an
+// copied into the A ring two steps ahead: wave w copies rows 32w..32w+31
+// (block w), eight rows (1 KiB) per copy, from `rowp[blk]` (row
+// 32w + 8 blk + lane / 8), when the tile has rows in that block (CPA; the
+// A reads of a wave never go past the tile's last block).  Per step: wait
+// until this wave's copies for the step have landed, one barrier, then widen
+// and multiply, with the copies of A and of the weights for step s + 2
+// issued between the MFMA groups (each copy occupies the address unit for a
+// while; issued between MFMAs that wait hides behind them).  A copy can take
+// longer to land than a step's MFMAs take to run: with A copied one step
+// ahead, tiles with few rows waited for it every step.  Copies past the last step are clamped to it (never used); with an
 // odd number of units the last step's second half (A and B both) is zeroed
 // when read.
-template <int FMT, int NB, typename Epilogue>
+template <int FMT, int NB, bool CPA, typename Epilogue>
 __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int64_t plane, int nU,
                                           const uint8_t* __restrict__ btile, int nC, uint8_t* smem,
                                           Epilogue&& epilogue) {
   constexpr int SPD = FMT == kMXFP4 ? 4 : 2;
   constexpr int NBA = NB > 0 ? NB : 1;
-  // copies this wave has in flight after issuing a step's: the weights of s + 2
-  constexpr int BCOPIES = NB > 0 ? 4 : 0;
+  // copies of later steps in flight when step s starts: those issued in the
+  // steps s - kADist + 1 .. s - 1 (4 for A, 4 more for the weights)
+  static_assert(kADist == kBSlots - 1, "A and the weights are copied the same number of steps ahead");
+  constexpr int BCOPIES = (kADist - 1) * ((CPA ? 4 : 0) + (NB > 0 ? 4 : 0));
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int nsteps = (nU + 1) / 2;
   const int full = nU / 2;
   uint8_t* const aring = smem;
-  uint8_t* const bring = smem + 2 * kAPlane + wave * kBWave;
+  uint8_t* const bring = smem + kASlots * kAPlane + wave * kBWave;
 
   f32x16_t acc[NBA][2];
 #pragma unroll
@@ -317,7 +324,7 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
     const int sc = s < nsteps ? s : nsteps - 1;
     const int c = cp_lo ^ (blk & 1);
     const uint8_t* g = (const uint8_t*)rowp[blk] + a_unit(2 * sc + (c >> 2)) + (c & 3) * 16;
-    dma16(g, lds_addr(aring + (s & 1) * kAPlane + (32 * wave + 8 * blk) * kARow));
+    dma16(g, lds_addr(aring + (s % kASlots) * kAPlane + (32 * wave + 8 * blk) * kARow));
   };
   // chunk of this lane's weight unit in step s (clamped; within its pass)
   auto b_chunk = [&](int s) {
@@ -333,16 +340,17 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
     dma4(btile + (int64_t)nC * 1024 + (cc / SPD) * 256 + row * 4, lds_addr(slot + 2048 + j * 256));
   };
   // Copies of a step, always issued in this order (vm_wait counts on it):
-  // copies 0..3 are A blocks for step s + 1, copies 4 and 5 the weight
-  // halves for step s + 2.
+  // copies 0..3 are A blocks for step s + 2 (none without CPA), copies 4 and
+  // 5 the weight halves for the same step.
   constexpr int NCOPY = NB > 0 ? 6 : 4;
   constexpr int NGROUP = 4 * NB;                             // MFMA groups of a step
   constexpr int NPRE = NCOPY > NGROUP ? NCOPY - NGROUP : 0;  // copies issued before them
   auto copy = [&](int s, int ci) {
-    if (ci < 4)
-      copy_a(s + 1, ci);
-    else
-      copy_b(s + 2, ci - 4);
+    if (ci < 4) {
+      if constexpr (CPA) copy_a(s + kADist, ci);
+    } else {
+      copy_b(s + kADist, ci - 4);
+    }
   };
   auto widen = [&](int s, bool tail, bf16x8_t (&bf)[4][2]) {
     const uint8_t* slot = bring + (s % kBSlots) * kBSlot;
@@ -357,7 +365,7 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
     }
   };
   auto mfmas = [&](int s, bool tail, const bf16x8_t (&bf)[4][2]) {
-    const uint8_t* slot = aring + (s & 1) * kAPlane;
+    const uint8_t* slot = aring + (s % kASlots) * kAPlane;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -385,13 +393,17 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
     }
   };
 
+  // the first kADist steps' copies, step by step in the same order
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) copy_a(0, blk);
-  if constexpr (NB > 0) {
-    copy_b(0, 0);
-    copy_b(0, 1);
-    copy_b(1, 0);
-    copy_b(1, 1);
+  for (int s = 0; s < kADist; ++s) {
+    if constexpr (CPA) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) copy_a(s, blk);
+    }
+    if constexpr (NB > 0) {
+      copy_b(s, 0);
+      copy_b(s, 1);
+    }
   }
   for (int s = 0; s < full; ++s) step(s, false);
   if (full < nsteps) step(full, true);
@@ -401,22 +413,37 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
 }
 
 // gemm_main with NB = the number of 32-row blocks holding the tile's rows
-// (0 when the wave has no weight tile).  Each variant carries its own copy
-// of the epilogue, called with the NB x 2 accumulator blocks.
+// (0 when the wave has no weight tile); the wave copies its A block when the
+// tile has rows in it.  Each variant carries its own copy of the epilogue,
+// called with the NB x 2 accumulator blocks.
 template <int FMT, typename Epilogue>
 __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp)[4], int64_t plane, int nU,
                                           const uint8_t* __restrict__ btile, bool bok, int nC,
                                           uint8_t* smem, Epilogue&& ep) {
-  if (!bok)
-    gemm_main<FMT, 0>(rowp, plane, nU, btile, nC, smem, ep);
-  else if (rows > 96)
-    gemm_main<FMT, 4>(rowp, plane, nU, btile, nC, smem, ep);
-  else if (rows > 64)
-    gemm_main<FMT, 3>(rowp, plane, nU, btile, nC, smem, ep);
-  else if (rows > 32)
-    gemm_main<FMT, 2>(rowp, plane, nU, btile, nC, smem, ep);
-  else
-    gemm_main<FMT, 1>(rowp, plane, nU, btile, nC, smem, ep);
+  const bool cpa = 32 * (threadIdx.x >> 6) < rows;
+  if (!bok) {
+    if (cpa)
+      gemm_main<FMT, 0, true>(rowp, plane, nU, btile, nC, smem, ep);
+    else
+      gemm_main<FMT, 0, false>(rowp, plane, nU, btile, nC, smem, ep);
+  } else if (rows > 96) {
+    gemm_main<FMT, 4, true>(rowp, plane, nU, btile, nC, smem, ep);
+  } else if (rows > 64) {
+    if (cpa)
+      gemm_main<FMT, 3, true>(rowp, plane, nU, btile, nC, smem, ep);
+    else
+      gemm_main<FMT, 3, false>(rowp, plane, nU, btile, nC, smem, ep);
+  } else if (rows > 32) {
+    if (cpa)
+      gemm_main<FMT, 2, true>(rowp, plane, nU, btile, nC, smem, ep);
+    else
+      gemm_main<FMT, 2, false>(rowp, plane, nU, btile, nC, smem, ep);
+  } else {
+    if (cpa)
+      gemm_main<FMT, 1, true>(rowp, plane, nU, btile, nC, smem, ep);
+    else
+      gemm_main<FMT, 1, false>(rowp, plane, nU, btile, nC, smem, ep);
+  }
 }
 
 template <int FMT>
@@ -449,9 +476,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
   const int n = 32 * b + (lane & 31);
   // a = f(gate, up) as hi/lo bf16 planes; a non-gated activation (relu2)
   // writes both halves as outputs, at columns n and Ip + n.
-  auto epilogue = [&](auto& acc) {
+  auto epilogue = [&](auto& acc) __attribute__((always_inline)) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
-    with_act_kind(L.act.kind, [&](auto kind) {
+    with_act_kind(L.act.kind, [&](auto kind) __attribute__((always_inline)) {
       constexpr int K = decltype(kind)::value;
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
@@ -501,7 +528,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
   const bool bok = hb < L.nB2;
   if (t < kGemmBM) wrow[t] = t < rows ? tw[perm[gs + t]] : 0.0f;
   const float g2 = FMT == kNVFP4 ? ((const float*)prep)[L.E + e] : 1.0f;
-  auto epilogue = [&](auto& acc) {
+  auto epilogue = [&](auto& acc) __attribute__((always_inline)) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
