@@ -19,13 +19,14 @@ struct PrefillWs {
   int64_t fill;        // int32 [E]   grouped rows handed out per expert (routing)
   int64_t perm;        // int32 [R]   grouped row -> route index t*k + j
   int64_t rpos;        // int32 [R]   route index -> grouped row (valid routes)
-  // bf16 activations:
-  int64_t act;         // bf16 [2][R][I] SiLU(gate)*up per grouped row: hi plane, then
-                       // lo plane (hi = bf16(a), lo = bf16(a - hi): 16 significant bits)
+  // bf16 activations a = SiLU(gate)*up per grouped row, hi = bf16(a) and
+  // lo = a - hi:
+  int64_t act;         // bf16 [R][I] hi plane; NVFP4: then bf16 [R][I] lo = bf16(a - hi)
+                       // (16 significant bits); MXFP4: lo as MXFP8 in aq / as
   // MXFP8 activations (W4A8-MX; scale rows padded to whole dwords):
   int64_t xq;          // u8 [M][H]  x codes per token
   int64_t xs;          // u8 [M][a8_scale_stride(H)]  x scales
-  int64_t aq;          // u8 [R][I]  SiLU(gate)*up codes per grouped row
+  int64_t aq;          // u8 [R][I]  SiLU(gate)*up codes per grouped row (MXFP4 bf16: lo codes)
   int64_t as;          // u8 [R][a8_scale_stride(I)]  their scales
   int64_t y;           // fp32 [R][H] router-weighted FC2 output per grouped row
   int64_t total;
@@ -53,7 +54,12 @@ inline PrefillWs prefill_ws(const Layout& L, int64_t routes, int64_t tokens, boo
     w.aq = w.xs + align_up(tokens * a8_scale_stride(L.H), 256);
     w.as = w.aq + align_up(routes * L.I, 256);
     o = w.as + align_up(routes * a8_scale_stride(L.I), 256);
+  } else if (L.fmt == kMXFP4) {
+    w.aq = w.act + align_up(2 * routes * L.I, 256);
+    w.as = w.aq + align_up(routes * L.I, 256);
+    o = w.as + align_up(routes * a8_scale_stride(L.I), 256);
   } else {
+    w.aq = w.as = w.act + align_up(2 * routes * L.I, 256);
     o = w.act + 2 * align_up(2 * routes * L.I, 256);
   }
   w.y = o;

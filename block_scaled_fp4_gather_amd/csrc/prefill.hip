@@ -27,6 +27,7 @@
 #include "decode.h"
 #include "gemm_util.h"
 #include "layout.h"
+#include "mxfp8.h"
 #include "prefill.h"
 
 namespace moe {
@@ -446,12 +447,232 @@ __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp
   }
 }
 
+// LDS of the MXFP4 FC2 workgroup, whose activations are a bf16 hi plane and
+// an MXFP8 lo part: the A ring of gemm_main in 2 slots; an A lo ring of 2
+// slots x 128 rows x 64 bytes (the 64 FP8 values of a step; 16-byte chunk c
+// of row r at position c ^ lo_swz(r)); an A lo scale ring of 2 slots x 4
+// waves x 256 bytes (one dword of 4 unit scales per row, rows 32w..32w+31;
+// the upper 128 bytes are spare); a weight ring of 3 slots x 4 waves x
+// (2 x 1 KiB codes + 256 B: the scale dword of each of the 64 weight rows,
+// which covers both units of a step): 77 KiB, two workgroups per CU.
+constexpr int kLoRow = 64;
+constexpr int kLoPlane = kGemmBM * kLoRow;  // 8 KiB
+constexpr int kLoScale = 4 * 256;
+constexpr int kBWaveHl = 2 * 1024 + 256;
+constexpr int kBSlotHl = 4 * kBWaveHl;
+constexpr int kHlLds = 2 * kAPlane + 2 * kLoPlane + 2 * kLoScale + kBSlots * kBSlotHl;
+
+__device__ __forceinline__ int lo_swz(int r) { return (r >> 1) & 3; }
+
+// FC2 main loop of MXFP4 layers for one 128-row x 256-column output tile,
+// followed by `epilogue(acc)`: one pass over the nU units of K (= I / 32) in
+// steps of two.  A step multiplies the hi plane as gemm_main does (bf16
+// MFMAs on the widened weight unit) and the lo part with two
+// v_mfma_scale_f32_32x32x64_f8f6f4 per row block, which take the same FP4
+// weight unit and its UE8M0 byte as they are stored (lane c + 32h: column
+// c's unit 2s + h) and the lo codes (lane r + 32h: bytes 16h..16h+15 of row
+// r's unit 2s, then the same bytes of unit 2s + 1, and the scale of unit
+// 2s + h).  So the weights are copied and widened once for both parts, and
+// the lo part runs at the FP8 rate with no widening.
+//
+// Copies (wave w, when the tile has rows in block w: CPA): hi rows as in
+// gemm_main and lo rows (16 rows of 64 bytes per copy, from `lrowp[blk]`,
+// row 32w + 16 blk + lane / 4) and the lo scale dword of row 32w + lane % 32
+// (from `srow`), one step ahead; the wave's weights (two code halves and
+// one copy of the 64 rows' scale dwords) two steps ahead.  With an odd
+// number of units the last step's second unit is zeroed when read (lo codes
+// and weights zero, scales 1).
+template <int NB, bool CPA, typename Epilogue>
+__device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], const uint8_t* const (&lrowp)[2],
+                                             const uint8_t* srow, int nU, const uint8_t* __restrict__ btile,
+                                             uint8_t* smem, Epilogue&& epilogue) {
+  constexpr int NBA = NB > 0 ? NB : 1;
+  constexpr int NA = CPA ? 7 : 0;       // copies of A per step: 4 hi, 2 lo, 1 lo scale
+  constexpr int NW = NB > 0 ? 3 : 0;    // copies of weights per step
+  constexpr int NCOPY = NA + NW;
+  constexpr int NGROUP = 5 * NB;                             // MFMA groups of a step (4 hi, 1 lo per block)
+  constexpr int NPRE = NCOPY > NGROUP ? NCOPY - NGROUP : 0;  // copies issued before them
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int n = lane & 31, h = lane >> 5;
+  const int nsteps = (nU + 1) / 2;
+  const int full = nU / 2;
+  uint8_t* const ahi = smem;
+  uint8_t* const alo = smem + 2 * kAPlane;
+  uint8_t* const asc = alo + 2 * kLoPlane;
+  uint8_t* const bring = asc + 2 * kLoScale + wave * kBWaveHl;
+
+  f32x16_t acc[NBA][2];
+#pragma unroll
+  for (int i = 0; i < NBA; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+
+  const int cp_lo = (lane & 7) ^ (lane >> 3);
+  const int swz = a_swz(n);
+  const int lsw = lo_swz(n);
+  auto copy_hi = [&](int s, int blk) {
+    const int sc = min(s, nsteps - 1);
+    const int c = cp_lo ^ (blk & 1);
+    const int u = min(2 * sc + (c >> 2), nU - 1);
+    dma16((const uint8_t*)rowp[blk] + u * 64 + (c & 3) * 16,
+          lds_addr(ahi + (s & 1) * kAPlane + (32 * wave + 8 * blk) * kARow));
+  };
+  auto copy_lo = [&](int s, int blk) {
+    const int sc = min(s, nsteps - 1);
+    const int c = (lane & 3) ^ ((lane >> 3) & 3);  // lane l writes position l % 4 of row l / 4
+    const int u = min(2 * sc + (c >> 1), nU - 1);
+    dma16(lrowp[blk] + u * 32 + (c & 1) * 16, lds_addr(alo + (s & 1) * kLoPlane + (32 * wave + 16 * blk) * kLoRow));
+  };
+  auto copy_ls = [&](int s) {
+    const int sc = min(s, nsteps - 1);
+    dma4(srow + 4 * (sc / 2), lds_addr(asc + (s & 1) * kLoScale + wave * 256));
+  };
+  auto b_unit = [&](int s) { return min(2 * s + h, nU - 1); };
+  auto copy_b = [&](int s, int j) {
+    const int cc = b_unit(min(s, nsteps - 1));
+    dma16(btile + (int64_t)cc * 1024 + (32 * j + n) * 16, lds_addr(bring + (s % kBSlots) * kBSlotHl + j * 1024));
+  };
+  auto copy_bs = [&](int s) {
+    const int cw = min(2 * min(s, nsteps - 1), nU - 1);
+    dma4(btile + (int64_t)nU * 1024 + (cw / 4) * 256 + lane * 4, lds_addr(bring + (s % kBSlots) * kBSlotHl + 2048));
+  };
+  // Copies of a step, always issued in this order (vm_wait counts on it):
+  // with CPA, 4 hi blocks, 2 lo blocks and the lo scales for step s + 1;
+  // then (waves with a weight tile) the 2 code halves and the scale dwords
+  // for step s + 2.
+  auto copy = [&](int s, int ci) {
+    if (CPA && ci < 4)
+      copy_hi(s + 1, ci);
+    else if (CPA && ci < 6)
+      copy_lo(s + 1, ci - 4);
+    else if (CPA && ci == 6)
+      copy_ls(s + 1);
+    else if (ci - NA < 2)
+      copy_b(s + 2, ci - NA);
+    else
+      copy_bs(s + 2);
+  };
+  auto step = [&](int s, bool tail) {
+    vm_wait<NW>();    // this wave's copies for step s have landed (the weights of s + 1 may not)
+    __syncthreads();  // everyone's have; everyone is done with step s - 1
+#pragma unroll
+    for (int ci = 0; ci < NPRE; ++ci) copy(s, ci);
+    if constexpr (NB > 0) {
+      const uint8_t* bs = bring + (s % kBSlots) * kBSlotHl;
+      const uint8_t* hs = ahi + (s & 1) * kAPlane;
+      const uint8_t* ls = alo + (s & 1) * kLoPlane;
+      const uint8_t* ss = asc + (s & 1) * kLoScale;
+      const int c = b_unit(s);
+      const bool z = tail && h;
+      u32x4 w[2];
+      uint32_t sw[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        w[j] = *(const u32x4*)(bs + j * 1024 + lane * 16);
+        sw[j] = *(const uint32_t*)(bs + 2048 + (32 * j + n) * 4);
+      }
+      int ci = NPRE;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        bf16x8_t bf[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bf[j] = z ? bf16x8_t{} : b_frag<kMXFP4>(w[j][q], b_scale<kMXFP4>(sw[j], c, q));
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          bf16x8_t af = lds_frag((const __bf16*)(hs + (i * 32 + n) * kARow + (((4 * h + q) ^ swz) * 16)));
+          if (z) af = bf16x8_t{};
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[j], acc[i][j], 0, 0, 0);
+          if (ci < NCOPY) copy(s, ci++);
+        }
+      }
+      i32x8_t bop[2];
+      int sb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bop[j] = z ? i32x8_t{} : i32x8_t{(int)w[j][0], (int)w[j][1], (int)w[j][2], (int)w[j][3], 0, 0, 0, 0};
+        sb[j] = z ? 127 : (int)((sw[j] >> (8 * (c & 3))) & 0xFFu);
+      }
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const uint8_t* lr = ls + (i * 32 + n) * kLoRow;
+        const i32x4_t a0 = *(const i32x4_t*)(lr + ((h ^ lsw) * 16));
+        i32x4_t a1 = *(const i32x4_t*)(lr + (((2 + h) ^ lsw) * 16));
+        if (tail) a1 = i32x4_t{};
+        const i32x8_t aop = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        const uint32_t asw = *(const uint32_t*)(ss + i * 256 + n * 4);
+        const int sa = z ? 127 : (int)((asw >> (8 * ((2 * s + h) & 3))) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, sa, 0, sb[j]);
+        if (ci < NCOPY) copy(s, ci++);
+      }
+      while (ci < NCOPY) copy(s, ci++);
+    }
+  };
+
+  if constexpr (CPA) {
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) copy_hi(0, blk);
+    copy_lo(0, 0);
+    copy_lo(0, 1);
+    copy_ls(0);
+  }
+  if constexpr (NB > 0) {
+    copy_b(0, 0);
+    copy_b(0, 1);
+    copy_bs(0);
+    copy_b(1, 0);
+    copy_b(1, 1);
+    copy_bs(1);
+  }
+  for (int s = 0; s < full; ++s) step(s, false);
+  if (full < nsteps) step(full, true);
+  vm_wait<0>();  // no copy may land after the workgroup's LDS is released
+  __syncthreads();
+  if constexpr (NB > 0) epilogue(acc);
+}
+
+template <typename Epilogue>
+__device__ __forceinline__ void gemm_rows_hl(int rows, const uint16_t* const (&rowp)[4],
+                                             const uint8_t* const (&lrowp)[2], const uint8_t* srow, int nU,
+                                             const uint8_t* __restrict__ btile, bool bok, uint8_t* smem,
+                                             Epilogue&& ep) {
+  const bool cpa = 32 * (threadIdx.x >> 6) < rows;
+  if (!bok) {
+    if (cpa)
+      gemm_main_hl<0, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+    else
+      gemm_main_hl<0, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+  } else if (rows > 96) {
+    gemm_main_hl<4, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+  } else if (rows > 64) {
+    if (cpa)
+      gemm_main_hl<3, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+    else
+      gemm_main_hl<3, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+  } else if (rows > 32) {
+    if (cpa)
+      gemm_main_hl<2, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+    else
+      gemm_main_hl<2, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+  } else {
+    if (cpa)
+      gemm_main_hl<1, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+    else
+      gemm_main_hl<1, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+  }
+}
+
 template <int FMT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     fc1_gemm(const uint8_t* __restrict__ prep, const Layout L, const uint16_t* __restrict__ x, int k,
              const int* __restrict__ counts, const int* __restrict__ grp_start,
              const int* __restrict__ tile_start, const int* __restrict__ perm,
-             uint16_t* __restrict__ act, int64_t plane) {
+             uint16_t* __restrict__ act, int64_t plane, uint8_t* __restrict__ aq, uint8_t* __restrict__ as,
+             int ass) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
   const GroupTile id = group_tile(fc1_blocks(L), tile_start, L.E);
   if (!id.ok) return;
@@ -474,10 +695,77 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
   }
   const float g13 = FMT == kNVFP4 ? ((const float*)prep)[e] : 1.0f;
   const int n = 32 * b + (lane & 31);
-  // a = f(gate, up) as hi/lo bf16 planes; a non-gated activation (relu2)
-  // writes both halves as outputs, at columns n and Ip + n.
+  // a = f(gate, up) as hi/lo planes; a non-gated activation (relu2) writes
+  // both halves as outputs, at columns n and Ip + n.  NVFP4: hi = bf16(a)
+  // and lo = bf16(a - hi), two bf16 planes.  MXFP4: the hi plane, and lo =
+  // a - hi as MXFP8 (codes `aq`, scale rows `as` of `ass` bytes): per 32-row
+  // block the lo values go to this wave's part of the (now idle) A ring as
+  // 32 rows x 32 columns (row stride 144 B); lane l then takes row l / 2,
+  // columns 16 (l % 2) .. + 15, whose block of 32 is its own 16 values and
+  // its neighbour's, and stores its 16 codes at once.
+  auto epilogue_mx = [&](auto& acc) __attribute__((always_inline)) {
+    constexpr int NB = sizeof(acc) / sizeof(acc[0]);
+    constexpr int kStride = 36;  // dwords per staged row
+    float* st = (float*)(smem + wave * 32 * kStride * 4);
+    const int rr = lane >> 1, half = lane & 1;
+    with_act_kind(L.act.kind, [&](auto kind) __attribute__((always_inline)) {
+      constexpr int K = decltype(kind)::value;
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+#pragma unroll
+        for (int jj = 0; jj < (K == kActRelu2 ? 2 : 1); ++jj) {
+          const int col0 = jj ? L.Ip : 0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + acc_row(r, lane);
+            const float a = K == kActRelu2 && jj ? act_of<K>(L.act, acc[i][1][r], 0.0f)
+                                                 : act_of<K>(L.act, acc[i][0][r], acc[i][1][r]);
+            const uint16_t hi = f32_to_bf16_rne(a);
+            if (row < rows) act[(int64_t)(gs + row) * L.I + col0 + n] = hi;
+            st[acc_row(r, lane) * kStride + (lane & 31)] = a - __uint_as_float((uint32_t)hi << 16);
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging stores are done
+          __builtin_amdgcn_wave_barrier();
+          float v[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 f = *(const float4*)(st + rr * kStride + 16 * half + 4 * q);
+            v[4 * q] = f.x;
+            v[4 * q + 1] = f.y;
+            v[4 * q + 2] = f.z;
+            v[4 * q + 3] = f.w;
+          }
+          uint32_t m = 0;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) m = max(m, __float_as_uint(v[q]) & 0x7FFFFFFFu);
+          m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+          const uint32_t sb = mx_scale_byte(m);
+          uint32_t w[4] = {0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+          if (sb != 255u) {
+            const float inv = mx_inv_scale(sb);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              w[q] = e4m3_code(v[4 * q] * inv) | (e4m3_code(v[4 * q + 1] * inv) << 8) |
+                     (e4m3_code(v[4 * q + 2] * inv) << 16) | (e4m3_code(v[4 * q + 3] * inv) << 24);
+          }
+          const int row = i * 32 + rr;
+          const int c0 = col0 + 32 * b;
+          if (row < rows) {
+            *(uint4*)(aq + (int64_t)(gs + row) * L.I + c0 + 16 * half) = make_uint4(w[0], w[1], w[2], w[3]);
+            if (half == 0) as[(int64_t)(gs + row) * ass + c0 / 32] = (uint8_t)sb;
+          }
+          __builtin_amdgcn_wave_barrier();  // the next block's staging stores come after these reads
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+        }
+      }
+    });
+  };
   auto epilogue = [&](auto& acc) __attribute__((always_inline)) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
+    if constexpr (FMT == kMXFP4) {
+      epilogue_mx(acc);
+      return;
+    }
     with_act_kind(L.act.kind, [&](auto kind) __attribute__((always_inline)) {
       constexpr int K = decltype(kind)::value;
 #pragma unroll
@@ -513,8 +801,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     fc2_gemm(const uint8_t* __restrict__ prep, const Layout L, const float* __restrict__ tw,
              const int* __restrict__ counts, const int* __restrict__ grp_start,
              const int* __restrict__ tile_start, const int* __restrict__ perm,
-             const uint16_t* __restrict__ act, int64_t plane, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
+             const uint16_t* __restrict__ act, int64_t plane, const uint8_t* __restrict__ aq,
+             const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kHlLds : kGemmLds];
   __shared__ float wrow[kGemmBM];
   const GroupTile id = group_tile(fc2_blocks(L), tile_start, L.E);
   if (!id.ok) return;
@@ -546,13 +835,26 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
       }
     }
   };
+  // hi rows this lane copies: rows 32 wave + 8 blk + lane / 8 of the tile
+  // (grouped rows past the tile repeat its last row)
   const uint16_t* rowp[4];
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk)
     rowp[blk] = act + (int64_t)(gs + min(32 * wave + 8 * blk + (lane >> 3), rows - 1)) * L.I;
-  // two passes over K: the hi activation plane, then the lo plane
-  gemm_rows<FMT>(rows, rowp, plane, 2 * L.nC2, prep + fc2_tile_offset(L, e, bok ? hb : 0), bok, L.nC2, smem,
-                 epilogue);
+  const uint8_t* btile = prep + fc2_tile_offset(L, e, bok ? hb : 0);
+  if constexpr (FMT == kMXFP4) {
+    // one pass: the hi plane and the MXFP8 lo codes (rows 32 wave + 16 blk +
+    // lane / 4) with their scale rows (row 32 wave + lane % 32)
+    const uint8_t* lrowp[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+      lrowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
+    const uint8_t* srow = as + (int64_t)(gs + min(32 * wave + (lane & 31), rows - 1)) * ass;
+    gemm_rows_hl(rows, rowp, lrowp, srow, L.nC2, btile, bok, smem, epilogue);
+  } else {
+    // two passes over K: the hi activation plane, then the lo plane
+    gemm_rows<FMT>(rows, rowp, plane, 2 * L.nC2, btile, bok, L.nC2, smem, epilogue);
+  }
 }
 
 // out[t][h] = bf16(sum over valid routes j of token t, in route order, of
@@ -615,7 +917,10 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   int* perm = (int*)(ws + W.perm);
   int* rpos = (int*)(ws + W.rpos);
   uint16_t* act = (uint16_t*)(ws + W.act);
-  const int64_t plane = (W.y - W.act) / 4;  // elements from the hi plane to the lo plane
+  const int64_t plane = (W.aq - W.act) / 2;  // elements from the hi plane to the lo plane (NVFP4)
+  uint8_t* aq = ws + W.aq;                   // MXFP4: the lo part as MXFP8
+  uint8_t* as = ws + W.as;
+  const int ass = a8_scale_stride(L.I);
   float* y = (float*)(ws + W.y);
   // m-tiles: at most one partial tile per expert beyond R / 128 full ones
   const unsigned mt = (unsigned)((R + kGemmBM - 1) / kGemmBM + L.E);
@@ -639,7 +944,7 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   } else if (phases & 1) {
     hipLaunchKernelGGL((fc1_gemm<FMT>), dim3(grid1), dim3(256), 0, st, prep, L, x, k,
                        (const int*)counts, (const int*)grp_start, (const int*)tile_start,
-                       (const int*)perm, act, plane);
+                       (const int*)perm, act, plane, aq, as, ass);
   }
   if ((phases & 2) && a8) {
     const hipError_t err = launch_fc2_a8(L, prep, tw, ws, W, grid2, st);
@@ -647,7 +952,8 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   } else if (phases & 2) {
     hipLaunchKernelGGL((fc2_gemm<FMT>), dim3(grid2), dim3(256), 0, st, prep, L, tw,
                        (const int*)counts, (const int*)grp_start, (const int*)tile_start,
-                       (const int*)perm, (const uint16_t*)act, plane, y);
+                       (const int*)perm, (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as,
+                       ass, y);
   }
   if (phases & 10) {
     hipLaunchKernelGGL((combine<IdT>), dim3(M, (L.H + 1023) / 1024), dim3(256), 0, st, ids, k, L.E, L.H,

@@ -30,9 +30,6 @@
 
 namespace moe {
 
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-
 // LDS of an A8 workgroup: A ring of 2 slots x 128 rows x 128 bytes (128 K
 // values of FP8, the 16-byte chunk c of row r at position c ^ swz(r)); A
 // scale ring of 2 slots x 4 waves x 256 bytes (rows 32w..32w+31 of the tile,
