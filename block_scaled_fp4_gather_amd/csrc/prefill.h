@@ -9,6 +9,7 @@
 namespace moe {
 
 constexpr int kGemmBM = 128;             // routes per m-tile of the grouped GEMMs
+constexpr int kSparseRoutesPerExpert = 16;  // up to this many routes per expert on average: 32-row m-tiles
 constexpr int kRouteMaxExperts = 8192;   // experts the grouping's LDS histogram holds
 
 // Workspace of the grouped path, byte offsets (256-byte aligned).
@@ -77,10 +78,20 @@ __host__ __device__ inline int fc1_blocks(const Layout& L) { return (L.nB1 + 3) 
 // FC2 column blocks: 4 prepared tiles (256 output columns) each.
 __host__ __device__ inline int fc2_blocks(const Layout& L) { return (L.nB2 + 3) / 4; }
 
-// Workgroups of the larger grouped GEMM grid for `routes` routes; the grid
-// must stay below 2^31 workgroups.
-inline int64_t prefill_max_workgroups(const Layout& L, int64_t routes) {
-  const int64_t mt = (routes + kGemmBM - 1) / kGemmBM + L.E;
+// Rows of the grouped GEMMs' m-tiles for `routes` routes: 128, or 32 when
+// the experts get few routes each (bf16 activations only), where most
+// 128-row tiles would hold a few rows and three smaller workgroups per CU
+// keep more weight copies in flight.
+inline int prefill_bm(const Layout& L, int64_t routes, bool a8) {
+  return !a8 && routes <= (int64_t)kSparseRoutesPerExpert * L.E ? 32 : kGemmBM;
+}
+
+// Workgroups of the larger grouped GEMM grid for up to `routes` routes (a
+// call with fewer routes may take 32-row tiles); the grid must stay below
+// 2^31 workgroups.
+inline int64_t prefill_max_workgroups(const Layout& L, int64_t routes, bool a8) {
+  const int64_t bm = a8 ? kGemmBM : 32;
+  const int64_t mt = (routes + bm - 1) / bm + L.E;
   const int64_t nb1 = (L.I + 63) / 64, nb2 = (L.H + 127) / 128;
   return mt * (nb1 > nb2 ? nb1 : nb2) + 8;
 }

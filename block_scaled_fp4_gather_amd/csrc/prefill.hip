@@ -54,11 +54,11 @@ constexpr int kRouteBlock = 4096;  // routes per workgroup of the routing kernel
 
 // Exclusive prefix over the E counters cnt (in LDS, E <= kRouteMaxExperts)
 // by the 1024 threads of a workgroup: counts[e], grp_start[e] and
-// tile_start[e] (m-tiles of kGemmBM rows; tile_start[E] the total) are
+// tile_start[e] (m-tiles of bm rows; tile_start[E] the total) are
 // written to global memory when `out` is set, and cnt[e] becomes
 // grp_start[e].  Ends with a barrier.
-__device__ void route_prefix(int* cnt, int E, bool out, int* __restrict__ counts, int* __restrict__ grp_start,
-                             int* __restrict__ tile_start) {
+__device__ void route_prefix(int* cnt, int E, int bm, bool out, int* __restrict__ counts,
+                             int* __restrict__ grp_start, int* __restrict__ tile_start) {
   __shared__ int wpart[2][16];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   constexpr int PER = kRouteMaxExperts / 1024;  // counters per thread
@@ -68,7 +68,7 @@ __device__ void route_prefix(int* cnt, int E, bool out, int* __restrict__ counts
   for (int i = 0; i < PER; ++i) {
     c[i] = e0 + i < E ? cnt[e0 + i] : 0;
     rsum += c[i];
-    tsum += (c[i] + kGemmBM - 1) / kGemmBM;
+    tsum += (c[i] + bm - 1) / bm;
   }
   // inclusive scans of the per-thread sums over the wave, then over the waves
   int ri = rsum, ti = tsum;
@@ -105,7 +105,7 @@ __device__ void route_prefix(int* cnt, int E, bool out, int* __restrict__ counts
       cnt[e] = rb;
     }
     rb += c[i];
-    tb += (c[i] + kGemmBM - 1) / kGemmBM;
+    tb += (c[i] + bm - 1) / bm;
   }
   if (out && t == 0) tile_start[E] = ttot;
   __syncthreads();
@@ -115,8 +115,9 @@ __device__ void route_prefix(int* cnt, int E, bool out, int* __restrict__ counts
 // its prefix, then every route takes its grouped row from an LDS counter.
 template <typename IdT>
 __global__ void __launch_bounds__(1024)
-    route_one(const IdT* __restrict__ ids, int R, int E, int* __restrict__ counts, int* __restrict__ grp_start,
-              int* __restrict__ tile_start, int* __restrict__ perm, int* __restrict__ rpos) {
+    route_one(const IdT* __restrict__ ids, int R, int E, int bm, int* __restrict__ counts,
+              int* __restrict__ grp_start, int* __restrict__ tile_start, int* __restrict__ perm,
+              int* __restrict__ rpos) {
   __shared__ int cnt[kRouteMaxExperts];
   const int t = threadIdx.x;
   for (int q = t; q < E; q += 1024) cnt[q] = 0;
@@ -128,7 +129,7 @@ __global__ void __launch_bounds__(1024)
     if (ex[i] >= 0) atomicAdd(&cnt[ex[i]], 1);
   }
   __syncthreads();
-  route_prefix(cnt, E, true, counts, grp_start, tile_start);
+  route_prefix(cnt, E, bm, true, counts, grp_start, tile_start);
 #pragma unroll
   for (int i = 0; i < kRouteBlock / 1024; ++i) {
     if (ex[i] < 0) continue;
@@ -172,8 +173,9 @@ __global__ void __launch_bounds__(1024)
 
 template <typename IdT>
 __global__ void __launch_bounds__(1024)
-    route_place(const IdT* __restrict__ ids, int R, int E, int* __restrict__ counts, int* __restrict__ grp_start,
-                int* __restrict__ tile_start, int* __restrict__ fill, int* __restrict__ perm, int* __restrict__ rpos) {
+    route_place(const IdT* __restrict__ ids, int R, int E, int bm, int* __restrict__ counts,
+                int* __restrict__ grp_start, int* __restrict__ tile_start, int* __restrict__ fill,
+                int* __restrict__ perm, int* __restrict__ rpos) {
   __shared__ int cnt[kRouteMaxExperts];  // counts, then grp_start, then the block's next row per expert
   __shared__ int mine[kRouteMaxExperts];  // the block's routes per expert
   const int t = threadIdx.x;
@@ -183,7 +185,7 @@ __global__ void __launch_bounds__(1024)
     mine[q] = 0;
   }
   __syncthreads();
-  route_prefix(cnt, E, blockIdx.x == 0, counts, grp_start, tile_start);
+  route_prefix(cnt, E, bm, blockIdx.x == 0, counts, grp_start, tile_start);
   int ex[kRouteBlock / 1024];
 #pragma unroll
   for (int i = 0; i < kRouteBlock / 1024; ++i) {
@@ -250,13 +252,15 @@ __device__ __forceinline__ bf16x8_t lds_frag(const __bf16* p) {
 // position c ^ swz(r)), and a weight ring of 3 slots x 4 waves x (2 x 1 KiB
 // codes + 2 x 256 B scales): 78 KiB, two workgroups per CU.
 constexpr int kARow = kBK * 2;                    // bytes of one A row of a step
-constexpr int kAPlane = kGemmBM * kARow;          // 16 KiB
+template <int BM>
+constexpr int kAPlane = BM * kARow;               // 16 KiB for 128 rows
 constexpr int kBWave = 2 * 1024 + 2 * 256;        // one wave's weights of a step
 constexpr int kBSlot = 4 * kBWave;
 constexpr int kBSlots = 3;
 constexpr int kASlots = 3;
 constexpr int kADist = kASlots - 1;  // steps ahead that A is copied (the weights: kBSlots - 1)
-constexpr int kGemmLds = kASlots * kAPlane + kBSlots * kBSlot;
+template <int BM>
+constexpr int kGemmLds = kASlots * kAPlane<BM> + kBSlots * kBSlot;
 
 // Grouped GEMM main loop for one 128-row x 256-column output tile, followed
 // by `epilogue(acc)`.  K runs over nU units of 32 values in steps of two; unit
@@ -287,7 +291,7 @@ constexpr int kGemmLds = kASlots * kAPlane + kBSlots * kBSlot;
 // ahead, tiles with few rows waited for it every step.  Copies past the last step are clamped to it (never used); with an
 // odd number of units the last step's second half (A and B both) is zeroed
 // when read.
-template <int FMT, int NB, bool CPA, typename Epilogue>
+template <int FMT, int BM, int NB, bool CPA, typename Epilogue>
 __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int64_t plane, int nU,
                                           const uint8_t* __restrict__ btile, int nC, uint8_t* smem,
                                           Epilogue&& epilogue) {
@@ -303,7 +307,7 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
   const int nsteps = (nU + 1) / 2;
   const int full = nU / 2;
   uint8_t* const aring = smem;
-  uint8_t* const bring = smem + kASlots * kAPlane + wave * kBWave;
+  uint8_t* const bring = smem + kASlots * kAPlane<BM> + wave * kBWave;
 
   f32x16_t acc[NBA][2];
 #pragma unroll
@@ -325,7 +329,7 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
     const int sc = s < nsteps ? s : nsteps - 1;
     const int c = cp_lo ^ (blk & 1);
     const uint8_t* g = (const uint8_t*)rowp[blk] + a_unit(2 * sc + (c >> 2)) + (c & 3) * 16;
-    dma16(g, lds_addr(aring + (s % kASlots) * kAPlane + (32 * wave + 8 * blk) * kARow));
+    dma16(g, lds_addr(aring + (s % kASlots) * kAPlane<BM> + (32 * wave + 8 * blk) * kARow));
   };
   // chunk of this lane's weight unit in step s (clamped; within its pass)
   auto b_chunk = [&](int s) {
@@ -366,7 +370,7 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
     }
   };
   auto mfmas = [&](int s, bool tail, const bf16x8_t (&bf)[4][2]) {
-    const uint8_t* slot = aring + (s % kASlots) * kAPlane;
+    const uint8_t* slot = aring + (s % kASlots) * kAPlane<BM>;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -415,35 +419,48 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
 
 // gemm_main with NB = the number of 32-row blocks holding the tile's rows
 // (0 when the wave has no weight tile); the wave copies its A block when the
-// tile has rows in it.  Each variant carries its own copy of the epilogue,
-// called with the NB x 2 accumulator blocks.
-template <int FMT, typename Epilogue>
+// tile has rows in it.  Tiles of BM = 32 rows have one block, copied by wave
+// 0.  Each variant carries its own copy of the epilogue, called with the
+// NB x 2 accumulator blocks.
+template <int FMT, int BM, typename Epilogue>
 __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp)[4], int64_t plane, int nU,
                                           const uint8_t* __restrict__ btile, bool bok, int nC,
                                           uint8_t* smem, Epilogue&& ep) {
   const bool cpa = 32 * (threadIdx.x >> 6) < rows;
-  if (!bok) {
+  if constexpr (BM == 32) {
+    if (!bok) {
+      if (cpa)
+        gemm_main<FMT, BM, 0, true>(rowp, plane, nU, btile, nC, smem, ep);
+      else
+        gemm_main<FMT, BM, 0, false>(rowp, plane, nU, btile, nC, smem, ep);
+    } else {
+      if (cpa)
+        gemm_main<FMT, BM, 1, true>(rowp, plane, nU, btile, nC, smem, ep);
+      else
+        gemm_main<FMT, BM, 1, false>(rowp, plane, nU, btile, nC, smem, ep);
+    }
+  } else if (!bok) {
     if (cpa)
-      gemm_main<FMT, 0, true>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 0, true>(rowp, plane, nU, btile, nC, smem, ep);
     else
-      gemm_main<FMT, 0, false>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 0, false>(rowp, plane, nU, btile, nC, smem, ep);
   } else if (rows > 96) {
-    gemm_main<FMT, 4, true>(rowp, plane, nU, btile, nC, smem, ep);
+    gemm_main<FMT, BM, 4, true>(rowp, plane, nU, btile, nC, smem, ep);
   } else if (rows > 64) {
     if (cpa)
-      gemm_main<FMT, 3, true>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 3, true>(rowp, plane, nU, btile, nC, smem, ep);
     else
-      gemm_main<FMT, 3, false>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 3, false>(rowp, plane, nU, btile, nC, smem, ep);
   } else if (rows > 32) {
     if (cpa)
-      gemm_main<FMT, 2, true>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 2, true>(rowp, plane, nU, btile, nC, smem, ep);
     else
-      gemm_main<FMT, 2, false>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 2, false>(rowp, plane, nU, btile, nC, smem, ep);
   } else {
     if (cpa)
-      gemm_main<FMT, 1, true>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 1, true>(rowp, plane, nU, btile, nC, smem, ep);
     else
-      gemm_main<FMT, 1, false>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 1, false>(rowp, plane, nU, btile, nC, smem, ep);
   }
 }
 
@@ -456,11 +473,13 @@ __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp
 // (2 x 1 KiB codes + 256 B: the scale dword of each of the 64 weight rows,
 // which covers both units of a step): 77 KiB, two workgroups per CU.
 constexpr int kLoRow = 64;
-constexpr int kLoPlane = kGemmBM * kLoRow;  // 8 KiB
+template <int BM>
+constexpr int kLoPlane = BM * kLoRow;  // 8 KiB for 128 rows
 constexpr int kLoScale = 4 * 256;
 constexpr int kBWaveHl = 2 * 1024 + 256;
 constexpr int kBSlotHl = 4 * kBWaveHl;
-constexpr int kHlLds = 2 * kAPlane + 2 * kLoPlane + 2 * kLoScale + kBSlots * kBSlotHl;
+template <int BM>
+constexpr int kHlLds = 2 * kAPlane<BM> + 2 * kLoPlane<BM> + 2 * kLoScale + kBSlots * kBSlotHl;
 
 __device__ __forceinline__ int lo_swz(int r) { return (r >> 1) & 3; }
 
@@ -482,7 +501,7 @@ __device__ __forceinline__ int lo_swz(int r) { return (r >> 1) & 3; }
 // one copy of the 64 rows' scale dwords) two steps ahead.  With an odd
 // number of units the last step's second unit is zeroed when read (lo codes
 // and weights zero, scales 1).
-template <int NB, bool CPA, typename Epilogue>
+template <int BM, int NB, bool CPA, typename Epilogue>
 __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], const uint8_t* const (&lrowp)[2],
                                              const uint8_t* srow, int nU, const uint8_t* __restrict__ btile,
                                              uint8_t* smem, Epilogue&& epilogue) {
@@ -498,8 +517,8 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
   const int nsteps = (nU + 1) / 2;
   const int full = nU / 2;
   uint8_t* const ahi = smem;
-  uint8_t* const alo = smem + 2 * kAPlane;
-  uint8_t* const asc = alo + 2 * kLoPlane;
+  uint8_t* const alo = smem + 2 * kAPlane<BM>;
+  uint8_t* const asc = alo + 2 * kLoPlane<BM>;
   uint8_t* const bring = asc + 2 * kLoScale + wave * kBWaveHl;
 
   f32x16_t acc[NBA][2];
@@ -516,13 +535,14 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
     const int c = cp_lo ^ (blk & 1);
     const int u = min(2 * sc + (c >> 2), nU - 1);
     dma16((const uint8_t*)rowp[blk] + u * 64 + (c & 3) * 16,
-          lds_addr(ahi + (s & 1) * kAPlane + (32 * wave + 8 * blk) * kARow));
+          lds_addr(ahi + (s & 1) * kAPlane<BM> + (32 * wave + 8 * blk) * kARow));
   };
   auto copy_lo = [&](int s, int blk) {
     const int sc = min(s, nsteps - 1);
     const int c = (lane & 3) ^ ((lane >> 3) & 3);  // lane l writes position l % 4 of row l / 4
     const int u = min(2 * sc + (c >> 1), nU - 1);
-    dma16(lrowp[blk] + u * 32 + (c & 1) * 16, lds_addr(alo + (s & 1) * kLoPlane + (32 * wave + 16 * blk) * kLoRow));
+    dma16(lrowp[blk] + u * 32 + (c & 1) * 16,
+          lds_addr(alo + (s & 1) * kLoPlane<BM> + (32 * wave + 16 * blk) * kLoRow));
   };
   auto copy_ls = [&](int s) {
     const int sc = min(s, nsteps - 1);
@@ -560,8 +580,8 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
     for (int ci = 0; ci < NPRE; ++ci) copy(s, ci);
     if constexpr (NB > 0) {
       const uint8_t* bs = bring + (s % kBSlots) * kBSlotHl;
-      const uint8_t* hs = ahi + (s & 1) * kAPlane;
-      const uint8_t* ls = alo + (s & 1) * kLoPlane;
+      const uint8_t* hs = ahi + (s & 1) * kAPlane<BM>;
+      const uint8_t* ls = alo + (s & 1) * kLoPlane<BM>;
       const uint8_t* ss = asc + (s & 1) * kLoScale;
       const int c = b_unit(s);
       const bool z = tail && h;
@@ -635,50 +655,67 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
   if constexpr (NB > 0) epilogue(acc);
 }
 
-template <typename Epilogue>
+template <int BM, typename Epilogue>
 __device__ __forceinline__ void gemm_rows_hl(int rows, const uint16_t* const (&rowp)[4],
                                              const uint8_t* const (&lrowp)[2], const uint8_t* srow, int nU,
                                              const uint8_t* __restrict__ btile, bool bok, uint8_t* smem,
                                              Epilogue&& ep) {
   const bool cpa = 32 * (threadIdx.x >> 6) < rows;
-  if (!bok) {
+  if constexpr (BM == 32) {
+    if (!bok) {
+      if (cpa)
+        gemm_main_hl<BM, 0, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+      else
+        gemm_main_hl<BM, 0, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+    } else {
+      if (cpa)
+        gemm_main_hl<BM, 1, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+      else
+        gemm_main_hl<BM, 1, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+    }
+  } else if (!bok) {
     if (cpa)
-      gemm_main_hl<0, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 0, true>(rowp, lrowp, srow, nU, btile, smem, ep);
     else
-      gemm_main_hl<0, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 0, false>(rowp, lrowp, srow, nU, btile, smem, ep);
   } else if (rows > 96) {
-    gemm_main_hl<4, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+    gemm_main_hl<BM, 4, true>(rowp, lrowp, srow, nU, btile, smem, ep);
   } else if (rows > 64) {
     if (cpa)
-      gemm_main_hl<3, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 3, true>(rowp, lrowp, srow, nU, btile, smem, ep);
     else
-      gemm_main_hl<3, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 3, false>(rowp, lrowp, srow, nU, btile, smem, ep);
   } else if (rows > 32) {
     if (cpa)
-      gemm_main_hl<2, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 2, true>(rowp, lrowp, srow, nU, btile, smem, ep);
     else
-      gemm_main_hl<2, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 2, false>(rowp, lrowp, srow, nU, btile, smem, ep);
   } else {
     if (cpa)
-      gemm_main_hl<1, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 1, true>(rowp, lrowp, srow, nU, btile, smem, ep);
     else
-      gemm_main_hl<1, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 1, false>(rowp, lrowp, srow, nU, btile, smem, ep);
   }
 }
 
-template <int FMT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// Occupancy of the grouped GEMMs: tiles of 32 rows need a quarter of the A
+// ring and a quarter of the accumulators, so three workgroups share a CU.
+template <int BM>
+constexpr int kGemmWaves = BM == 32 ? 3 : 2;
+
+template <int FMT, int BM>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmWaves<BM>)))
     fc1_gemm(const uint8_t* __restrict__ prep, const Layout L, const uint16_t* __restrict__ x, int k,
              const int* __restrict__ counts, const int* __restrict__ grp_start,
              const int* __restrict__ tile_start, const int* __restrict__ perm,
              uint16_t* __restrict__ act, int64_t plane, uint8_t* __restrict__ aq, uint8_t* __restrict__ as,
              int ass) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds<BM>];
   const GroupTile id = group_tile(fc1_blocks(L), tile_start, L.E);
   if (!id.ok) return;
   const int e = id.e;
-  const int m0 = (id.gm - tile_start[e]) * kGemmBM;
-  const int rows = min(kGemmBM, counts[e] - m0);
+  const int m0 = (id.gm - tile_start[e]) * BM;
+  const int rows = min(BM, counts[e] - m0);
   const int gs = grp_start[e] + m0;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // wave w computes prepared FC1 tile b: its rows 0..31 are gate columns
@@ -792,30 +829,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
       }
     });
   };
-  gemm_rows<FMT>(rows, rowp, 0, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, L.nC1, smem,
+  gemm_rows<FMT, BM>(rows, rowp, 0, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, L.nC1, smem,
                  epilogue);
 }
 
-template <int FMT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+template <int FMT, int BM>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmWaves<BM>)))
     fc2_gemm(const uint8_t* __restrict__ prep, const Layout L, const float* __restrict__ tw,
              const int* __restrict__ counts, const int* __restrict__ grp_start,
              const int* __restrict__ tile_start, const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, const uint8_t* __restrict__ aq,
              const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kHlLds : kGemmLds];
-  __shared__ float wrow[kGemmBM];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kHlLds<BM> : kGemmLds<BM>];
+  __shared__ float wrow[BM];
   const GroupTile id = group_tile(fc2_blocks(L), tile_start, L.E);
   if (!id.ok) return;
   const int e = id.e;
-  const int m0 = (id.gm - tile_start[e]) * kGemmBM;
-  const int rows = min(kGemmBM, counts[e] - m0);
+  const int m0 = (id.gm - tile_start[e]) * BM;
+  const int rows = min(BM, counts[e] - m0);
   const int gs = grp_start[e] + m0;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   // wave w computes prepared FC2 tile hb: output columns 64hb..64hb+63
   const int hb = 4 * id.nb + wave;
   const bool bok = hb < L.nB2;
-  if (t < kGemmBM) wrow[t] = t < rows ? tw[perm[gs + t]] : 0.0f;
+  if (t < BM) wrow[t] = t < rows ? tw[perm[gs + t]] : 0.0f;
   const float g2 = FMT == kNVFP4 ? ((const float*)prep)[L.E + e] : 1.0f;
   auto epilogue = [&](auto& acc) __attribute__((always_inline)) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
@@ -850,10 +887,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     for (int blk = 0; blk < 2; ++blk)
       lrowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
     const uint8_t* srow = as + (int64_t)(gs + min(32 * wave + (lane & 31), rows - 1)) * ass;
-    gemm_rows_hl(rows, rowp, lrowp, srow, L.nC2, btile, bok, smem, epilogue);
+    gemm_rows_hl<BM>(rows, rowp, lrowp, srow, L.nC2, btile, bok, smem, epilogue);
   } else {
     // two passes over K: the hi activation plane, then the lo plane
-    gemm_rows<FMT>(rows, rowp, plane, 2 * L.nC2, btile, bok, L.nC2, smem, epilogue);
+    gemm_rows<FMT, BM>(rows, rowp, plane, 2 * L.nC2, btile, bok, L.nC2, smem, epilogue);
   }
 }
 
@@ -922,18 +959,19 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   uint8_t* as = ws + W.as;
   const int ass = a8_scale_stride(L.I);
   float* y = (float*)(ws + W.y);
-  // m-tiles: at most one partial tile per expert beyond R / 128 full ones
-  const unsigned mt = (unsigned)((R + kGemmBM - 1) / kGemmBM + L.E);
+  // m-tiles of bm rows: at most one partial tile per expert beyond R / bm full ones
+  const int bm = prefill_bm(L, R, a8);
+  const unsigned mt = (unsigned)((R + bm - 1) / bm + L.E);
   if (phases & 5) {
     if (R <= kRouteBlock) {
-      hipLaunchKernelGGL((route_one<IdT>), dim3(1), dim3(1024), 0, st, ids, R, L.E, counts, grp_start, tile_start,
-                         perm, rpos);
+      hipLaunchKernelGGL((route_one<IdT>), dim3(1), dim3(1024), 0, st, ids, R, L.E, bm, counts, grp_start,
+                         tile_start, perm, rpos);
     } else {
       int* fill = (int*)(ws + W.fill);
       const unsigned nb = (unsigned)((R + kRouteBlock - 1) / kRouteBlock);
       hipLaunchKernelGGL(route_zero, dim3((L.E + 255) / 256), dim3(256), 0, st, L.E, counts, fill);
       hipLaunchKernelGGL((route_count<IdT>), dim3(nb), dim3(1024), 0, st, ids, R, L.E, counts);
-      hipLaunchKernelGGL((route_place<IdT>), dim3(nb), dim3(1024), 0, st, ids, R, L.E, counts, grp_start,
+      hipLaunchKernelGGL((route_place<IdT>), dim3(nb), dim3(1024), 0, st, ids, R, L.E, bm, counts, grp_start,
                          tile_start, fill, perm, rpos);
     }
   }
@@ -942,18 +980,29 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
     const hipError_t err = launch_fc1_a8(L, prep, x, M, k, ws, W, grid1, st);
     if (err != hipSuccess) return err;
   } else if (phases & 1) {
-    hipLaunchKernelGGL((fc1_gemm<FMT>), dim3(grid1), dim3(256), 0, st, prep, L, x, k,
-                       (const int*)counts, (const int*)grp_start, (const int*)tile_start,
-                       (const int*)perm, act, plane, aq, as, ass);
+    if (bm == 32)
+      hipLaunchKernelGGL((fc1_gemm<FMT, 32>), dim3(grid1), dim3(256), 0, st, prep, L, x, k,
+                         (const int*)counts, (const int*)grp_start, (const int*)tile_start,
+                         (const int*)perm, act, plane, aq, as, ass);
+    else
+      hipLaunchKernelGGL((fc1_gemm<FMT, kGemmBM>), dim3(grid1), dim3(256), 0, st, prep, L, x, k,
+                         (const int*)counts, (const int*)grp_start, (const int*)tile_start,
+                         (const int*)perm, act, plane, aq, as, ass);
   }
   if ((phases & 2) && a8) {
     const hipError_t err = launch_fc2_a8(L, prep, tw, ws, W, grid2, st);
     if (err != hipSuccess) return err;
   } else if (phases & 2) {
-    hipLaunchKernelGGL((fc2_gemm<FMT>), dim3(grid2), dim3(256), 0, st, prep, L, tw,
-                       (const int*)counts, (const int*)grp_start, (const int*)tile_start,
-                       (const int*)perm, (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as,
-                       ass, y);
+    if (bm == 32)
+      hipLaunchKernelGGL((fc2_gemm<FMT, 32>), dim3(grid2), dim3(256), 0, st, prep, L, tw,
+                         (const int*)counts, (const int*)grp_start, (const int*)tile_start,
+                         (const int*)perm, (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as,
+                         ass, y);
+    else
+      hipLaunchKernelGGL((fc2_gemm<FMT, kGemmBM>), dim3(grid2), dim3(256), 0, st, prep, L, tw,
+                         (const int*)counts, (const int*)grp_start, (const int*)tile_start,
+                         (const int*)perm, (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as,
+                         ass, y);
   }
   if (phases & 10) {
     hipLaunchKernelGGL((combine<IdT>), dim3(M, (L.H + 1023) / 1024), dim3(256), 0, st, ids, k, L.E, L.H,

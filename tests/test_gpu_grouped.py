@@ -46,6 +46,10 @@ CASES = [
     ("nvfp4", 12, 2560, 64, 200, 2, 6, 0.0),
     ("mxfp4", 3, 1536, 544, 100, 2, 7, 0.0),  # 17 FC1 tiles: last column block half empty
     ("mxfp4", 1, 64, 32, 130, 1, 8, 0.0),     # a single expert, 128 + 2 rows
+    # few routes per expert (at most 16 on average): 32-row m-tiles
+    ("mxfp4", 64, 512, 128, 100, 4, 9, 0.9),  # hot expert: three 32-row tiles and a ragged one
+    ("nvfp4", 40, 512, 96, 120, 4, 10, 0.6),  # I = 3 units: odd FC2 K; hot expert over several tiles
+    ("mxfp4", 256, 1024, 64, 60, 8, 11, 0.0), # 480 routes over 256 experts, 1-2 rows each
 ]
 
 
