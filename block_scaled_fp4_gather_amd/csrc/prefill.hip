@@ -254,13 +254,19 @@ __device__ __forceinline__ bf16x8_t lds_frag(const __bf16* p) {
 constexpr int kARow = kBK * 2;                    // bytes of one A row of a step
 template <int BM>
 constexpr int kAPlane = BM * kARow;               // 16 KiB for 128 rows
-constexpr int kBWave = 2 * 1024 + 2 * 256;        // one wave's weights of a step
-constexpr int kBSlot = 4 * kBWave;
+// One wave's weights of a step: 2 x 1 KiB codes and the scale dwords of the
+// 64 weight rows, one per row (both units of a step share it), or, for FC2's
+// two passes over K (whose step can take its units from two passes), one per
+// row and lane half.
+template <bool PASS2>
+constexpr int kBWave = 2 * 1024 + (PASS2 ? 2 : 1) * 256;
+template <bool PASS2>
+constexpr int kBSlot = 4 * kBWave<PASS2>;
 constexpr int kBSlots = 3;
 constexpr int kASlots = 3;
 constexpr int kADist = kASlots - 1;  // steps ahead that A is copied (the weights: kBSlots - 1)
-template <int BM>
-constexpr int kGemmLds = kASlots * kAPlane<BM> + kBSlots * kBSlot;
+template <int BM, bool PASS2>
+constexpr int kGemmLds = kASlots * kAPlane<BM> + kBSlots * kBSlot<PASS2>;
 
 // Grouped GEMM main loop for one 128-row x 256-column output tile, followed
 // by `epilogue(acc)`.  K runs over nU units of 32 values in steps of two; unit
@@ -291,23 +297,24 @@ constexpr int kGemmLds = kASlots * kAPlane<BM> + kBSlots * kBSlot;
 // ahead, tiles with few rows waited for it every step.  Copies past the last step are clamped to it (never used); with an
 // odd number of units the last step's second half (A and B both) is zeroed
 // when read.
-template <int FMT, int BM, int NB, bool CPA, typename Epilogue>
+template <int FMT, int BM, int NB, bool CPA, bool PASS2, typename Epilogue>
 __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int64_t plane, int nU,
                                           const uint8_t* __restrict__ btile, int nC, uint8_t* smem,
                                           Epilogue&& epilogue) {
   constexpr int SPD = FMT == kMXFP4 ? 4 : 2;
   constexpr int NBA = NB > 0 ? NB : 1;
   // copies of later steps in flight when step s starts: those issued in the
-  // steps s - kADist + 1 .. s - 1 (4 for A, 4 more for the weights)
+  // steps s - kADist + 1 .. s - 1 (4 for A, 3 or 4 more for the weights)
   static_assert(kADist == kBSlots - 1, "A and the weights are copied the same number of steps ahead");
-  constexpr int BCOPIES = (kADist - 1) * ((CPA ? 4 : 0) + (NB > 0 ? 4 : 0));
+  constexpr int NW = NB > 0 ? (PASS2 ? 4 : 3) : 0;  // weight copies per step
+  constexpr int BCOPIES = (kADist - 1) * ((CPA ? 4 : 0) + NW);
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int nsteps = (nU + 1) / 2;
   const int full = nU / 2;
   uint8_t* const aring = smem;
-  uint8_t* const bring = smem + kASlots * kAPlane<BM> + wave * kBWave;
+  uint8_t* const bring = smem + kASlots * kAPlane<BM> + wave * kBWave<PASS2>;
 
   f32x16_t acc[NBA][2];
 #pragma unroll
@@ -339,32 +346,42 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
   // copy of weight half j (codes and scale word) of step s into its ring slot
   auto copy_b = [&](int s, int j) {
     const int cc = b_chunk(s < nsteps ? s : nsteps - 1);
-    uint8_t* slot = bring + (s % kBSlots) * kBSlot;
+    uint8_t* slot = bring + (s % kBSlots) * kBSlot<PASS2>;
     const int row = 32 * j + n;
     dma16(btile + (int64_t)cc * 1024 + row * 16, lds_addr(slot + j * 1024));
-    dma4(btile + (int64_t)nC * 1024 + (cc / SPD) * 256 + row * 4, lds_addr(slot + 2048 + j * 256));
+    if constexpr (PASS2)
+      dma4(btile + (int64_t)nC * 1024 + (cc / SPD) * 256 + row * 4, lds_addr(slot + 2048 + j * 256));
+  };
+  // the scale dwords of the step's units for the 64 weight rows (lane l: row
+  // l; one pass, so both units of the step are in the same dword)
+  auto copy_bs = [&](int s) {
+    const int cw = min(2 * (s < nsteps ? s : nsteps - 1), nU - 1);
+    dma4(btile + (int64_t)nC * 1024 + (cw / SPD) * 256 + lane * 4,
+         lds_addr(bring + (s % kBSlots) * kBSlot<PASS2> + 2048));
   };
   // Copies of a step, always issued in this order (vm_wait counts on it):
   // copies 0..3 are A blocks for step s + 2 (none without CPA), copies 4 and
-  // 5 the weight halves for the same step.
-  constexpr int NCOPY = NB > 0 ? 6 : 4;
+  // 5 the weight halves for the same step, copy 6 (one pass) their scales.
+  constexpr int NCOPY = NB > 0 ? (PASS2 ? 6 : 7) : 4;
   constexpr int NGROUP = 4 * NB;                             // MFMA groups of a step
   constexpr int NPRE = NCOPY > NGROUP ? NCOPY - NGROUP : 0;  // copies issued before them
   auto copy = [&](int s, int ci) {
     if (ci < 4) {
       if constexpr (CPA) copy_a(s + kADist, ci);
-    } else {
+    } else if (ci < 6) {
       copy_b(s + kADist, ci - 4);
+    } else {
+      copy_bs(s + kADist);
     }
   };
   auto widen = [&](int s, bool tail, bf16x8_t (&bf)[4][2]) {
-    const uint8_t* slot = bring + (s % kBSlots) * kBSlot;
+    const uint8_t* slot = bring + (s % kBSlots) * kBSlot<PASS2>;
     const int c = b_chunk(s);
     const bool z = tail && h;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const u32x4 w = *(const u32x4*)(slot + j * 1024 + lane * 16);
-      const uint32_t sw = *(const uint32_t*)(slot + 2048 + j * 256 + lane * 4);
+      const uint32_t sw = *(const uint32_t*)(slot + 2048 + (PASS2 ? j * 256 + lane * 4 : (32 * j + n) * 4));
 #pragma unroll
       for (int q = 0; q < 4; ++q) bf[q][j] = z ? bf16x8_t{} : b_frag<FMT>(w[q], b_scale<FMT>(sw, c, q));
     }
@@ -408,6 +425,7 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
     if constexpr (NB > 0) {
       copy_b(s, 0);
       copy_b(s, 1);
+      if constexpr (!PASS2) copy_bs(s);
     }
   }
   for (int s = 0; s < full; ++s) step(s, false);
@@ -422,7 +440,7 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
 // tile has rows in it.  Tiles of BM = 32 rows have one block, copied by wave
 // 0.  Each variant carries its own copy of the epilogue, called with the
 // NB x 2 accumulator blocks.
-template <int FMT, int BM, typename Epilogue>
+template <int FMT, int BM, bool PASS2, typename Epilogue>
 __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp)[4], int64_t plane, int nU,
                                           const uint8_t* __restrict__ btile, bool bok, int nC,
                                           uint8_t* smem, Epilogue&& ep) {
@@ -430,37 +448,37 @@ __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp
   if constexpr (BM == 32) {
     if (!bok) {
       if (cpa)
-        gemm_main<FMT, BM, 0, true>(rowp, plane, nU, btile, nC, smem, ep);
+        gemm_main<FMT, BM, 0, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
       else
-        gemm_main<FMT, BM, 0, false>(rowp, plane, nU, btile, nC, smem, ep);
+        gemm_main<FMT, BM, 0, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
     } else {
       if (cpa)
-        gemm_main<FMT, BM, 1, true>(rowp, plane, nU, btile, nC, smem, ep);
+        gemm_main<FMT, BM, 1, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
       else
-        gemm_main<FMT, BM, 1, false>(rowp, plane, nU, btile, nC, smem, ep);
+        gemm_main<FMT, BM, 1, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
     }
   } else if (!bok) {
     if (cpa)
-      gemm_main<FMT, BM, 0, true>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 0, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
     else
-      gemm_main<FMT, BM, 0, false>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 0, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
   } else if (rows > 96) {
-    gemm_main<FMT, BM, 4, true>(rowp, plane, nU, btile, nC, smem, ep);
+    gemm_main<FMT, BM, 4, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
   } else if (rows > 64) {
     if (cpa)
-      gemm_main<FMT, BM, 3, true>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 3, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
     else
-      gemm_main<FMT, BM, 3, false>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 3, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
   } else if (rows > 32) {
     if (cpa)
-      gemm_main<FMT, BM, 2, true>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 2, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
     else
-      gemm_main<FMT, BM, 2, false>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 2, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
   } else {
     if (cpa)
-      gemm_main<FMT, BM, 1, true>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 1, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
     else
-      gemm_main<FMT, BM, 1, false>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 1, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
   }
 }
 
@@ -475,11 +493,12 @@ __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp
 constexpr int kLoRow = 64;
 template <int BM>
 constexpr int kLoPlane = BM * kLoRow;  // 8 KiB for 128 rows
-constexpr int kLoScale = 4 * 256;
+template <int BM>
+constexpr int kLoScale = BM / 32 * 256;
 constexpr int kBWaveHl = 2 * 1024 + 256;
 constexpr int kBSlotHl = 4 * kBWaveHl;
 template <int BM>
-constexpr int kHlLds = 2 * kAPlane<BM> + 2 * kLoPlane<BM> + 2 * kLoScale + kBSlots * kBSlotHl;
+constexpr int kHlLds = 2 * kAPlane<BM> + 2 * kLoPlane<BM> + 2 * kLoScale<BM> + kBSlots * kBSlotHl;
 
 __device__ __forceinline__ int lo_swz(int r) { return (r >> 1) & 3; }
 
@@ -519,7 +538,7 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
   uint8_t* const ahi = smem;
   uint8_t* const alo = smem + 2 * kAPlane<BM>;
   uint8_t* const asc = alo + 2 * kLoPlane<BM>;
-  uint8_t* const bring = asc + 2 * kLoScale + wave * kBWaveHl;
+  uint8_t* const bring = asc + 2 * kLoScale<BM> + wave * kBWaveHl;
 
   f32x16_t acc[NBA][2];
 #pragma unroll
@@ -546,7 +565,7 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
   };
   auto copy_ls = [&](int s) {
     const int sc = min(s, nsteps - 1);
-    dma4(srow + 4 * (sc / 2), lds_addr(asc + (s & 1) * kLoScale + wave * 256));
+    dma4(srow + 4 * (sc / 2), lds_addr(asc + (s & 1) * kLoScale<BM> + wave * 256));
   };
   auto b_unit = [&](int s) { return min(2 * s + h, nU - 1); };
   auto copy_b = [&](int s, int j) {
@@ -582,7 +601,7 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
       const uint8_t* bs = bring + (s % kBSlots) * kBSlotHl;
       const uint8_t* hs = ahi + (s & 1) * kAPlane<BM>;
       const uint8_t* ls = alo + (s & 1) * kLoPlane<BM>;
-      const uint8_t* ss = asc + (s & 1) * kLoScale;
+      const uint8_t* ss = asc + (s & 1) * kLoScale<BM>;
       const int c = b_unit(s);
       const bool z = tail && h;
       u32x4 w[2];
@@ -698,19 +717,23 @@ __device__ __forceinline__ void gemm_rows_hl(int rows, const uint16_t* const (&r
   }
 }
 
-// Occupancy of the grouped GEMMs: tiles of 32 rows need a quarter of the A
-// ring and a quarter of the accumulators, so three workgroups share a CU.
+// Occupancy of the grouped GEMMs (waves per SIMD): tiles of 32 rows need a
+// quarter of the A ring and a quarter of the accumulators, so three
+// workgroups share a CU, and four for MXFP4 FC1 (39 KiB of LDS, 120 VGPRs;
+// the other 32-row kernels would spill registers at four).
 template <int BM>
 constexpr int kGemmWaves = BM == 32 ? 3 : 2;
+template <int FMT, int BM>
+constexpr int kFc1Waves = BM == 32 && FMT == kMXFP4 ? 4 : kGemmWaves<BM>;
 
 template <int FMT, int BM>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmWaves<BM>)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFc1Waves<FMT, BM>)))
     fc1_gemm(const uint8_t* __restrict__ prep, const Layout L, const uint16_t* __restrict__ x, int k,
              const int* __restrict__ counts, const int* __restrict__ grp_start,
              const int* __restrict__ tile_start, const int* __restrict__ perm,
              uint16_t* __restrict__ act, int64_t plane, uint8_t* __restrict__ aq, uint8_t* __restrict__ as,
              int ass) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds<BM>];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds<BM, false>];
   const GroupTile id = group_tile(fc1_blocks(L), tile_start, L.E);
   if (!id.ok) return;
   const int e = id.e;
@@ -829,7 +852,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
       }
     });
   };
-  gemm_rows<FMT, BM>(rows, rowp, 0, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, L.nC1, smem,
+  gemm_rows<FMT, BM, false>(rows, rowp, 0, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, L.nC1, smem,
                  epilogue);
 }
 
@@ -840,7 +863,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
              const int* __restrict__ tile_start, const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, const uint8_t* __restrict__ aq,
              const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kHlLds<BM> : kGemmLds<BM>];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kHlLds<BM> : kGemmLds<BM, true>];
   __shared__ float wrow[BM];
   const GroupTile id = group_tile(fc2_blocks(L), tile_start, L.E);
   if (!id.ok) return;
@@ -890,7 +913,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
     gemm_rows_hl<BM>(rows, rowp, lrowp, srow, L.nC2, btile, bok, smem, epilogue);
   } else {
     // two passes over K: the hi activation plane, then the lo plane
-    gemm_rows<FMT, BM>(rows, rowp, plane, 2 * L.nC2, btile, bok, L.nC2, smem, epilogue);
+    gemm_rows<FMT, BM, true>(rows, rowp, plane, 2 * L.nC2, btile, bok, L.nC2, smem, epilogue);
   }
 }
 
