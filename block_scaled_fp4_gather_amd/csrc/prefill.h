@@ -20,6 +20,7 @@ struct PrefillWs {
   int64_t fill;        // int32 [E]   grouped rows handed out per expert (routing)
   int64_t perm;        // int32 [R]   grouped row -> route index t*k + j
   int64_t rpos;        // int32 [R]   route index -> grouped row (valid routes)
+  int64_t gw;          // fp32 [R]   router weight of each grouped row
   // bf16 activations a = SiLU(gate)*up per grouped row, hi = bf16(a) and
   // lo = a - hi:
   int64_t act;         // bf16 [R][I] hi plane; NVFP4: then bf16 [R][I] lo = bf16(a - hi)
@@ -47,7 +48,8 @@ inline PrefillWs prefill_ws(const Layout& L, int64_t routes, int64_t tokens, boo
   w.fill = w.tile_start + align_up(4 * ((int64_t)L.E + 1), 256);
   w.perm = w.fill + align_up(4 * (int64_t)L.E, 256);
   w.rpos = w.perm + align_up(4 * routes, 256);
-  int64_t o = w.rpos + align_up(4 * routes, 256);
+  w.gw = w.rpos + align_up(4 * routes, 256);
+  int64_t o = w.gw + align_up(4 * routes, 256);
   w.act = w.xq = w.xs = w.aq = w.as = o;
   if (a8) {
     w.xq = o;
@@ -69,7 +71,7 @@ inline PrefillWs prefill_ws(const Layout& L, int64_t routes, int64_t tokens, boo
 }
 
 // Largest routes (M * k) the grouped path takes: grouped-row indexes stay in
-// int32 and the workspace within 4 * (I + H) bytes per route (bf16
+// int32 and the workspace within 4 * (I + H) + 16 bytes per route (bf16
 // activations; less with MXFP8 activations, plus H + H / 32 per token).
 constexpr int64_t kPrefillMaxRoutes = int64_t(1) << 22;
 

@@ -44,7 +44,8 @@ __device__ __forceinline__ int route_expert(const IdT* __restrict__ ids, int r, 
 // Routing: the valid routes grouped by expert.  Expert e's routes take the
 // grouped rows [grp_start[e], grp_start[e] + counts[e]) and its m-tiles
 // [tile_start[e], tile_start[e + 1]); perm maps a grouped row to its route,
-// rpos a route to its grouped row.  The order of an expert's routes within
+// rpos a route to its grouped row, and gw holds each grouped row's router
+// weight.  The order of an expert's routes within
 // its rows is whatever the atomics hand out: every grouped row is computed
 // from its own route alone and the combine sums a token's routes in route
 // order through rpos, so the layer's output does not depend on it.  Ids are
@@ -115,9 +116,9 @@ __device__ void route_prefix(int* cnt, int E, int bm, bool out, int* __restrict_
 // its prefix, then every route takes its grouped row from an LDS counter.
 template <typename IdT>
 __global__ void __launch_bounds__(1024)
-    route_one(const IdT* __restrict__ ids, int R, int E, int bm, int* __restrict__ counts,
-              int* __restrict__ grp_start, int* __restrict__ tile_start, int* __restrict__ perm,
-              int* __restrict__ rpos) {
+    route_one(const IdT* __restrict__ ids, const float* __restrict__ tw, int R, int E, int bm,
+              int* __restrict__ counts, int* __restrict__ grp_start, int* __restrict__ tile_start,
+              int* __restrict__ perm, int* __restrict__ rpos, float* __restrict__ gw) {
   __shared__ int cnt[kRouteMaxExperts];
   const int t = threadIdx.x;
   for (int q = t; q < E; q += 1024) cnt[q] = 0;
@@ -137,6 +138,7 @@ __global__ void __launch_bounds__(1024)
     const int p = atomicAdd(&cnt[ex[i]], 1);
     perm[p] = r;
     rpos[r] = p;
+    gw[p] = tw[r];
   }
 }
 
@@ -173,9 +175,10 @@ __global__ void __launch_bounds__(1024)
 
 template <typename IdT>
 __global__ void __launch_bounds__(1024)
-    route_place(const IdT* __restrict__ ids, int R, int E, int bm, int* __restrict__ counts,
-                int* __restrict__ grp_start, int* __restrict__ tile_start, int* __restrict__ fill,
-                int* __restrict__ perm, int* __restrict__ rpos) {
+    route_place(const IdT* __restrict__ ids, const float* __restrict__ tw, int R, int E, int bm,
+                int* __restrict__ counts, int* __restrict__ grp_start, int* __restrict__ tile_start,
+                int* __restrict__ fill, int* __restrict__ perm, int* __restrict__ rpos,
+                float* __restrict__ gw) {
   __shared__ int cnt[kRouteMaxExperts];  // counts, then grp_start, then the block's next row per expert
   __shared__ int mine[kRouteMaxExperts];  // the block's routes per expert
   const int t = threadIdx.x;
@@ -203,6 +206,7 @@ __global__ void __launch_bounds__(1024)
     const int p = atomicAdd(&cnt[ex[i]], 1);
     perm[p] = r;
     rpos[r] = p;
+    gw[p] = tw[r];
   }
 }
 
@@ -297,9 +301,9 @@ constexpr int kGemmLds = kASlots * kAPlane<BM> + kBSlots * kBSlot<PASS2>;
 // ahead, tiles with few rows waited for it every step.  Copies past the last step are clamped to it (never used); with an
 // odd number of units the last step's second half (A and B both) is zeroed
 // when read.
-template <int FMT, int BM, int NB, bool CPA, bool PASS2, typename Epilogue>
+template <int FMT, int BM, int NB, bool CPA, bool PASS2, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int64_t plane, int nU,
-                                          const uint8_t* __restrict__ btile, int nC, uint8_t* smem,
+                                          const uint8_t* __restrict__ btile, int nC, uint8_t* smem, Pre&& pre,
                                           Epilogue&& epilogue) {
   constexpr int SPD = FMT == kMXFP4 ? 4 : 2;
   constexpr int NBA = NB > 0 ? NB : 1;
@@ -430,6 +434,7 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
   }
   for (int s = 0; s < full; ++s) step(s, false);
   if (full < nsteps) step(full, true);
+  pre();             // LDS the epilogue reads, written before the barrier
   vm_wait<0>();      // no copy may land after the workgroup's LDS is released
   __syncthreads();
   if constexpr (NB > 0) epilogue(acc);
@@ -440,45 +445,45 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
 // tile has rows in it.  Tiles of BM = 32 rows have one block, copied by wave
 // 0.  Each variant carries its own copy of the epilogue, called with the
 // NB x 2 accumulator blocks.
-template <int FMT, int BM, bool PASS2, typename Epilogue>
+template <int FMT, int BM, bool PASS2, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp)[4], int64_t plane, int nU,
                                           const uint8_t* __restrict__ btile, bool bok, int nC,
-                                          uint8_t* smem, Epilogue&& ep) {
+                                          uint8_t* smem, Pre&& pre, Epilogue&& ep) {
   const bool cpa = 32 * (threadIdx.x >> 6) < rows;
   if constexpr (BM == 32) {
     if (!bok) {
       if (cpa)
-        gemm_main<FMT, BM, 0, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+        gemm_main<FMT, BM, 0, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
       else
-        gemm_main<FMT, BM, 0, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+        gemm_main<FMT, BM, 0, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
     } else {
       if (cpa)
-        gemm_main<FMT, BM, 1, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+        gemm_main<FMT, BM, 1, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
       else
-        gemm_main<FMT, BM, 1, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+        gemm_main<FMT, BM, 1, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
     }
   } else if (!bok) {
     if (cpa)
-      gemm_main<FMT, BM, 0, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 0, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
     else
-      gemm_main<FMT, BM, 0, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 0, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
   } else if (rows > 96) {
-    gemm_main<FMT, BM, 4, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+    gemm_main<FMT, BM, 4, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
   } else if (rows > 64) {
     if (cpa)
-      gemm_main<FMT, BM, 3, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 3, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
     else
-      gemm_main<FMT, BM, 3, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 3, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
   } else if (rows > 32) {
     if (cpa)
-      gemm_main<FMT, BM, 2, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 2, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
     else
-      gemm_main<FMT, BM, 2, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 2, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
   } else {
     if (cpa)
-      gemm_main<FMT, BM, 1, true, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 1, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
     else
-      gemm_main<FMT, BM, 1, false, PASS2>(rowp, plane, nU, btile, nC, smem, ep);
+      gemm_main<FMT, BM, 1, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
   }
 }
 
@@ -520,10 +525,10 @@ __device__ __forceinline__ int lo_swz(int r) { return (r >> 1) & 3; }
 // one copy of the 64 rows' scale dwords) two steps ahead.  With an odd
 // number of units the last step's second unit is zeroed when read (lo codes
 // and weights zero, scales 1).
-template <int BM, int NB, bool CPA, typename Epilogue>
+template <int BM, int NB, bool CPA, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], const uint8_t* const (&lrowp)[2],
                                              const uint8_t* srow, int nU, const uint8_t* __restrict__ btile,
-                                             uint8_t* smem, Epilogue&& epilogue) {
+                                             uint8_t* smem, Pre&& pre, Epilogue&& epilogue) {
   constexpr int NBA = NB > 0 ? NB : 1;
   constexpr int NA = CPA ? 7 : 0;       // copies of A per step: 4 hi, 2 lo, 1 lo scale
   constexpr int NW = NB > 0 ? 3 : 0;    // copies of weights per step
@@ -669,51 +674,52 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
   }
   for (int s = 0; s < full; ++s) step(s, false);
   if (full < nsteps) step(full, true);
+  pre();         // LDS the epilogue reads, written before the barrier
   vm_wait<0>();  // no copy may land after the workgroup's LDS is released
   __syncthreads();
   if constexpr (NB > 0) epilogue(acc);
 }
 
-template <int BM, typename Epilogue>
+template <int BM, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_rows_hl(int rows, const uint16_t* const (&rowp)[4],
                                              const uint8_t* const (&lrowp)[2], const uint8_t* srow, int nU,
                                              const uint8_t* __restrict__ btile, bool bok, uint8_t* smem,
-                                             Epilogue&& ep) {
+                                             Pre&& pre, Epilogue&& ep) {
   const bool cpa = 32 * (threadIdx.x >> 6) < rows;
   if constexpr (BM == 32) {
     if (!bok) {
       if (cpa)
-        gemm_main_hl<BM, 0, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+        gemm_main_hl<BM, 0, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
       else
-        gemm_main_hl<BM, 0, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+        gemm_main_hl<BM, 0, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
     } else {
       if (cpa)
-        gemm_main_hl<BM, 1, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+        gemm_main_hl<BM, 1, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
       else
-        gemm_main_hl<BM, 1, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+        gemm_main_hl<BM, 1, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
     }
   } else if (!bok) {
     if (cpa)
-      gemm_main_hl<BM, 0, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 0, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
     else
-      gemm_main_hl<BM, 0, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 0, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
   } else if (rows > 96) {
-    gemm_main_hl<BM, 4, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+    gemm_main_hl<BM, 4, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
   } else if (rows > 64) {
     if (cpa)
-      gemm_main_hl<BM, 3, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 3, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
     else
-      gemm_main_hl<BM, 3, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 3, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
   } else if (rows > 32) {
     if (cpa)
-      gemm_main_hl<BM, 2, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 2, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
     else
-      gemm_main_hl<BM, 2, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 2, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
   } else {
     if (cpa)
-      gemm_main_hl<BM, 1, true>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 1, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
     else
-      gemm_main_hl<BM, 1, false>(rowp, lrowp, srow, nU, btile, smem, ep);
+      gemm_main_hl<BM, 1, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
   }
 }
 
@@ -853,12 +859,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFc1Wa
     });
   };
   gemm_rows<FMT, BM, false>(rows, rowp, 0, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, L.nC1, smem,
-                 epilogue);
+                            [] {}, epilogue);
 }
 
 template <int FMT, int BM>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmWaves<BM>)))
-    fc2_gemm(const uint8_t* __restrict__ prep, const Layout L, const float* __restrict__ tw,
+    fc2_gemm(const uint8_t* __restrict__ prep, const Layout L, const float* __restrict__ gw,
              const int* __restrict__ counts, const int* __restrict__ grp_start,
              const int* __restrict__ tile_start, const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, const uint8_t* __restrict__ aq,
@@ -875,7 +881,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
   // wave w computes prepared FC2 tile hb: output columns 64hb..64hb+63
   const int hb = 4 * id.nb + wave;
   const bool bok = hb < L.nB2;
-  if (t < BM) wrow[t] = t < rows ? tw[perm[gs + t]] : 0.0f;
+  // the router weights of the tile's rows, loaded now and put in LDS after
+  // the main loop (no copy waits for them)
+  const float wv = t < rows ? gw[gs + t] : 0.0f;
+  auto pre = [&] {
+    if (t < BM) wrow[t] = wv;
+  };
   const float g2 = FMT == kNVFP4 ? ((const float*)prep)[L.E + e] : 1.0f;
   auto epilogue = [&](auto& acc) __attribute__((always_inline)) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
@@ -910,10 +921,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
     for (int blk = 0; blk < 2; ++blk)
       lrowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
     const uint8_t* srow = as + (int64_t)(gs + min(32 * wave + (lane & 31), rows - 1)) * ass;
-    gemm_rows_hl<BM>(rows, rowp, lrowp, srow, L.nC2, btile, bok, smem, epilogue);
+    gemm_rows_hl<BM>(rows, rowp, lrowp, srow, L.nC2, btile, bok, smem, pre, epilogue);
   } else {
     // two passes over K: the hi activation plane, then the lo plane
-    gemm_rows<FMT, BM, true>(rows, rowp, plane, 2 * L.nC2, btile, bok, L.nC2, smem, epilogue);
+    gemm_rows<FMT, BM, true>(rows, rowp, plane, 2 * L.nC2, btile, bok, L.nC2, smem, pre, epilogue);
   }
 }
 
@@ -976,6 +987,7 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   int* tile_start = (int*)(ws + W.tile_start);
   int* perm = (int*)(ws + W.perm);
   int* rpos = (int*)(ws + W.rpos);
+  float* gw = (float*)(ws + W.gw);
   uint16_t* act = (uint16_t*)(ws + W.act);
   const int64_t plane = (W.aq - W.act) / 2;  // elements from the hi plane to the lo plane (NVFP4)
   uint8_t* aq = ws + W.aq;                   // MXFP4: the lo part as MXFP8
@@ -987,15 +999,15 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   const unsigned mt = (unsigned)((R + bm - 1) / bm + L.E);
   if (phases & 5) {
     if (R <= kRouteBlock) {
-      hipLaunchKernelGGL((route_one<IdT>), dim3(1), dim3(1024), 0, st, ids, R, L.E, bm, counts, grp_start,
-                         tile_start, perm, rpos);
+      hipLaunchKernelGGL((route_one<IdT>), dim3(1), dim3(1024), 0, st, ids, tw, R, L.E, bm, counts, grp_start,
+                         tile_start, perm, rpos, gw);
     } else {
       int* fill = (int*)(ws + W.fill);
       const unsigned nb = (unsigned)((R + kRouteBlock - 1) / kRouteBlock);
       hipLaunchKernelGGL(route_zero, dim3((L.E + 255) / 256), dim3(256), 0, st, L.E, counts, fill);
       hipLaunchKernelGGL((route_count<IdT>), dim3(nb), dim3(1024), 0, st, ids, R, L.E, counts);
-      hipLaunchKernelGGL((route_place<IdT>), dim3(nb), dim3(1024), 0, st, ids, R, L.E, bm, counts, grp_start,
-                         tile_start, fill, perm, rpos);
+      hipLaunchKernelGGL((route_place<IdT>), dim3(nb), dim3(1024), 0, st, ids, tw, R, L.E, bm, counts, grp_start,
+                         tile_start, fill, perm, rpos, gw);
     }
   }
   const unsigned grid1 = grid8((int64_t)mt * fc1_blocks(L)), grid2 = grid8((int64_t)mt * fc2_blocks(L));
@@ -1017,12 +1029,12 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
     if (err != hipSuccess) return err;
   } else if (phases & 2) {
     if (bm == 32)
-      hipLaunchKernelGGL((fc2_gemm<FMT, 32>), dim3(grid2), dim3(256), 0, st, prep, L, tw,
+      hipLaunchKernelGGL((fc2_gemm<FMT, 32>), dim3(grid2), dim3(256), 0, st, prep, L, (const float*)gw,
                          (const int*)counts, (const int*)grp_start, (const int*)tile_start,
                          (const int*)perm, (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as,
                          ass, y);
     else
-      hipLaunchKernelGGL((fc2_gemm<FMT, kGemmBM>), dim3(grid2), dim3(256), 0, st, prep, L, tw,
+      hipLaunchKernelGGL((fc2_gemm<FMT, kGemmBM>), dim3(grid2), dim3(256), 0, st, prep, L, (const float*)gw,
                          (const int*)counts, (const int*)grp_start, (const int*)tile_start,
                          (const int*)perm, (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as,
                          ass, y);
