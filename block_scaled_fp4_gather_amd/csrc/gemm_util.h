@@ -51,36 +51,32 @@ __device__ __forceinline__ int a_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int acc_row(int r, int lane) { return (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3); }
 
 // Workgroup -> (expert, m-tile, column block) of a grouped GEMM whose experts
-// own m-tiles [tile_start[e], tile_start[e + 1]).  Workgroups are dealt to the
-// 8 XCDs in turn, so consecutive ids are remapped to give each XCD a
-// contiguous range of tiles; within it the order is expert by expert, column
-// block by column block, with the expert's m-tiles innermost: the workgroups
-// that stream the same weight slab (same expert and column block) are
-// dispatched together and share it in that XCD's L2, and the column blocks of
-// an m-tile share its A rows there.  The grid is a multiple of 8; ok is false
-// past the last tile.
+// own m-tiles [tile_start[e], tile_start[e + 1]) (tile_expert[t]: the expert
+// of m-tile t).  Workgroups are dealt to the 8 XCDs in turn, so consecutive
+// ids are remapped to give each XCD a contiguous range of tiles; within it
+// the order is expert by expert, column block by column block, with the
+// expert's m-tiles innermost: the workgroups that stream the same weight slab
+// (same expert and column block) are dispatched together and share it in
+// that XCD's L2, and the column blocks of an m-tile share its A rows there.
+// Expert e's workgroups are the ids [tile_start[e], tile_start[e + 1]) times
+// nblocks, so the expert of id l is tile_expert[l / nblocks]: one load where
+// a search over tile_start would take log2(E) dependent ones.  The grid is a
+// multiple of 8; ok is false past the last tile.
 struct GroupTile {
   int e, gm, nb;
   bool ok;
 };
-__device__ __forceinline__ GroupTile group_tile(int nblocks, const int* __restrict__ tile_start, int E) {
+__device__ __forceinline__ GroupTile group_tile(int nblocks, const int* __restrict__ tile_start,
+                                                const int* __restrict__ tile_expert, int E) {
   const int per = gridDim.x / 8;
   const int logical = (blockIdx.x % 8) * per + blockIdx.x / 8;
   const int total = tile_start[E];
   if (logical >= total * nblocks) return GroupTile{0, 0, 0, false};
-  // the last expert whose tiles start at or before this one (it owns tiles:
-  // the next expert's range starts past `logical`)
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (tile_start[mid] * nblocks <= logical)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  const int nt = tile_start[lo + 1] - tile_start[lo];
-  const int local = logical - tile_start[lo] * nblocks;
-  return GroupTile{lo, tile_start[lo] + local % nt, local / nt, true};
+  const int e = tile_expert[logical / nblocks];
+  const int t0 = tile_start[e];
+  const int nt = tile_start[e + 1] - t0;
+  const int local = logical - t0 * nblocks;
+  return GroupTile{e, t0 + local % nt, local / nt, true};
 }
 
 // Grid of n tiles rounded up to whole XCD rounds (group_tile needs a multiple of 8).

@@ -18,6 +18,7 @@ struct PrefillWs {
   int64_t grp_start;   // int32 [E]   first grouped row of each expert
   int64_t tile_start;  // int32 [E+1] first m-tile of each expert; [E] = total tiles
   int64_t fill;        // int32 [E]   grouped rows handed out per expert (routing)
+  int64_t tile_expert; // int32 [R/32 + E] expert of each m-tile
   int64_t perm;        // int32 [R]   grouped row -> route index t*k + j
   int64_t rpos;        // int32 [R]   route index -> grouped row (valid routes)
   int64_t gw;          // fp32 [R]   router weight of each grouped row
@@ -46,7 +47,8 @@ inline PrefillWs prefill_ws(const Layout& L, int64_t routes, int64_t tokens, boo
   w.grp_start = align_up(4 * (int64_t)L.E, 256);
   w.tile_start = w.grp_start + align_up(4 * (int64_t)L.E, 256);
   w.fill = w.tile_start + align_up(4 * ((int64_t)L.E + 1), 256);
-  w.perm = w.fill + align_up(4 * (int64_t)L.E, 256);
+  w.tile_expert = w.fill + align_up(4 * (int64_t)L.E, 256);
+  w.perm = w.tile_expert + align_up(4 * ((routes + 31) / 32 + (int64_t)L.E), 256);
   w.rpos = w.perm + align_up(4 * routes, 256);
   w.gw = w.rpos + align_up(4 * routes, 256);
   int64_t o = w.gw + align_up(4 * routes, 256);

@@ -54,12 +54,14 @@ __device__ __forceinline__ int route_expert(const IdT* __restrict__ ids, int r, 
 constexpr int kRouteBlock = 4096;  // routes per workgroup of the routing kernels
 
 // Exclusive prefix over the E counters cnt (in LDS, E <= kRouteMaxExperts)
-// by the 1024 threads of a workgroup: counts[e], grp_start[e] and
-// tile_start[e] (m-tiles of bm rows; tile_start[E] the total) are
+// by the 1024 threads of a workgroup: counts[e], grp_start[e],
+// tile_start[e] (m-tiles of bm rows; tile_start[E] the total) and the expert
+// of each m-tile, tile_expert[t], are
 // written to global memory when `out` is set, and cnt[e] becomes
 // grp_start[e].  Ends with a barrier.
 __device__ void route_prefix(int* cnt, int E, int bm, bool out, int* __restrict__ counts,
-                             int* __restrict__ grp_start, int* __restrict__ tile_start) {
+                             int* __restrict__ grp_start, int* __restrict__ tile_start,
+                             int* __restrict__ tile_expert) {
   __shared__ int wpart[2][16];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   constexpr int PER = kRouteMaxExperts / 1024;  // counters per thread
@@ -102,6 +104,8 @@ __device__ void route_prefix(int* cnt, int E, int bm, bool out, int* __restrict_
         counts[e] = c[i];
         grp_start[e] = rb;
         tile_start[e] = tb;
+        const int nt = (c[i] + bm - 1) / bm;
+        for (int q = 0; q < nt; ++q) tile_expert[tb + q] = e;
       }
       cnt[e] = rb;
     }
@@ -118,7 +122,8 @@ template <typename IdT>
 __global__ void __launch_bounds__(1024)
     route_one(const IdT* __restrict__ ids, const float* __restrict__ tw, int R, int E, int bm,
               int* __restrict__ counts, int* __restrict__ grp_start, int* __restrict__ tile_start,
-              int* __restrict__ perm, int* __restrict__ rpos, float* __restrict__ gw) {
+              int* __restrict__ tile_expert, int* __restrict__ perm, int* __restrict__ rpos,
+              float* __restrict__ gw) {
   __shared__ int cnt[kRouteMaxExperts];
   const int t = threadIdx.x;
   for (int q = t; q < E; q += 1024) cnt[q] = 0;
@@ -130,7 +135,7 @@ __global__ void __launch_bounds__(1024)
     if (ex[i] >= 0) atomicAdd(&cnt[ex[i]], 1);
   }
   __syncthreads();
-  route_prefix(cnt, E, bm, true, counts, grp_start, tile_start);
+  route_prefix(cnt, E, bm, true, counts, grp_start, tile_start, tile_expert);
 #pragma unroll
   for (int i = 0; i < kRouteBlock / 1024; ++i) {
     if (ex[i] < 0) continue;
@@ -177,8 +182,8 @@ template <typename IdT>
 __global__ void __launch_bounds__(1024)
     route_place(const IdT* __restrict__ ids, const float* __restrict__ tw, int R, int E, int bm,
                 int* __restrict__ counts, int* __restrict__ grp_start, int* __restrict__ tile_start,
-                int* __restrict__ fill, int* __restrict__ perm, int* __restrict__ rpos,
-                float* __restrict__ gw) {
+                int* __restrict__ tile_expert, int* __restrict__ fill, int* __restrict__ perm,
+                int* __restrict__ rpos, float* __restrict__ gw) {
   __shared__ int cnt[kRouteMaxExperts];  // counts, then grp_start, then the block's next row per expert
   __shared__ int mine[kRouteMaxExperts];  // the block's routes per expert
   const int t = threadIdx.x;
@@ -188,7 +193,7 @@ __global__ void __launch_bounds__(1024)
     mine[q] = 0;
   }
   __syncthreads();
-  route_prefix(cnt, E, bm, blockIdx.x == 0, counts, grp_start, tile_start);
+  route_prefix(cnt, E, bm, blockIdx.x == 0, counts, grp_start, tile_start, tile_expert);
   int ex[kRouteBlock / 1024];
 #pragma unroll
   for (int i = 0; i < kRouteBlock / 1024; ++i) {
@@ -736,11 +741,12 @@ template <int FMT, int BM>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFc1Waves<FMT, BM>)))
     fc1_gemm(const uint8_t* __restrict__ prep, const Layout L, const uint16_t* __restrict__ x, int k,
              const int* __restrict__ counts, const int* __restrict__ grp_start,
-             const int* __restrict__ tile_start, const int* __restrict__ perm,
+             const int* __restrict__ tile_start, const int* __restrict__ tile_expert,
+             const int* __restrict__ perm,
              uint16_t* __restrict__ act, int64_t plane, uint8_t* __restrict__ aq, uint8_t* __restrict__ as,
              int ass) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds<BM, false>];
-  const GroupTile id = group_tile(fc1_blocks(L), tile_start, L.E);
+  const GroupTile id = group_tile(fc1_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
   const int e = id.e;
   const int m0 = (id.gm - tile_start[e]) * BM;
@@ -866,12 +872,13 @@ template <int FMT, int BM>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmWaves<BM>)))
     fc2_gemm(const uint8_t* __restrict__ prep, const Layout L, const float* __restrict__ gw,
              const int* __restrict__ counts, const int* __restrict__ grp_start,
-             const int* __restrict__ tile_start, const int* __restrict__ perm,
+             const int* __restrict__ tile_start, const int* __restrict__ tile_expert,
+             const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, const uint8_t* __restrict__ aq,
              const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kHlLds<BM> : kGemmLds<BM, true>];
   __shared__ float wrow[BM];
-  const GroupTile id = group_tile(fc2_blocks(L), tile_start, L.E);
+  const GroupTile id = group_tile(fc2_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
   const int e = id.e;
   const int m0 = (id.gm - tile_start[e]) * BM;
@@ -988,6 +995,7 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   int* perm = (int*)(ws + W.perm);
   int* rpos = (int*)(ws + W.rpos);
   float* gw = (float*)(ws + W.gw);
+  int* tile_expert = (int*)(ws + W.tile_expert);
   uint16_t* act = (uint16_t*)(ws + W.act);
   const int64_t plane = (W.aq - W.act) / 2;  // elements from the hi plane to the lo plane (NVFP4)
   uint8_t* aq = ws + W.aq;                   // MXFP4: the lo part as MXFP8
@@ -1000,14 +1008,14 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   if (phases & 5) {
     if (R <= kRouteBlock) {
       hipLaunchKernelGGL((route_one<IdT>), dim3(1), dim3(1024), 0, st, ids, tw, R, L.E, bm, counts, grp_start,
-                         tile_start, perm, rpos, gw);
+                         tile_start, tile_expert, perm, rpos, gw);
     } else {
       int* fill = (int*)(ws + W.fill);
       const unsigned nb = (unsigned)((R + kRouteBlock - 1) / kRouteBlock);
       hipLaunchKernelGGL(route_zero, dim3((L.E + 255) / 256), dim3(256), 0, st, L.E, counts, fill);
       hipLaunchKernelGGL((route_count<IdT>), dim3(nb), dim3(1024), 0, st, ids, R, L.E, counts);
       hipLaunchKernelGGL((route_place<IdT>), dim3(nb), dim3(1024), 0, st, ids, tw, R, L.E, bm, counts, grp_start,
-                         tile_start, fill, perm, rpos, gw);
+                         tile_start, tile_expert, fill, perm, rpos, gw);
     }
   }
   const unsigned grid1 = grid8((int64_t)mt * fc1_blocks(L)), grid2 = grid8((int64_t)mt * fc2_blocks(L));
@@ -1017,11 +1025,11 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   } else if (phases & 1) {
     if (bm == 32)
       hipLaunchKernelGGL((fc1_gemm<FMT, 32>), dim3(grid1), dim3(256), 0, st, prep, L, x, k,
-                         (const int*)counts, (const int*)grp_start, (const int*)tile_start,
+                         (const int*)counts, (const int*)grp_start, (const int*)tile_start, (const int*)tile_expert,
                          (const int*)perm, act, plane, aq, as, ass);
     else
       hipLaunchKernelGGL((fc1_gemm<FMT, kGemmBM>), dim3(grid1), dim3(256), 0, st, prep, L, x, k,
-                         (const int*)counts, (const int*)grp_start, (const int*)tile_start,
+                         (const int*)counts, (const int*)grp_start, (const int*)tile_start, (const int*)tile_expert,
                          (const int*)perm, act, plane, aq, as, ass);
   }
   if ((phases & 2) && a8) {
@@ -1030,12 +1038,12 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   } else if (phases & 2) {
     if (bm == 32)
       hipLaunchKernelGGL((fc2_gemm<FMT, 32>), dim3(grid2), dim3(256), 0, st, prep, L, (const float*)gw,
-                         (const int*)counts, (const int*)grp_start, (const int*)tile_start,
+                         (const int*)counts, (const int*)grp_start, (const int*)tile_start, (const int*)tile_expert,
                          (const int*)perm, (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as,
                          ass, y);
     else
       hipLaunchKernelGGL((fc2_gemm<FMT, kGemmBM>), dim3(grid2), dim3(256), 0, st, prep, L, (const float*)gw,
-                         (const int*)counts, (const int*)grp_start, (const int*)tile_start,
+                         (const int*)counts, (const int*)grp_start, (const int*)tile_start, (const int*)tile_expert,
                          (const int*)perm, (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as,
                          ass, y);
   }

@@ -203,9 +203,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     fc1_gemm_a8(const uint8_t* __restrict__ prep, const Layout L, const uint8_t* __restrict__ xq,
                 const uint8_t* __restrict__ xs, int xss, int k, const int* __restrict__ counts,
                 const int* __restrict__ grp_start, const int* __restrict__ tile_start,
-                const int* __restrict__ perm, uint8_t* __restrict__ aq, uint8_t* __restrict__ as, int ass) {
+                const int* __restrict__ tile_expert, const int* __restrict__ perm, uint8_t* __restrict__ aq,
+                uint8_t* __restrict__ as, int ass) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds8];
-  const GroupTile id = group_tile(fc1_blocks(L), tile_start, L.E);
+  const GroupTile id = group_tile(fc1_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
   const int e = id.e;
   const int m0 = (id.gm - tile_start[e]) * kGemmBM;
@@ -286,11 +287,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     fc2_gemm_a8(const uint8_t* __restrict__ prep, const Layout L, const float* __restrict__ tw,
                 const int* __restrict__ counts, const int* __restrict__ grp_start,
-                const int* __restrict__ tile_start, const int* __restrict__ perm,
-                const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
+                const int* __restrict__ tile_start, const int* __restrict__ tile_expert,
+                const int* __restrict__ perm, const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds8];
   __shared__ float wrow[kGemmBM];
-  const GroupTile id = group_tile(fc2_blocks(L), tile_start, L.E);
+  const GroupTile id = group_tile(fc2_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
   const int e = id.e;
   const int m0 = (id.gm - tile_start[e]) * kGemmBM;
@@ -334,7 +335,8 @@ hipError_t launch_fc1_a8(const Layout& L, const uint8_t* prep, const uint16_t* x
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(fc1_gemm_a8, dim3(grid), dim3(256), 0, st, prep, L, (const uint8_t*)xq, (const uint8_t*)xs,
                      a8_scale_stride(L.H), k, (const int*)(ws + W.counts), (const int*)(ws + W.grp_start),
-                     (const int*)(ws + W.tile_start), (const int*)(ws + W.perm), ws + W.aq, ws + W.as,
+                     (const int*)(ws + W.tile_start), (const int*)(ws + W.tile_expert), (const int*)(ws + W.perm),
+                     ws + W.aq, ws + W.as,
                      a8_scale_stride(L.I));
   return hipGetLastError();
 }
@@ -342,7 +344,8 @@ hipError_t launch_fc1_a8(const Layout& L, const uint8_t* prep, const uint16_t* x
 hipError_t launch_fc2_a8(const Layout& L, const uint8_t* prep, const float* tw, uint8_t* ws, const PrefillWs& W,
                          unsigned grid, hipStream_t st) {
   hipLaunchKernelGGL(fc2_gemm_a8, dim3(grid), dim3(256), 0, st, prep, L, tw, (const int*)(ws + W.counts),
-                     (const int*)(ws + W.grp_start), (const int*)(ws + W.tile_start), (const int*)(ws + W.perm),
+                     (const int*)(ws + W.grp_start), (const int*)(ws + W.tile_start),
+                     (const int*)(ws + W.tile_expert), (const int*)(ws + W.perm),
                      (const uint8_t*)(ws + W.aq), (const uint8_t*)(ws + W.as), a8_scale_stride(L.I),
                      (float*)(ws + W.y));
   return hipGetLastError();
