@@ -7,17 +7,21 @@
 // smaller than 128 rows), and reduces the routed outputs into fp32 before one
 // cast (b12x #311, commit on the prefill fused-sum epilogue).  Here:
 //   routing    groups the valid routes by expert (route_one, or route_zero,
-//              route_count and route_place for many routes) and numbers the
-//              128-row m-tiles of every expert;
-//   fc1_gemm   x rows gathered into LDS, FP4 weight tiles dequantised to
-//              bf16 into LDS (exact: E2M1 times a UE8M0 or E4M3 block scale
-//              has at most 6 significant bits), v_mfma_f32_32x32x16_bf16 with
-//              fp32 accumulation, SiLU(gate)*up epilogue -> activation rows as
-//              two bf16 planes, hi = bf16(a) and lo = bf16(a - hi);
-//   fc2_gemm   the same over the activation rows and W2, one MFMA per plane
-//              (so the activation keeps 16 significant bits, as in the decode
-//              path), times the NVFP4 global and the route's router weight ->
-//              fp32 rows;
+//              route_count and route_place for many routes), numbers the
+//              m-tiles of every expert (128 rows, or 32 when the experts get
+//              few routes each) and records each m-tile's expert and each
+//              grouped row's router weight;
+//   fc1_gemm   x rows gathered into LDS, FP4 weight units copied into LDS and
+//              widened to bf16 in registers (exact: E2M1 times a UE8M0 or
+//              E4M3 block scale has at most 6 significant bits), v_mfma_f32_32x32x16_bf16 with
+//              fp32 accumulation, SiLU(gate)*up epilogue -> the activation as
+//              hi = bf16(a) plus the residual lo = a - hi (NVFP4: a second
+//              bf16 plane; MXFP4: MXFP8 codes and scales);
+//   fc2_gemm   the same over the activation rows and W2: NVFP4 in two passes
+//              over K, one per bf16 plane; MXFP4 in one pass, the residual on
+//              v_mfma_scale_f32_32x32x64_f8f6f4 with the weights as stored;
+//              times the NVFP4 global and the route's router weight -> fp32
+//              rows;
 //   combine    per token, the fp32 sum of its valid routes' rows in route
 //              order, rounded once to bf16.
 // Invalid ids (negative or >= E) join no group and are skipped by combine.
@@ -256,10 +260,11 @@ __device__ __forceinline__ bf16x8_t lds_frag(const __bf16* p) {
   return __builtin_bit_cast(bf16x8_t, *(const u32x4*)p);
 }
 
-// LDS of a grouped GEMM workgroup: an A ring of 3 slots x 128 rows x 128
+// LDS of a grouped GEMM workgroup: an A ring of 3 slots x BM rows x 128
 // bytes (64 bf16 per row, unpadded; the 16-byte chunk c of row r sits at
 // position c ^ swz(r)), and a weight ring of 3 slots x 4 waves x (2 x 1 KiB
-// codes + 2 x 256 B scales): 78 KiB, two workgroups per CU.
+// codes + 256 B of scale dwords, 512 B for FC2's two passes): 75 KiB for
+// FC1 with 128-row tiles (two workgroups per CU), 39 KiB with 32-row tiles.
 constexpr int kARow = kBK * 2;                    // bytes of one A row of a step
 template <int BM>
 constexpr int kAPlane = BM * kARow;               // 16 KiB for 128 rows
