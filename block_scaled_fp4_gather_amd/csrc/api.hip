@@ -225,7 +225,7 @@ moe_fp4_status moe_fp4_prepared_bytes(const moe_fp4_desc* desc, size_t* bytes) {
   moe_fp4_status st = desc_layout(desc, &L);
   if (st != MOE_FP4_OK) return st;
   if (!bytes) return MOE_FP4_EINVAL;
-  *bytes = (size_t)L.total;
+  *bytes = (size_t)moe::layout_total(L);
   return MOE_FP4_OK;
 }
 
@@ -241,7 +241,7 @@ moe_fp4_status moe_fp4_prepare(const moe_fp4_desc* desc, const uint8_t* w13_code
   if (nv != (g13 != nullptr) || nv != (g2 != nullptr)) return MOE_FP4_EINVAL;
   if (!aligned(w13_codes, 16) || !aligned(w2_codes, 16) || !aligned(prepared, 256)) return MOE_FP4_EINVAL;
   if ((nv && (!aligned(g13, 4) || !aligned(g2, 4)))) return MOE_FP4_EINVAL;
-  if ((int64_t)prepared_bytes < L.total) return MOE_FP4_EWORKSPACE;
+  if ((int64_t)prepared_bytes < moe::layout_total(L)) return MOE_FP4_EWORKSPACE;
   return from_hip(moe::launch_repack(L, 0, (uint8_t*)w13_codes, (uint8_t*)w13_scales,
                                      (uint8_t*)w2_codes, (uint8_t*)w2_scales, (float*)g13,
                                      (float*)g2, (uint8_t*)prepared, (hipStream_t)stream));

@@ -263,7 +263,7 @@ __global__ void __launch_bounds__(1024)
   if (e < 0) return;  // same decision in every wave of the workgroup
   const uint8_t* tile = prep + fc1_tile_offset(L, e, b);
   const uint8_t* sbase = tile + (int64_t)L.nC1 * 1024;
-  const uint8_t* csf = tile + L.csf1;  // compressed scales (CSF block)
+  const uint8_t* csf = tile + csf_offset1(L);  // compressed scales (CSF block)
 
   int m = 0;
   for (int t = 0; t < M; ++t) m += token_routes(mask, t, k) != 0;
@@ -397,7 +397,7 @@ __global__ void __launch_bounds__(64 * fc2_max_waves(KL))
     if (e < 0) continue;
     const uint8_t* tile = prep + fc2_tile_offset(L, e, hb);
     const uint8_t* sbase = tile + (int64_t)L.nC2 * 1024;
-    const uint8_t* csf = tile + L.csf2;  // compressed scales (CSF block)
+    const uint8_t* csf = tile + csf_offset2(L);  // compressed scales (CSF block)
     const float g2 = FMT == kNVFP4 ? ((const float*)prep)[L.E + e] : 1.0f;
     // CI groups of KL chunks per pass, all their loads issued together
     for (int c0 = 0; c0 < L.nC2; c0 += CI * KL) {

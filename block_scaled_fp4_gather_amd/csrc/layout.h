@@ -71,17 +71,25 @@ struct Layout {
   int32_t nB2;      // FC2 tiles per expert (ceil(H/64))
   int32_t nQ1;      // FC1 scale dwords per lane (ceil(H/G/4))
   int32_t nQ2;      // FC2 scale dwords per lane (ceil(I/G/4))
+  int32_t csf;      // tiles carry a CSF block (compressed scale format)
   int64_t tile1;    // bytes of one FC1 tile
   int64_t tile2;    // bytes of one FC2 tile
   int64_t w13;      // bytes of an expert's FC1 tiles
   int64_t expert;   // expert stride
   int64_t globals;  // bytes of the globals header
-  int64_t total;    // whole prepared buffer
-  int32_t csf;      // tiles carry a CSF block (compressed scale format)
-  int64_t csf1;     // offset of the CSF block in an FC1 tile (0 without)
-  int64_t csf2;     // offset of the CSF block in an FC2 tile (0 without)
   ActParams act;    // the layer's activation (not part of the byte layout)
 };
+// The decode kernels take a Layout by value: it stays at 112 bytes (derived
+// sizes below are functions, not fields), so their arguments fit the same
+// kernel-argument cache lines as before the CSF flag (a larger struct cost
+// FC2 0.3 us per launch from a cold cache).
+static_assert(sizeof(Layout) == 112, "Layout is passed by value to every kernel");
+
+// Whole prepared buffer.
+MOE_HD inline int64_t layout_total(const Layout& L) { return L.globals + L.expert * L.E; }
+// Offset of the CSF block in an FC1 / FC2 tile (after the codes and plain scales).
+MOE_HD inline int64_t csf_offset1(const Layout& L) { return (int64_t)L.nC1 * 1024 + (int64_t)L.nQ1 * 256; }
+MOE_HD inline int64_t csf_offset2(const Layout& L) { return (int64_t)L.nC2 * 1024 + (int64_t)L.nQ2 * 256; }
 
 MOE_HD inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -116,14 +124,11 @@ MOE_HD inline bool make_layout(int32_t fmt, int32_t E, int32_t H, int32_t I, Lay
   L->nQ1 = (H / L->G + 3) / 4;
   L->nQ2 = (I / L->G + 3) / 4;
   L->csf = csf ? 1 : 0;
-  L->csf1 = csf ? (int64_t)L->nC1 * 1024 + (int64_t)L->nQ1 * 256 : 0;
-  L->csf2 = csf ? (int64_t)L->nC2 * 1024 + (int64_t)L->nQ2 * 256 : 0;
   L->tile1 = (int64_t)L->nC1 * 1024 + (int64_t)L->nQ1 * 256 + (csf ? csf_block_bytes(fmt, L->nC1) : 0);
   L->tile2 = (int64_t)L->nC2 * 1024 + (int64_t)L->nQ2 * 256 + (csf ? csf_block_bytes(fmt, L->nC2) : 0);
   L->w13 = L->tile1 * L->nB1;
   L->expert = align_up(L->w13 + L->tile2 * L->nB2, 256);
   L->globals = fmt == kNVFP4 ? align_up(8 * (int64_t)E, 256) : 0;
-  L->total = L->globals + L->expert * E;
   L->act = ActParams{kActSilu, 0.0f, 0.0f, 0.0f};
   return true;
 }

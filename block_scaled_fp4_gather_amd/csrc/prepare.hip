@@ -94,7 +94,7 @@ __global__ void __launch_bounds__(256) csf_kernel(Layout L, const uint8_t* __res
   const int row = fc1 ? fc1_row(L, t, lane) : t * 64 + lane;
   const int nC = fc1 ? L.nC1 : L.nC2;
   const int nsc = (fc1 ? L.H : L.I) / L.G;  // scale bytes per row
-  uint8_t* blk = prep + (fc1 ? fc1_tile_offset(L, e, t) + L.csf1 : fc2_tile_offset(L, e, t) + L.csf2);
+  uint8_t* blk = prep + (fc1 ? fc1_tile_offset(L, e, t) + csf_offset1(L) : fc2_tile_offset(L, e, t) + csf_offset2(L));
   const uint8_t* src = (fc1 ? w13s : w2s) + ((int64_t)e * rows + row) * nsc;
   const uint32_t reach = L.fmt == kMXFP4 ? 1u : 15u;
   uint32_t base = 0u;
@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(256) export_kernel(Layout L, int e, int which,
     }
   }
   float s0, s1;
-  const uint8_t* csf = L.csf ? prep + toff + (fc1 ? L.csf1 : L.csf2) : nullptr;
+  const uint8_t* csf = L.csf ? prep + toff + (fc1 ? csf_offset1(L) : csf_offset2(L)) : nullptr;
   if (L.fmt == kMXFP4) {
     const uint32_t word = csf ? csf_scale_word<kMXFP4>(csf, lane, c, sw[64 * (c / 4)]) : sw[64 * (c / 4)];
     s0 = s1 = mx_scale(word, c);
