@@ -44,6 +44,14 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return sign | (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
 }
 
+// Value of an E4M3 code (finite codes only): exponent field e and mantissa m
+// give (1 + m / 8) * 2^(e - 7), or m * 2^-9 for e = 0.
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
 }  // namespace moe
 
 // MXFP8 quantisation of bf16 rows: codes [rows][cols] (row stride cols),

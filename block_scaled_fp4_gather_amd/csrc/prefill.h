@@ -24,13 +24,17 @@ struct PrefillWs {
   int64_t gw;          // fp32 [R]   router weight of each grouped row
   // bf16 activations a = SiLU(gate)*up per grouped row, hi = bf16(a) and
   // lo = a - hi:
-  int64_t act;         // bf16 [R][I] hi plane; NVFP4: then bf16 [R][I] lo = bf16(a - hi)
-                       // (16 significant bits); MXFP4: lo as MXFP8 in aq / as
+  int64_t act;         // NVFP4: bf16 [R][I] hi plane, then bf16 [R][I] lo = bf16(a - hi)
+                       // (16 significant bits); MXFP4: three MXFP8 planes in aq / as
   // MXFP8 activations (W4A8-MX; scale rows padded to whole dwords):
   int64_t xq;          // u8 [M][H]  x codes per token
   int64_t xs;          // u8 [M][a8_scale_stride(H)]  x scales
-  int64_t aq;          // u8 [R][I]  SiLU(gate)*up codes per grouped row (MXFP4 bf16: lo codes)
-  int64_t as;          // u8 [R][a8_scale_stride(I)]  their scales
+  int64_t aq;          // u8 [R][I]  SiLU(gate)*up codes per grouped row; MXFP4 with bf16
+                       // activations: u8 [3][R][I] (plane p at p * pst bytes), planes 0 and 1
+                       // hold hi (its MXFP8 rounding, then the remainder), plane 2 lo
+  int64_t as;          // u8 [R][a8_scale_stride(I)]  their scales; MXFP4 with bf16 activations:
+                       // u32 [R][I / 32], byte p the scale of plane p for those 32 columns
+  int64_t pst;         // bytes from one MXFP8 plane to the next (MXFP4 with bf16 activations)
   int64_t y;           // fp32 [R][H] router-weighted FC2 output per grouped row
   int64_t total;
 };
@@ -53,6 +57,7 @@ inline PrefillWs prefill_ws(const Layout& L, int64_t routes, int64_t tokens, boo
   w.gw = w.rpos + align_up(4 * routes, 256);
   int64_t o = w.gw + align_up(4 * routes, 256);
   w.act = w.xq = w.xs = w.aq = w.as = o;
+  w.pst = 0;
   if (a8) {
     w.xq = o;
     w.xs = w.xq + align_up(tokens * L.H, 256);
@@ -60,9 +65,10 @@ inline PrefillWs prefill_ws(const Layout& L, int64_t routes, int64_t tokens, boo
     w.as = w.aq + align_up(routes * L.I, 256);
     o = w.as + align_up(routes * a8_scale_stride(L.I), 256);
   } else if (L.fmt == kMXFP4) {
-    w.aq = w.act + align_up(2 * routes * L.I, 256);
-    w.as = w.aq + align_up(routes * L.I, 256);
-    o = w.as + align_up(routes * a8_scale_stride(L.I), 256);
+    w.pst = align_up(routes * L.I, 256);
+    w.aq = o;
+    w.as = w.aq + 3 * w.pst;
+    o = w.as + align_up(routes * (L.I / 32) * 4, 256);
   } else {
     w.aq = w.as = w.act + align_up(2 * routes * L.I, 256);
     o = w.act + 2 * align_up(2 * routes * L.I, 256);

@@ -15,13 +15,14 @@
 //              widened to bf16 in registers (exact: E2M1 times a UE8M0 or
 //              E4M3 block scale has at most 6 significant bits), v_mfma_f32_32x32x16_bf16 with
 //              fp32 accumulation, SiLU(gate)*up epilogue -> the activation as
-//              hi = bf16(a) plus the residual lo = a - hi (NVFP4: a second
-//              bf16 plane; MXFP4: MXFP8 codes and scales);
-//   fc2_gemm   the same over the activation rows and W2: NVFP4 in two passes
-//              over K, one per bf16 plane; MXFP4 in one pass, the residual on
-//              v_mfma_scale_f32_32x32x64_f8f6f4 with the weights as stored;
-//              times the NVFP4 global and the route's router weight -> fp32
-//              rows;
+//              hi = bf16(a) plus the residual lo = a - hi: NVFP4 as two bf16
+//              planes; MXFP4 as three MXFP8 planes (hi rounded to MXFP8, what
+//              that leaves of hi, and lo);
+//   fc2_gemm   over the activation rows and W2: NVFP4 as fc1_gemm, in two
+//              passes over K, one per bf16 plane; MXFP4 in one pass on
+//              v_mfma_scale_f32_32x32x64_f8f6f4, three per block and step,
+//              with the weights as stored; times the NVFP4 global and the
+//              route's router weight -> fp32 rows;
 //   combine    per token, the fp32 sum of its valid routes' rows in route
 //              order, rounded once to bf16.
 // Invalid ids (negative or >= E) join no group and are skipped by combine.
@@ -497,63 +498,66 @@ __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp
   }
 }
 
-// LDS of the MXFP4 FC2 workgroup, whose activations are a bf16 hi plane and
-// an MXFP8 lo part: the A ring of gemm_main in 2 slots; an A lo ring of 2
-// slots x 128 rows x 64 bytes (the 64 FP8 values of a step; 16-byte chunk c
-// of row r at position c ^ lo_swz(r)); an A lo scale ring of 2 slots x 4
-// waves x 256 bytes (one dword of 4 unit scales per row, rows 32w..32w+31;
-// the upper 128 bytes are spare); a weight ring of 3 slots x 4 waves x
-// (2 x 1 KiB codes + 256 B: the scale dword of each of the 64 weight rows,
-// which covers both units of a step): 77 KiB, two workgroups per CU.
-constexpr int kLoRow = 64;
+// LDS of the MXFP4 FC2 workgroup, whose activations are three MXFP8 planes:
+// an A ring of 2 slots x 3 planes x BM rows x 64 bytes (the 64 FP8 values of
+// a step; 16-byte chunk c of row r at position c ^ pl_swz(r)); an A scale
+// ring of 2 slots x BM / 32 waves x 256 bytes (lane n + 32h of wave w: the
+// scale dword of row 32w + n for unit 2s + h, one byte per plane); a weight
+// ring of 3 slots x 4 waves x (2 x 1 KiB codes + 256 B: the scale dword of
+// each of the 64 weight rows, which covers both units of a step): 77 KiB for
+// 128-row tiles, two workgroups per CU.
+constexpr int kPlRow = 64;
 template <int BM>
-constexpr int kLoPlane = BM * kLoRow;  // 8 KiB for 128 rows
+constexpr int kPlPlane = BM * kPlRow;  // 8 KiB for 128 rows
 template <int BM>
-constexpr int kLoScale = BM / 32 * 256;
-constexpr int kBWaveHl = 2 * 1024 + 256;
-constexpr int kBSlotHl = 4 * kBWaveHl;
+constexpr int kPlSlot = 3 * kPlPlane<BM>;
 template <int BM>
-constexpr int kHlLds = 2 * kAPlane<BM> + 2 * kLoPlane<BM> + 2 * kLoScale<BM> + kBSlots * kBSlotHl;
+constexpr int kPlScale = BM / 32 * 256;
+constexpr int kBWavePl = 2 * 1024 + 256;
+constexpr int kBSlotPl = 4 * kBWavePl;
+template <int BM>
+constexpr int kPlLds = 2 * kPlSlot<BM> + 2 * kPlScale<BM> + kBSlots * kBSlotPl;
 
-__device__ __forceinline__ int lo_swz(int r) { return (r >> 1) & 3; }
+// Position swizzle of a 64-byte plane row: for every 8, 16 or 32 lanes that
+// read one chunk each of rows n = lane % 32 (the same chunk index) the 16-byte
+// units land in distinct LDS banks.
+__device__ __forceinline__ int pl_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // FC2 main loop of MXFP4 layers for one 128-row x 256-column output tile,
 // followed by `epilogue(acc)`: one pass over the nU units of K (= I / 32) in
-// steps of two.  A step multiplies the hi plane as gemm_main does (bf16
-// MFMAs on the widened weight unit) and the lo part with two
-// v_mfma_scale_f32_32x32x64_f8f6f4 per row block, which take the same FP4
-// weight unit and its UE8M0 byte as they are stored (lane c + 32h: column
-// c's unit 2s + h) and the lo codes (lane r + 32h: bytes 16h..16h+15 of row
-// r's unit 2s, then the same bytes of unit 2s + 1, and the scale of unit
-// 2s + h).  So the weights are copied and widened once for both parts, and
-// the lo part runs at the FP8 rate with no widening.
+// steps of two.  For each row block a step runs, per activation plane, two
+// v_mfma_scale_f32_32x32x64_f8f6f4 that take the FP4 weight unit and its
+// UE8M0 byte as stored (lane c + 32h: column c's unit 2s + h) and the plane's
+// codes (lane r + 32h: bytes 16h..16h+15 of row r's unit 2s, then the same
+// bytes of unit 2s + 1, and the plane's scale of unit 2s + h).  So the
+// weights are copied once and never widened, and the whole product runs at
+// the FP8 rate.
 //
-// Copies (wave w, when the tile has rows in block w: CPA): hi rows as in
-// gemm_main and lo rows (16 rows of 64 bytes per copy, from `lrowp[blk]`,
-// row 32w + 16 blk + lane / 4) and the lo scale dword of row 32w + lane % 32
-// (from `srow`), one step ahead; the wave's weights (two code halves and
-// one copy of the 64 rows' scale dwords) two steps ahead.  With an odd
-// number of units the last step's second unit is zeroed when read (lo codes
-// and weights zero, scales 1).
+// Copies (wave w, when the tile has rows in block w: CPA): the plane codes
+// (16 rows of 64 bytes per copy, plane p at p * pst bytes from `prowp[blk]`,
+// row 32w + 16 blk + lane / 4) and the scale dwords (from `srow`, row
+// 32w + lane % 32, unit 2s + lane / 32), one step ahead; the wave's weights
+// (two code halves and one copy of the 64 rows' scale dwords) two steps
+// ahead.  With an odd number of units the last step's second unit is zeroed
+// when read (codes and weights zero, scales 1).
 template <int BM, int NB, bool CPA, typename Pre, typename Epilogue>
-__device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], const uint8_t* const (&lrowp)[2],
-                                             const uint8_t* srow, int nU, const uint8_t* __restrict__ btile,
-                                             uint8_t* smem, Pre&& pre, Epilogue&& epilogue) {
+__device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], int64_t pst, const uint8_t* srow,
+                                             int nU, const uint8_t* __restrict__ btile, uint8_t* smem, Pre&& pre,
+                                             Epilogue&& epilogue) {
   constexpr int NBA = NB > 0 ? NB : 1;
-  constexpr int NA = CPA ? 7 : 0;       // copies of A per step: 4 hi, 2 lo, 1 lo scale
+  constexpr int NA = CPA ? 7 : 0;       // copies of A per step: 3 planes x 2 row halves, 1 scale
   constexpr int NW = NB > 0 ? 3 : 0;    // copies of weights per step
   constexpr int NCOPY = NA + NW;
-  constexpr int NGROUP = 5 * NB;                             // MFMA groups of a step (4 hi, 1 lo per block)
+  constexpr int NGROUP = 3 * NB;                             // MFMA groups of a step (3 planes per block)
   constexpr int NPRE = NCOPY > NGROUP ? NCOPY - NGROUP : 0;  // copies issued before them
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int nsteps = (nU + 1) / 2;
   const int full = nU / 2;
-  uint8_t* const ahi = smem;
-  uint8_t* const alo = smem + 2 * kAPlane<BM>;
-  uint8_t* const asc = alo + 2 * kLoPlane<BM>;
-  uint8_t* const bring = asc + 2 * kLoScale<BM> + wave * kBWaveHl;
+  uint8_t* const aring = smem;
+  uint8_t* const asc = smem + 2 * kPlSlot<BM>;
+  uint8_t* const bring = asc + 2 * kPlScale<BM> + wave * kBWavePl;
 
   f32x16_t acc[NBA][2];
 #pragma unroll
@@ -561,47 +565,36 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-  const int cp_lo = (lane & 7) ^ (lane >> 3);
-  const int swz = a_swz(n);
-  const int lsw = lo_swz(n);
-  auto copy_hi = [&](int s, int blk) {
+  const int psw = pl_swz(n);
+  auto copy_a = [&](int s, int p, int blk) {
     const int sc = min(s, nsteps - 1);
-    const int c = cp_lo ^ (blk & 1);
-    const int u = min(2 * sc + (c >> 2), nU - 1);
-    dma16((const uint8_t*)rowp[blk] + u * 64 + (c & 3) * 16,
-          lds_addr(ahi + (s & 1) * kAPlane<BM> + (32 * wave + 8 * blk) * kARow));
-  };
-  auto copy_lo = [&](int s, int blk) {
-    const int sc = min(s, nsteps - 1);
-    const int c = (lane & 3) ^ ((lane >> 3) & 3);  // lane l writes position l % 4 of row l / 4
+    const int c = (lane & 3) ^ pl_swz(16 * blk + (lane >> 2));  // lane l writes position l % 4 of row l / 4
     const int u = min(2 * sc + (c >> 1), nU - 1);
-    dma16(lrowp[blk] + u * 32 + (c & 1) * 16,
-          lds_addr(alo + (s & 1) * kLoPlane<BM> + (32 * wave + 16 * blk) * kLoRow));
+    dma16(prowp[blk] + p * pst + u * 32 + (c & 1) * 16,
+          lds_addr(aring + (s & 1) * kPlSlot<BM> + p * kPlPlane<BM> + (32 * wave + 16 * blk) * kPlRow));
   };
-  auto copy_ls = [&](int s) {
+  auto copy_as = [&](int s) {
     const int sc = min(s, nsteps - 1);
-    dma4(srow + 4 * (sc / 2), lds_addr(asc + (s & 1) * kLoScale<BM> + wave * 256));
+    dma4(srow + 4 * min(2 * sc + h, nU - 1), lds_addr(asc + (s & 1) * kPlScale<BM> + wave * 256));
   };
   auto b_unit = [&](int s) { return min(2 * s + h, nU - 1); };
   auto copy_b = [&](int s, int j) {
     const int cc = b_unit(min(s, nsteps - 1));
-    dma16(btile + (int64_t)cc * 1024 + (32 * j + n) * 16, lds_addr(bring + (s % kBSlots) * kBSlotHl + j * 1024));
+    dma16(btile + (int64_t)cc * 1024 + (32 * j + n) * 16, lds_addr(bring + (s % kBSlots) * kBSlotPl + j * 1024));
   };
   auto copy_bs = [&](int s) {
     const int cw = min(2 * min(s, nsteps - 1), nU - 1);
-    dma4(btile + (int64_t)nU * 1024 + (cw / 4) * 256 + lane * 4, lds_addr(bring + (s % kBSlots) * kBSlotHl + 2048));
+    dma4(btile + (int64_t)nU * 1024 + (cw / 4) * 256 + lane * 4, lds_addr(bring + (s % kBSlots) * kBSlotPl + 2048));
   };
   // Copies of a step, always issued in this order (vm_wait counts on it):
-  // with CPA, 4 hi blocks, 2 lo blocks and the lo scales for step s + 1;
+  // with CPA, the 3 planes' 2 row halves and the scale dwords for step s + 1;
   // then (waves with a weight tile) the 2 code halves and the scale dwords
   // for step s + 2.
   auto copy = [&](int s, int ci) {
-    if (CPA && ci < 4)
-      copy_hi(s + 1, ci);
-    else if (CPA && ci < 6)
-      copy_lo(s + 1, ci - 4);
+    if (CPA && ci < 6)
+      copy_a(s + 1, ci >> 1, ci & 1);
     else if (CPA && ci == 6)
-      copy_ls(s + 1);
+      copy_as(s + 1);
     else if (ci - NA < 2)
       copy_b(s + 2, ci - NA);
     else
@@ -613,55 +606,37 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
 #pragma unroll
     for (int ci = 0; ci < NPRE; ++ci) copy(s, ci);
     if constexpr (NB > 0) {
-      const uint8_t* bs = bring + (s % kBSlots) * kBSlotHl;
-      const uint8_t* hs = ahi + (s & 1) * kAPlane<BM>;
-      const uint8_t* ls = alo + (s & 1) * kLoPlane<BM>;
-      const uint8_t* ss = asc + (s & 1) * kLoScale<BM>;
+      const uint8_t* bs = bring + (s % kBSlots) * kBSlotPl;
+      const uint8_t* ps = aring + (s & 1) * kPlSlot<BM>;
+      const uint8_t* ss = asc + (s & 1) * kPlScale<BM>;
       const int c = b_unit(s);
       const bool z = tail && h;
-      u32x4 w[2];
-      uint32_t sw[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        w[j] = *(const u32x4*)(bs + j * 1024 + lane * 16);
-        sw[j] = *(const uint32_t*)(bs + 2048 + (32 * j + n) * 4);
-      }
-      int ci = NPRE;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x8_t bf[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bf[j] = z ? bf16x8_t{} : b_frag<kMXFP4>(w[j][q], b_scale<kMXFP4>(sw[j], c, q));
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-          bf16x8_t af = lds_frag((const __bf16*)(hs + (i * 32 + n) * kARow + (((4 * h + q) ^ swz) * 16)));
-          if (z) af = bf16x8_t{};
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[j], acc[i][j], 0, 0, 0);
-          if (ci < NCOPY) copy(s, ci++);
-        }
-      }
       i32x8_t bop[2];
       int sb[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        bop[j] = z ? i32x8_t{} : i32x8_t{(int)w[j][0], (int)w[j][1], (int)w[j][2], (int)w[j][3], 0, 0, 0, 0};
-        sb[j] = z ? 127 : (int)((sw[j] >> (8 * (c & 3))) & 0xFFu);
+        const i32x4_t w = *(const i32x4_t*)(bs + j * 1024 + lane * 16);
+        const uint32_t sw = *(const uint32_t*)(bs + 2048 + (32 * j + n) * 4);
+        bop[j] = z ? i32x8_t{} : i32x8_t{w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+        sb[j] = z ? 127 : (int)((sw >> (8 * (c & 3))) & 0xFFu);
       }
+      int ci = NPRE;
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const uint8_t* lr = ls + (i * 32 + n) * kLoRow;
-        const i32x4_t a0 = *(const i32x4_t*)(lr + ((h ^ lsw) * 16));
-        i32x4_t a1 = *(const i32x4_t*)(lr + (((2 + h) ^ lsw) * 16));
-        if (tail) a1 = i32x4_t{};
-        const i32x8_t aop = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        const uint32_t asw = *(const uint32_t*)(ss + i * 256 + n * 4);
-        const int sa = z ? 127 : (int)((asw >> (8 * ((2 * s + h) & 3))) & 0xFFu);
+        const uint32_t asw = *(const uint32_t*)(ss + i * 256 + lane * 4);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, sa, 0, sb[j]);
-        if (ci < NCOPY) copy(s, ci++);
+        for (int p = 0; p < 3; ++p) {
+          const uint8_t* pr = ps + p * kPlPlane<BM> + (i * 32 + n) * kPlRow;
+          const i32x4_t a0 = *(const i32x4_t*)(pr + ((h ^ psw) * 16));
+          i32x4_t a1 = *(const i32x4_t*)(pr + (((2 + h) ^ psw) * 16));
+          if (tail) a1 = i32x4_t{};
+          const i32x8_t aop = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+          const int sa = z ? 127 : (int)((asw >> (8 * p)) & 0xFFu);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, sa, 0, sb[j]);
+          if (ci < NCOPY) copy(s, ci++);
+        }
       }
       while (ci < NCOPY) copy(s, ci++);
     }
@@ -669,10 +644,11 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
 
   if constexpr (CPA) {
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) copy_hi(0, blk);
-    copy_lo(0, 0);
-    copy_lo(0, 1);
-    copy_ls(0);
+    for (int p = 0; p < 3; ++p) {
+      copy_a(0, p, 0);
+      copy_a(0, p, 1);
+    }
+    copy_as(0);
   }
   if constexpr (NB > 0) {
     copy_b(0, 0);
@@ -691,46 +667,90 @@ __device__ __forceinline__ void gemm_main_hl(const uint16_t* const (&rowp)[4], c
 }
 
 template <int BM, typename Pre, typename Epilogue>
-__device__ __forceinline__ void gemm_rows_hl(int rows, const uint16_t* const (&rowp)[4],
-                                             const uint8_t* const (&lrowp)[2], const uint8_t* srow, int nU,
-                                             const uint8_t* __restrict__ btile, bool bok, uint8_t* smem,
-                                             Pre&& pre, Epilogue&& ep) {
+__device__ __forceinline__ void gemm_rows_pl(int rows, const uint8_t* const (&prowp)[2], int64_t pst,
+                                             const uint8_t* srow, int nU, const uint8_t* __restrict__ btile,
+                                             bool bok, uint8_t* smem, Pre&& pre, Epilogue&& ep) {
   const bool cpa = 32 * (threadIdx.x >> 6) < rows;
   if constexpr (BM == 32) {
     if (!bok) {
       if (cpa)
-        gemm_main_hl<BM, 0, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+        gemm_main_pl<BM, 0, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
       else
-        gemm_main_hl<BM, 0, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+        gemm_main_pl<BM, 0, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
     } else {
       if (cpa)
-        gemm_main_hl<BM, 1, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+        gemm_main_pl<BM, 1, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
       else
-        gemm_main_hl<BM, 1, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+        gemm_main_pl<BM, 1, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
     }
   } else if (!bok) {
     if (cpa)
-      gemm_main_hl<BM, 0, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+      gemm_main_pl<BM, 0, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
     else
-      gemm_main_hl<BM, 0, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+      gemm_main_pl<BM, 0, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
   } else if (rows > 96) {
-    gemm_main_hl<BM, 4, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+    gemm_main_pl<BM, 4, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
   } else if (rows > 64) {
     if (cpa)
-      gemm_main_hl<BM, 3, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+      gemm_main_pl<BM, 3, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
     else
-      gemm_main_hl<BM, 3, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+      gemm_main_pl<BM, 3, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
   } else if (rows > 32) {
     if (cpa)
-      gemm_main_hl<BM, 2, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+      gemm_main_pl<BM, 2, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
     else
-      gemm_main_hl<BM, 2, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+      gemm_main_pl<BM, 2, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
   } else {
     if (cpa)
-      gemm_main_hl<BM, 1, true>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+      gemm_main_pl<BM, 1, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
     else
-      gemm_main_hl<BM, 1, false>(rowp, lrowp, srow, nU, btile, smem, pre, ep);
+      gemm_main_pl<BM, 1, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
   }
+}
+
+// bf16(v) as a float (round to nearest even).
+__device__ __forceinline__ float bf16_value(float v) { return __uint_as_float((uint32_t)f32_to_bf16_rne(v) << 16); }
+
+// One plane of an MXFP8 block of 32 values held 16 per lane by lanes 2r and
+// 2r + 1: returns the block's scale byte and sets this lane's 16 codes (w,
+// four to a dword in value order).  The shared exponent is the OCP one,
+// raised by one where that would cap the block's largest value at 448, so
+// that every value is rounded to nearest and none is clamped.  A block
+// holding a NaN or an infinity gets scale byte 255 and codes 0x7F.  With
+// `keep`, v becomes what the plane leaves of it (exact: a value and its
+// rounding are within a factor of two); a non-finite block is left as it
+// is, so the next plane is non-finite too.
+__device__ __forceinline__ uint32_t mx_block16(float (&v)[16], uint32_t (&w)[4], bool keep) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) m = max(m, __float_as_uint(v[q]) & 0x7FFFFFFFu);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  uint32_t sb = mx_scale_byte(m);
+  if (sb == 255u) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = 0x7F7F7F7Fu;
+    return sb;
+  }
+  if (__uint_as_float(m) * mx_inv_scale(sb) > 448.0f) ++sb;
+  const float inv = mx_inv_scale(sb);
+  const float sc = __uint_as_float(sb ? sb << 23 : 0x00400000u);  // 2^(sb - 127)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = v[4 * q + e] * inv;
+    // v_cvt_pk_fp8_f32: two values to E4M3, rounded to nearest even (|x| <= 448)
+    int word = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    word = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], word, true);
+    w[q] = (uint32_t)word;
+    if (keep) {
+      v[4 * q] = (x[0] - __builtin_amdgcn_cvt_f32_fp8(word, 0)) * sc;
+      v[4 * q + 1] = (x[1] - __builtin_amdgcn_cvt_f32_fp8(word, 1)) * sc;
+      v[4 * q + 2] = (x[2] - __builtin_amdgcn_cvt_f32_fp8(word, 2)) * sc;
+      v[4 * q + 3] = (x[3] - __builtin_amdgcn_cvt_f32_fp8(word, 3)) * sc;
+    }
+  }
+  return sb;
 }
 
 // Occupancy of the grouped GEMMs (waves per SIMD): tiles of 32 rows need a
@@ -772,14 +792,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFc1Wa
   }
   const float g13 = FMT == kNVFP4 ? ((const float*)prep)[e] : 1.0f;
   const int n = 32 * b + (lane & 31);
-  // a = f(gate, up) as hi/lo planes; a non-gated activation (relu2) writes
-  // both halves as outputs, at columns n and Ip + n.  NVFP4: hi = bf16(a)
-  // and lo = bf16(a - hi), two bf16 planes.  MXFP4: the hi plane, and lo =
-  // a - hi as MXFP8 (codes `aq`, scale rows `as` of `ass` bytes): per 32-row
-  // block the lo values go to this wave's part of the (now idle) A ring as
-  // 32 rows x 32 columns (row stride 144 B); lane l then takes row l / 2,
-  // columns 16 (l % 2) .. + 15, whose block of 32 is its own 16 values and
-  // its neighbour's, and stores its 16 codes at once.
+  // a = f(gate, up); a non-gated activation (relu2) writes both halves as
+  // outputs, at columns n and Ip + n.  NVFP4: hi = bf16(a) and lo =
+  // bf16(a - hi), two bf16 planes.  MXFP4: three MXFP8 planes (codes `aq`,
+  // plane p at p * `plane` bytes; one scale dword per row and 32 columns at
+  // `as`, `ass` bytes per row, byte p for plane p): plane 0 is hi = bf16(a)
+  // rounded to MXFP8, plane 1 what that leaves of hi, plane 2 lo = a - hi.
+  // Per 32-row block the values of a go to this wave's part of the (now idle)
+  // A ring as 32 rows x 32 columns (row stride 144 B); lane l then takes row
+  // l / 2, columns 16 (l % 2) .. + 15, whose block of 32 is its own 16 values
+  // and its neighbour's, and stores its 16 codes of each plane at once.
   auto epilogue_mx = [&](auto& acc) __attribute__((always_inline)) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
     constexpr int kStride = 36;  // dwords per staged row
@@ -793,43 +815,39 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFc1Wa
         for (int jj = 0; jj < (K == kActRelu2 ? 2 : 1); ++jj) {
           const int col0 = jj ? L.Ip : 0;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = i * 32 + acc_row(r, lane);
-            const float a = K == kActRelu2 && jj ? act_of<K>(L.act, acc[i][1][r], 0.0f)
-                                                 : act_of<K>(L.act, acc[i][0][r], acc[i][1][r]);
-            const uint16_t hi = f32_to_bf16_rne(a);
-            if (row < rows) act[(int64_t)(gs + row) * L.I + col0 + n] = hi;
-            st[acc_row(r, lane) * kStride + (lane & 31)] = a - __uint_as_float((uint32_t)hi << 16);
-          }
+          for (int r = 0; r < 16; ++r)
+            st[acc_row(r, lane) * kStride + (lane & 31)] =
+                K == kActRelu2 && jj ? act_of<K>(L.act, acc[i][1][r], 0.0f)
+                                     : act_of<K>(L.act, acc[i][0][r], acc[i][1][r]);
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging stores are done
           __builtin_amdgcn_wave_barrier();
+          // this lane's 16 staged values: hi = bf16(a) (lo = false) or a - hi
+          // (read again rather than kept, which leaves registers for the
+          // 32-row tiles' four waves per SIMD)
           float v[16];
+          auto take = [&](bool lo) __attribute__((always_inline)) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 f = *(const float4*)(st + rr * kStride + 16 * half + 4 * q);
-            v[4 * q] = f.x;
-            v[4 * q + 1] = f.y;
-            v[4 * q + 2] = f.z;
-            v[4 * q + 3] = f.w;
-          }
-          uint32_t m = 0;
+            for (int q = 0; q < 4; ++q) {
+              const float4 f = *(const float4*)(st + rr * kStride + 16 * half + 4 * q);
+              const float g[4] = {f.x, f.y, f.z, f.w};
 #pragma unroll
-          for (int q = 0; q < 16; ++q) m = max(m, __float_as_uint(v[q]) & 0x7FFFFFFFu);
-          m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-          const uint32_t sb = mx_scale_byte(m);
-          uint32_t w[4] = {0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
-          if (sb != 255u) {
-            const float inv = mx_inv_scale(sb);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              w[q] = e4m3_code(v[4 * q] * inv) | (e4m3_code(v[4 * q + 1] * inv) << 8) |
-                     (e4m3_code(v[4 * q + 2] * inv) << 16) | (e4m3_code(v[4 * q + 3] * inv) << 24);
-          }
+              for (int e = 0; e < 4; ++e) v[4 * q + e] = lo ? g[e] - bf16_value(g[e]) : bf16_value(g[e]);
+            }
+          };
           const int row = i * 32 + rr;
           const int c0 = col0 + 32 * b;
+          uint8_t* dst = aq + (int64_t)(gs + row) * L.I + c0 + 16 * half;
+          uint32_t w[4];
+          take(false);
+          const uint32_t s0 = mx_block16(v, w, true);
+          if (row < rows) *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+          const uint32_t s1 = mx_block16(v, w, false);
+          if (row < rows) *(uint4*)(dst + plane) = make_uint4(w[0], w[1], w[2], w[3]);
+          take(true);
+          const uint32_t s2 = mx_block16(v, w, false);
           if (row < rows) {
-            *(uint4*)(aq + (int64_t)(gs + row) * L.I + c0 + 16 * half) = make_uint4(w[0], w[1], w[2], w[3]);
-            if (half == 0) as[(int64_t)(gs + row) * ass + c0 / 32] = (uint8_t)sb;
+            *(uint4*)(dst + 2 * plane) = make_uint4(w[0], w[1], w[2], w[3]);
+            if (half == 0) *(uint32_t*)(as + (int64_t)(gs + row) * ass + c0 / 8) = s0 | (s1 << 8) | (s2 << 16);
           }
           __builtin_amdgcn_wave_barrier();  // the next block's staging stores come after these reads
           __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -881,7 +899,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
              const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, const uint8_t* __restrict__ aq,
              const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kHlLds<BM> : kGemmLds<BM, true>];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kPlLds<BM> : kGemmLds<BM, true>];
   __shared__ float wrow[BM];
   const GroupTile id = group_tile(fc2_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
@@ -918,24 +936,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
       }
     }
   };
-  // hi rows this lane copies: rows 32 wave + 8 blk + lane / 8 of the tile
-  // (grouped rows past the tile repeat its last row)
-  const uint16_t* rowp[4];
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk)
-    rowp[blk] = act + (int64_t)(gs + min(32 * wave + 8 * blk + (lane >> 3), rows - 1)) * L.I;
   const uint8_t* btile = prep + fc2_tile_offset(L, e, bok ? hb : 0);
   if constexpr (FMT == kMXFP4) {
-    // one pass: the hi plane and the MXFP8 lo codes (rows 32 wave + 16 blk +
-    // lane / 4) with their scale rows (row 32 wave + lane % 32)
-    const uint8_t* lrowp[2];
+    // one pass over the three MXFP8 planes: codes of rows 32 wave + 16 blk +
+    // lane / 4, the scale dwords of row 32 wave + lane % 32 (grouped rows
+    // past the tile repeat its last row)
+    const uint8_t* prowp[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
-      lrowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
+      prowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
     const uint8_t* srow = as + (int64_t)(gs + min(32 * wave + (lane & 31), rows - 1)) * ass;
-    gemm_rows_hl<BM>(rows, rowp, lrowp, srow, L.nC2, btile, bok, smem, pre, epilogue);
+    gemm_rows_pl<BM>(rows, prowp, plane, srow, L.nC2, btile, bok, smem, pre, epilogue);
   } else {
-    // two passes over K: the hi activation plane, then the lo plane
+    // two passes over K: the hi activation plane, then the lo plane; rows
+    // 32 wave + 8 blk + lane / 8 of the tile
+    const uint16_t* rowp[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+      rowp[blk] = act + (int64_t)(gs + min(32 * wave + 8 * blk + (lane >> 3), rows - 1)) * L.I;
     gemm_rows<FMT, BM, true>(rows, rowp, plane, 2 * L.nC2, btile, bok, L.nC2, smem, pre, epilogue);
   }
 }
@@ -1002,10 +1020,12 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   float* gw = (float*)(ws + W.gw);
   int* tile_expert = (int*)(ws + W.tile_expert);
   uint16_t* act = (uint16_t*)(ws + W.act);
-  const int64_t plane = (W.aq - W.act) / 2;  // elements from the hi plane to the lo plane (NVFP4)
-  uint8_t* aq = ws + W.aq;                   // MXFP4: the lo part as MXFP8
+  // NVFP4: elements from the hi plane to the lo plane; MXFP4: bytes from one
+  // MXFP8 plane (aq, scale dwords as) to the next
+  const int64_t plane = FMT == kMXFP4 ? W.pst : (W.aq - W.act) / 2;
+  uint8_t* aq = ws + W.aq;
   uint8_t* as = ws + W.as;
-  const int ass = a8_scale_stride(L.I);
+  const int ass = 4 * L.nC2;  // bytes of a row's scale dwords
   float* y = (float*)(ws + W.y);
   // m-tiles of bm rows: at most one partial tile per expert beyond R / bm full ones
   const int bm = prefill_bm(L, R, a8);
