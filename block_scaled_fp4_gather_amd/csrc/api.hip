@@ -105,7 +105,7 @@ moe_fp4_status make_plan(const moe_fp4_desc* desc, const Layout& L, int32_t M,
       return MOE_FP4_EINVAL;
   }
   if (prefill_routes(desc) > moe::kPrefillMaxRoutes ||
-      moe::prefill_max_workgroups(L, prefill_routes(desc), act_mxfp8(desc)) >= ((int64_t)1 << 31))
+      moe::prefill_max_workgroups(L, prefill_routes(desc)) >= ((int64_t)1 << 31))
     return MOE_FP4_EUNSUPPORTED;
   const int k = desc->top_k;
   // The decode path takes any M in chunks of at most decode_max_tokens(k)

@@ -89,18 +89,18 @@ __host__ __device__ inline int fc1_blocks(const Layout& L) { return (L.nB1 + 3) 
 __host__ __device__ inline int fc2_blocks(const Layout& L) { return (L.nB2 + 3) / 4; }
 
 // Rows of the grouped GEMMs' m-tiles for `routes` routes: 128, or 32 when
-// the experts get few routes each (bf16 activations only), where most
-// 128-row tiles would hold a few rows and three smaller workgroups per CU
-// keep more weight copies in flight.
-inline int prefill_bm(const Layout& L, int64_t routes, bool a8) {
-  return !a8 && routes <= (int64_t)kSparseRoutesPerExpert * L.E ? 32 : kGemmBM;
+// the experts get few routes each, where most 128-row tiles would hold a few
+// rows and three or four smaller workgroups per CU keep more weight copies
+// in flight.
+inline int prefill_bm(const Layout& L, int64_t routes) {
+  return routes <= (int64_t)kSparseRoutesPerExpert * L.E ? 32 : kGemmBM;
 }
 
 // Workgroups of the larger grouped GEMM grid for up to `routes` routes (a
 // call with fewer routes may take 32-row tiles); the grid must stay below
 // 2^31 workgroups.
-inline int64_t prefill_max_workgroups(const Layout& L, int64_t routes, bool a8) {
-  const int64_t bm = a8 ? kGemmBM : 32;
+inline int64_t prefill_max_workgroups(const Layout& L, int64_t routes) {
+  const int64_t bm = 32;
   const int64_t mt = (routes + bm - 1) / bm + L.E;
   const int64_t nb1 = (L.I + 63) / 64, nb2 = (L.H + 127) / 128;
   return mt * (nb1 > nb2 ? nb1 : nb2) + 8;
@@ -117,10 +117,10 @@ hipError_t launch_prefill(const Layout& L, const uint8_t* prep, const uint16_t* 
                           const PrefillWs& W, int phases, bool a8, hipStream_t st);
 
 // The A8 GEMM launches (x quantisation + FC1, FC2) over a grid of `grid`
-// workgroups (the same tile grids as the bf16 GEMMs).
+// workgroups of m-tiles of `bm` rows (the same tile grids as the bf16 GEMMs).
 hipError_t launch_fc1_a8(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k, uint8_t* ws,
-                         const PrefillWs& W, unsigned grid, hipStream_t st);
-hipError_t launch_fc2_a8(const Layout& L, const uint8_t* prep, const float* tw, uint8_t* ws, const PrefillWs& W,
+                         const PrefillWs& W, int bm, unsigned grid, hipStream_t st);
+hipError_t launch_fc2_a8(const Layout& L, const uint8_t* prep, uint8_t* ws, const PrefillWs& W, int bm,
                          unsigned grid, hipStream_t st);
 
 }  // namespace moe

@@ -30,6 +30,7 @@
 
 #include "act.h"
 #include "decode.h"
+#include "gemm_planes.h"
 #include "gemm_util.h"
 #include "layout.h"
 #include "mxfp8.h"
@@ -498,216 +499,6 @@ __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp
   }
 }
 
-// LDS of the MXFP4 FC2 workgroup, whose activations are three MXFP8 planes:
-// an A ring of 2 slots x 3 planes x BM rows x 64 bytes (the 64 FP8 values of
-// a step; 16-byte chunk c of row r at position c ^ pl_swz(r)); an A scale
-// ring of 2 slots x BM / 32 waves x 256 bytes (lane n + 32h of wave w: the
-// scale dword of row 32w + n for unit 2s + h, one byte per plane); a weight
-// ring of 3 slots x 4 waves x (2 x 1 KiB codes + 256 B: the scale dword of
-// each of the 64 weight rows, which covers both units of a step): 77 KiB for
-// 128-row tiles, two workgroups per CU.
-constexpr int kPlRow = 64;
-template <int BM>
-constexpr int kPlPlane = BM * kPlRow;  // 8 KiB for 128 rows
-template <int BM>
-constexpr int kPlSlot = 3 * kPlPlane<BM>;
-template <int BM>
-constexpr int kPlScale = BM / 32 * 256;
-constexpr int kBWavePl = 2 * 1024 + 256;
-constexpr int kBSlotPl = 4 * kBWavePl;
-template <int BM>
-constexpr int kPlLds = 2 * kPlSlot<BM> + 2 * kPlScale<BM> + kBSlots * kBSlotPl;
-
-// Position swizzle of a 64-byte plane row: for every 8, 16 or 32 lanes that
-// read one chunk each of rows n = lane % 32 (the same chunk index) the 16-byte
-// units land in distinct LDS banks.
-__device__ __forceinline__ int pl_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
-
-// FC2 main loop of MXFP4 layers for one 128-row x 256-column output tile,
-// followed by `epilogue(acc)`: one pass over the nU units of K (= I / 32) in
-// steps of two.  For each row block a step runs, per activation plane, two
-// v_mfma_scale_f32_32x32x64_f8f6f4 that take the FP4 weight unit and its
-// UE8M0 byte as stored (lane c + 32h: column c's unit 2s + h) and the plane's
-// codes (lane r + 32h: bytes 16h..16h+15 of row r's unit 2s, then the same
-// bytes of unit 2s + 1, and the plane's scale of unit 2s + h).  So the
-// weights are copied once and never widened, and the whole product runs at
-// the FP8 rate.
-//
-// Copies (wave w, when the tile has rows in block w: CPA): the plane codes
-// (16 rows of 64 bytes per copy, plane p at p * pst bytes from `prowp[blk]`,
-// row 32w + 16 blk + lane / 4) and the scale dwords (from `srow`, row
-// 32w + lane % 32, unit 2s + lane / 32), one step ahead; the wave's weights
-// (two code halves and one copy of the 64 rows' scale dwords) two steps
-// ahead.  With an odd number of units the last step's second unit is zeroed
-// when read (codes and weights zero, scales 1).
-template <int BM, int NB, bool CPA, typename Pre, typename Epilogue>
-__device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], int64_t pst, const uint8_t* srow,
-                                             int nU, const uint8_t* __restrict__ btile, uint8_t* smem, Pre&& pre,
-                                             Epilogue&& epilogue) {
-  constexpr int NBA = NB > 0 ? NB : 1;
-  constexpr int NA = CPA ? 7 : 0;       // copies of A per step: 3 planes x 2 row halves, 1 scale
-  constexpr int NW = NB > 0 ? 3 : 0;    // copies of weights per step
-  constexpr int NCOPY = NA + NW;
-  constexpr int NGROUP = 3 * NB;                             // MFMA groups of a step (3 planes per block)
-  constexpr int NPRE = NCOPY > NGROUP ? NCOPY - NGROUP : 0;  // copies issued before them
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int n = lane & 31, h = lane >> 5;
-  const int nsteps = (nU + 1) / 2;
-  const int full = nU / 2;
-  uint8_t* const aring = smem;
-  uint8_t* const asc = smem + 2 * kPlSlot<BM>;
-  uint8_t* const bring = asc + 2 * kPlScale<BM> + wave * kBWavePl;
-
-  f32x16_t acc[NBA][2];
-#pragma unroll
-  for (int i = 0; i < NBA; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
-
-  const int psw = pl_swz(n);
-  auto copy_a = [&](int s, int p, int blk) {
-    const int sc = min(s, nsteps - 1);
-    const int c = (lane & 3) ^ pl_swz(16 * blk + (lane >> 2));  // lane l writes position l % 4 of row l / 4
-    const int u = min(2 * sc + (c >> 1), nU - 1);
-    dma16(prowp[blk] + p * pst + u * 32 + (c & 1) * 16,
-          lds_addr(aring + (s & 1) * kPlSlot<BM> + p * kPlPlane<BM> + (32 * wave + 16 * blk) * kPlRow));
-  };
-  auto copy_as = [&](int s) {
-    const int sc = min(s, nsteps - 1);
-    dma4(srow + 4 * min(2 * sc + h, nU - 1), lds_addr(asc + (s & 1) * kPlScale<BM> + wave * 256));
-  };
-  auto b_unit = [&](int s) { return min(2 * s + h, nU - 1); };
-  auto copy_b = [&](int s, int j) {
-    const int cc = b_unit(min(s, nsteps - 1));
-    dma16(btile + (int64_t)cc * 1024 + (32 * j + n) * 16, lds_addr(bring + (s % kBSlots) * kBSlotPl + j * 1024));
-  };
-  auto copy_bs = [&](int s) {
-    const int cw = min(2 * min(s, nsteps - 1), nU - 1);
-    dma4(btile + (int64_t)nU * 1024 + (cw / 4) * 256 + lane * 4, lds_addr(bring + (s % kBSlots) * kBSlotPl + 2048));
-  };
-  // Copies of a step, always issued in this order (vm_wait counts on it):
-  // with CPA, the 3 planes' 2 row halves and the scale dwords for step s + 1;
-  // then (waves with a weight tile) the 2 code halves and the scale dwords
-  // for step s + 2.
-  auto copy = [&](int s, int ci) {
-    if (CPA && ci < 6)
-      copy_a(s + 1, ci >> 1, ci & 1);
-    else if (CPA && ci == 6)
-      copy_as(s + 1);
-    else if (ci - NA < 2)
-      copy_b(s + 2, ci - NA);
-    else
-      copy_bs(s + 2);
-  };
-  auto step = [&](int s, bool tail) {
-    vm_wait<NW>();    // this wave's copies for step s have landed (the weights of s + 1 may not)
-    __syncthreads();  // everyone's have; everyone is done with step s - 1
-#pragma unroll
-    for (int ci = 0; ci < NPRE; ++ci) copy(s, ci);
-    if constexpr (NB > 0) {
-      const uint8_t* bs = bring + (s % kBSlots) * kBSlotPl;
-      const uint8_t* ps = aring + (s & 1) * kPlSlot<BM>;
-      const uint8_t* ss = asc + (s & 1) * kPlScale<BM>;
-      const int c = b_unit(s);
-      const bool z = tail && h;
-      i32x8_t bop[2];
-      int sb[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const i32x4_t w = *(const i32x4_t*)(bs + j * 1024 + lane * 16);
-        const uint32_t sw = *(const uint32_t*)(bs + 2048 + (32 * j + n) * 4);
-        bop[j] = z ? i32x8_t{} : i32x8_t{w[0], w[1], w[2], w[3], 0, 0, 0, 0};
-        sb[j] = z ? 127 : (int)((sw >> (8 * (c & 3))) & 0xFFu);
-      }
-      int ci = NPRE;
-#pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const uint32_t asw = *(const uint32_t*)(ss + i * 256 + lane * 4);
-#pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          const uint8_t* pr = ps + p * kPlPlane<BM> + (i * 32 + n) * kPlRow;
-          const i32x4_t a0 = *(const i32x4_t*)(pr + ((h ^ psw) * 16));
-          i32x4_t a1 = *(const i32x4_t*)(pr + (((2 + h) ^ psw) * 16));
-          if (tail) a1 = i32x4_t{};
-          const i32x8_t aop = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-          const int sa = z ? 127 : (int)((asw >> (8 * p)) & 0xFFu);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, sa, 0, sb[j]);
-          if (ci < NCOPY) copy(s, ci++);
-        }
-      }
-      while (ci < NCOPY) copy(s, ci++);
-    }
-  };
-
-  if constexpr (CPA) {
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      copy_a(0, p, 0);
-      copy_a(0, p, 1);
-    }
-    copy_as(0);
-  }
-  if constexpr (NB > 0) {
-    copy_b(0, 0);
-    copy_b(0, 1);
-    copy_bs(0);
-    copy_b(1, 0);
-    copy_b(1, 1);
-    copy_bs(1);
-  }
-  for (int s = 0; s < full; ++s) step(s, false);
-  if (full < nsteps) step(full, true);
-  pre();         // LDS the epilogue reads, written before the barrier
-  vm_wait<0>();  // no copy may land after the workgroup's LDS is released
-  __syncthreads();
-  if constexpr (NB > 0) epilogue(acc);
-}
-
-template <int BM, typename Pre, typename Epilogue>
-__device__ __forceinline__ void gemm_rows_pl(int rows, const uint8_t* const (&prowp)[2], int64_t pst,
-                                             const uint8_t* srow, int nU, const uint8_t* __restrict__ btile,
-                                             bool bok, uint8_t* smem, Pre&& pre, Epilogue&& ep) {
-  const bool cpa = 32 * (threadIdx.x >> 6) < rows;
-  if constexpr (BM == 32) {
-    if (!bok) {
-      if (cpa)
-        gemm_main_pl<BM, 0, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
-      else
-        gemm_main_pl<BM, 0, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
-    } else {
-      if (cpa)
-        gemm_main_pl<BM, 1, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
-      else
-        gemm_main_pl<BM, 1, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
-    }
-  } else if (!bok) {
-    if (cpa)
-      gemm_main_pl<BM, 0, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
-    else
-      gemm_main_pl<BM, 0, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
-  } else if (rows > 96) {
-    gemm_main_pl<BM, 4, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
-  } else if (rows > 64) {
-    if (cpa)
-      gemm_main_pl<BM, 3, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
-    else
-      gemm_main_pl<BM, 3, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
-  } else if (rows > 32) {
-    if (cpa)
-      gemm_main_pl<BM, 2, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
-    else
-      gemm_main_pl<BM, 2, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
-  } else {
-    if (cpa)
-      gemm_main_pl<BM, 1, true>(prowp, pst, srow, nU, btile, smem, pre, ep);
-    else
-      gemm_main_pl<BM, 1, false>(prowp, pst, srow, nU, btile, smem, pre, ep);
-  }
-}
-
 // bf16(v) as a float (round to nearest even).
 __device__ __forceinline__ float bf16_value(float v) { return __uint_as_float((uint32_t)f32_to_bf16_rne(v) << 16); }
 
@@ -899,7 +690,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
              const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, const uint8_t* __restrict__ aq,
              const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kPlLds<BM> : kGemmLds<BM, true>];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kPlLds<BM, 3> : kGemmLds<BM, true>];
   __shared__ float wrow[BM];
   const GroupTile id = group_tile(fc2_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
@@ -946,7 +737,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
     for (int blk = 0; blk < 2; ++blk)
       prowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
     const uint8_t* srow = as + (int64_t)(gs + min(32 * wave + (lane & 31), rows - 1)) * ass;
-    gemm_rows_pl<BM>(rows, prowp, plane, srow, L.nC2, btile, bok, smem, pre, epilogue);
+    gemm_rows_pl<BM, 3, false>(rows, prowp, plane, srow, L.nC2, btile, bok, smem, pre, epilogue);
   } else {
     // two passes over K: the hi activation plane, then the lo plane; rows
     // 32 wave + 8 blk + lane / 8 of the tile
@@ -1028,7 +819,7 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   const int ass = 4 * L.nC2;  // bytes of a row's scale dwords
   float* y = (float*)(ws + W.y);
   // m-tiles of bm rows: at most one partial tile per expert beyond R / bm full ones
-  const int bm = prefill_bm(L, R, a8);
+  const int bm = prefill_bm(L, R);
   const unsigned mt = (unsigned)((R + bm - 1) / bm + L.E);
   if (phases & 5) {
     if (R <= kRouteBlock) {
@@ -1045,7 +836,7 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   }
   const unsigned grid1 = grid8((int64_t)mt * fc1_blocks(L)), grid2 = grid8((int64_t)mt * fc2_blocks(L));
   if ((phases & 1) && a8) {
-    const hipError_t err = launch_fc1_a8(L, prep, x, M, k, ws, W, grid1, st);
+    const hipError_t err = launch_fc1_a8(L, prep, x, M, k, ws, W, bm, grid1, st);
     if (err != hipSuccess) return err;
   } else if (phases & 1) {
     if (bm == 32)
@@ -1058,7 +849,7 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
                          (const int*)perm, act, plane, aq, as, ass);
   }
   if ((phases & 2) && a8) {
-    const hipError_t err = launch_fc2_a8(L, prep, tw, ws, W, grid2, st);
+    const hipError_t err = launch_fc2_a8(L, prep, ws, W, bm, grid2, st);
     if (err != hipSuccess) return err;
   } else if (phases & 2) {
     if (bm == 32)

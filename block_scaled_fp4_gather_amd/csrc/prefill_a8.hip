@@ -1,28 +1,23 @@
 // Grouped GEMMs of the W4A8-MX variant: MXFP8 activation rows times MXFP4
 // weights on the CDNA4 scaled matrix instruction
 // v_mfma_scale_f32_32x32x64_f8f6f4 (A: E4M3, B: E2M1, one E8M0 scale per 32
-// K values of each row and column, fp32 accumulation).  The FP4 weights and
-// their UE8M0 bytes enter the instruction as stored, with no decode (b12x
-// PR #22, Measured table: the A8 path keeps its prefill advantage; the
-// dynamic path quantises activations to MXFP8).
-//
-// Operand layout of the instruction (one wave, 64 lanes, K = 64 as two
-// 32-value blocks): lane c + 32h holds B column c's block h (32 E2M1 values
-// in K order, 16 bytes) and that block's scale; lane r + 32h holds A row r's
-// bytes 16h..16h+15 of block 0 followed by the same bytes of block 1, and
-// the scale of row r's block h.  So a lane's B operand is one 16-byte unit
-// of the prepared weights (one row, 32 K values) and its scale byte.
+// K values of each row and column, fp32 accumulation): 128-row m-tiles in the
+// loop below, 32-row ones in the plane loop with one plane.  The FP4 weights and their UE8M0 bytes enter the
+// instruction as stored, with no decode (b12x PR #22, Measured table: the A8
+// path keeps its prefill advantage; the dynamic path quantises activations to
+// MXFP8).
 //
 //   fc1_gemm_a8  x rows (MXFP8, quantised once per token) gathered by
 //                grouped row, the activation f(gate, up) in fp32 (relu2:
 //                both halves as outputs), quantised to MXFP8 in blocks of 32
 //                along I (the 32 columns of one wave's prepared tile are one
 //                block) -> act codes and scales;
-//   fc2_gemm_a8  act rows times W2, times the route's router weight -> the
-//                same fp32 rows that the combine sums.
+//   fc2_gemm_a8  act rows times W2, times the grouped row's router weight ->
+//                the same fp32 rows that the combine sums.
 #include <hip/hip_runtime.h>
 
 #include "act.h"
+#include "gemm_planes.h"
 #include "gemm_util.h"
 #include "layout.h"
 #include "mxfp8.h"
@@ -51,7 +46,10 @@ __device__ __forceinline__ i32x4_t lds16(const uint8_t* p) { return *(const i32x
 __device__ __forceinline__ int scale_byte(uint32_t w, int b) { return (int)((w >> (8 * b)) & 0xFFu); }
 
 // Main loop for one 128-row x 256-column output tile of the A8 GEMMs,
-// followed by `epilogue(acc)`.  K runs over nU units of 32 values in steps
+// followed by `epilogue(acc)` (32-row tiles take the plane loop, whose steps
+// of 64 K values suit their single row block; with four row blocks this
+// loop's steps of 128 share each barrier among twice the MFMAs, measured 12%
+// faster on full tiles).  K runs over nU units of 32 values in steps
 // of 4 units; MFMA t (0, 1) of a step takes units 2t and 2t + 1.
 //
 // Wave w owns the 64 columns of one prepared weight tile (`btile`, nU
@@ -199,28 +197,30 @@ __device__ __forceinline__ void gemm_rows_a8(int rows, const uint8_t* const (&ro
     gemm_main_a8<1>(rowp, srow, nU, btile, smem, ep);
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// Occupancy (waves per SIMD): two 128-row workgroups per CU (the
+// accumulators of four row blocks), four of 32 rows.
+template <int BM>
+constexpr int kA8Waves = BM == 32 ? 4 : 2;
+
+template <int BM>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kA8Waves<BM>)))
     fc1_gemm_a8(const uint8_t* __restrict__ prep, const Layout L, const uint8_t* __restrict__ xq,
                 const uint8_t* __restrict__ xs, int xss, int k, const int* __restrict__ counts,
                 const int* __restrict__ grp_start, const int* __restrict__ tile_start,
                 const int* __restrict__ tile_expert, const int* __restrict__ perm, uint8_t* __restrict__ aq,
                 uint8_t* __restrict__ as, int ass) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds8];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[BM == 32 ? kPlLds<32, 1> : kGemmLds8];
   const GroupTile id = group_tile(fc1_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
   const int e = id.e;
-  const int m0 = (id.gm - tile_start[e]) * kGemmBM;
-  const int rows = min(kGemmBM, counts[e] - m0);
+  const int m0 = (id.gm - tile_start[e]) * BM;
+  const int rows = min(BM, counts[e] - m0);
   const int gs = grp_start[e] + m0;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int b = 4 * id.nb + wave;  // prepared FC1 tile: gate columns 32b.. and the matching up columns
   const bool bok = b < L.nB1;
-  const uint8_t* rowp[4];
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-    const int r = min(32 * wave + 8 * blk + (lane >> 3), rows - 1);
-    rowp[blk] = xq + (int64_t)(perm[gs + r] / k) * L.H;
-  }
+  // the scale row of row 32 wave + lane % 32 of the tile (grouped rows past
+  // the tile repeat its last row), a token's
   const uint8_t* srow = xs + (int64_t)(perm[gs + min(32 * wave + (lane & 31), rows - 1)] / k) * xss;
   // Epilogue, per 32-row block: a = f(gate, up) in fp32 goes to this wave's
   // part of the (now idle) A ring as 32 rows x 32 columns (row stride 144 B),
@@ -229,13 +229,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
   // in one 16-byte store.  A non-gated activation (relu2) makes two such
   // blocks per row block, columns 32b.. from the first accumulator and
   // Ip + 32b.. from the second.
-  auto epilogue = [&](auto& acc) {
+  auto epilogue = [&](auto& acc) __attribute__((always_inline)) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
     constexpr int kStride = 36;  // dwords per staged row
     float* st = (float*)(smem + wave * 32 * kStride * 4);
     const int n = lane & 31;
     const int rr = lane >> 1, half = lane & 1;
-    with_act_kind(L.act.kind, [&](auto kind) {
+    with_act_kind(L.act.kind, [&](auto kind) __attribute__((always_inline)) {
     constexpr int K = decltype(kind)::value;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -281,32 +281,50 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
     }
     });
   };
-  gemm_rows_a8(rows, rowp, srow, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, smem, epilogue);
+  const uint8_t* btile = prep + fc1_tile_offset(L, e, bok ? b : 0);
+  if constexpr (BM == 32) {
+    // x rows this lane copies: rows 32 wave + 16 blk + lane / 4 of the tile
+    const uint8_t* prowp[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+      prowp[blk] = xq + (int64_t)(perm[gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)] / k) * L.H;
+    gemm_rows_pl<BM, 1, true>(rows, prowp, 0, srow, L.nC1, btile, bok, smem, [] {}, epilogue);
+  } else {
+    // x rows this lane copies: rows 32 wave + 8 blk + lane / 8 of the tile
+    const uint8_t* rowp[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+      rowp[blk] = xq + (int64_t)(perm[gs + min(32 * wave + 8 * blk + (lane >> 3), rows - 1)] / k) * L.H;
+    gemm_rows_a8(rows, rowp, srow, L.nC1, btile, bok, smem, epilogue);
+  }
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-    fc2_gemm_a8(const uint8_t* __restrict__ prep, const Layout L, const float* __restrict__ tw,
+template <int BM>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kA8Waves<BM>)))
+    fc2_gemm_a8(const uint8_t* __restrict__ prep, const Layout L, const float* __restrict__ gw,
                 const int* __restrict__ counts, const int* __restrict__ grp_start,
                 const int* __restrict__ tile_start, const int* __restrict__ tile_expert,
-                const int* __restrict__ perm, const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kGemmLds8];
-  __shared__ float wrow[kGemmBM];
+                const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[BM == 32 ? kPlLds<32, 1> : kGemmLds8];
+  __shared__ float wrow[BM];
   const GroupTile id = group_tile(fc2_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
   const int e = id.e;
-  const int m0 = (id.gm - tile_start[e]) * kGemmBM;
-  const int rows = min(kGemmBM, counts[e] - m0);
+  const int m0 = (id.gm - tile_start[e]) * BM;
+  const int rows = min(BM, counts[e] - m0);
   const int gs = grp_start[e] + m0;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int hb = 4 * id.nb + wave;  // prepared FC2 tile: output columns 64hb..64hb+63
   const bool bok = hb < L.nB2;
-  if (t < kGemmBM) wrow[t] = t < rows ? tw[perm[gs + t]] : 0.0f;
-  const uint8_t* rowp[4];
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk)
-    rowp[blk] = aq + (int64_t)(gs + min(32 * wave + 8 * blk + (lane >> 3), rows - 1)) * L.I;
+  // the router weights of the tile's rows, loaded now and put in LDS after
+  // the main loop (no copy waits for them)
+  const float wv = t < rows ? gw[gs + t] : 0.0f;
+  auto pre = [&] {
+    if (t < BM) wrow[t] = wv;
+  };
+  // the scale row of row 32 wave + lane % 32 of the tile
   const uint8_t* srow = as + (int64_t)(gs + min(32 * wave + (lane & 31), rows - 1)) * ass;
-  auto epilogue = [&](auto& acc) {
+  auto epilogue = [&](auto& acc) __attribute__((always_inline)) {
     constexpr int NB = sizeof(acc) / sizeof(acc[0]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -324,30 +342,59 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
       }
     }
   };
-  gemm_rows_a8(rows, rowp, srow, L.nC2, prep + fc2_tile_offset(L, e, bok ? hb : 0), bok, smem, epilogue);
+  const uint8_t* btile = prep + fc2_tile_offset(L, e, bok ? hb : 0);
+  if constexpr (BM == 32) {
+    // act rows this lane copies: rows 32 wave + 16 blk + lane / 4 of the tile
+    const uint8_t* prowp[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+      prowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
+    gemm_rows_pl<BM, 1, true>(rows, prowp, 0, srow, L.nC2, btile, bok, smem, pre, epilogue);
+  } else {
+    // act rows this lane copies: rows 32 wave + 8 blk + lane / 8 of the tile;
+    // the router weights go to LDS before the main loop, whose barriers
+    // order them before the epilogue
+    const uint8_t* rowp[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk)
+      rowp[blk] = aq + (int64_t)(gs + min(32 * wave + 8 * blk + (lane >> 3), rows - 1)) * L.I;
+    pre();
+    gemm_rows_a8(rows, rowp, srow, L.nC2, btile, bok, smem, epilogue);
+  }
 }
 
 hipError_t launch_fc1_a8(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k, uint8_t* ws,
-                         const PrefillWs& W, unsigned grid, hipStream_t st) {
+                         const PrefillWs& W, int bm, unsigned grid, hipStream_t st) {
   uint8_t* xq = ws + W.xq;
   uint8_t* xs = ws + W.xs;
   hipError_t err = launch_mxfp8_quantize(x, M, L.H, xq, xs, a8_scale_stride(L.H), st);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(fc1_gemm_a8, dim3(grid), dim3(256), 0, st, prep, L, (const uint8_t*)xq, (const uint8_t*)xs,
-                     a8_scale_stride(L.H), k, (const int*)(ws + W.counts), (const int*)(ws + W.grp_start),
-                     (const int*)(ws + W.tile_start), (const int*)(ws + W.tile_expert), (const int*)(ws + W.perm),
-                     ws + W.aq, ws + W.as,
-                     a8_scale_stride(L.I));
+#define MOE_FC1A8(BM)                                                                                           \
+  hipLaunchKernelGGL(fc1_gemm_a8<BM>, dim3(grid), dim3(256), 0, st, prep, L, (const uint8_t*)xq,               \
+                     (const uint8_t*)xs, a8_scale_stride(L.H), k, (const int*)(ws + W.counts),                  \
+                     (const int*)(ws + W.grp_start), (const int*)(ws + W.tile_start),                           \
+                     (const int*)(ws + W.tile_expert), (const int*)(ws + W.perm), ws + W.aq, ws + W.as,          \
+                     a8_scale_stride(L.I))
+  if (bm == 32)
+    MOE_FC1A8(32);
+  else
+    MOE_FC1A8(kGemmBM);
+#undef MOE_FC1A8
   return hipGetLastError();
 }
 
-hipError_t launch_fc2_a8(const Layout& L, const uint8_t* prep, const float* tw, uint8_t* ws, const PrefillWs& W,
+hipError_t launch_fc2_a8(const Layout& L, const uint8_t* prep, uint8_t* ws, const PrefillWs& W, int bm,
                          unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL(fc2_gemm_a8, dim3(grid), dim3(256), 0, st, prep, L, tw, (const int*)(ws + W.counts),
-                     (const int*)(ws + W.grp_start), (const int*)(ws + W.tile_start),
-                     (const int*)(ws + W.tile_expert), (const int*)(ws + W.perm),
-                     (const uint8_t*)(ws + W.aq), (const uint8_t*)(ws + W.as), a8_scale_stride(L.I),
-                     (float*)(ws + W.y));
+#define MOE_FC2A8(BM)                                                                                           \
+  hipLaunchKernelGGL(fc2_gemm_a8<BM>, dim3(grid), dim3(256), 0, st, prep, L, (const float*)(ws + W.gw),        \
+                     (const int*)(ws + W.counts), (const int*)(ws + W.grp_start), (const int*)(ws + W.tile_start), \
+                     (const int*)(ws + W.tile_expert), (const uint8_t*)(ws + W.aq), (const uint8_t*)(ws + W.as), \
+                     a8_scale_stride(L.I), (float*)(ws + W.y))
+  if (bm == 32)
+    MOE_FC2A8(32);
+  else
+    MOE_FC2A8(kGemmBM);
+#undef MOE_FC2A8
   return hipGetLastError();
 }
 
