@@ -24,14 +24,15 @@
 
 namespace moe {
 
-// LDS of a plane-loop workgroup: an A ring of 2 slots x NP planes x BM rows x
-// 64 bytes (the 64 FP8 values of a step; the 16-byte chunk c of row r at
-// position c ^ pl_swz(r)); an A scale ring of 2 slots x BM / 32 waves x 256
-// bytes (lane n + 32h of wave w: the scale dword of row 32w + n for unit
-// 2s + h); a weight ring of 3 slots x 4 waves x (2 x 1 KiB codes + 256 B: the
-// scale dword of each of the 64 weight rows, which covers both units of a
-// step).  NP = 3: 77 KiB for 128-row tiles (two workgroups per CU); NP = 1:
-// 45 KiB.
+// LDS of a plane-loop workgroup whose A is copied AD steps ahead: an A ring
+// of AD + 1 slots x NP planes x BM rows x 64 bytes (the 64 FP8 values of a
+// step; the 16-byte chunk c of row r at position c ^ pl_swz(r)); an A scale
+// ring of AD + 1 slots x BM / 32 waves x 256 bytes (lane n + 32h of wave w:
+// the scale dword of row 32w + n for unit 2s + h); a weight ring of 3 slots
+// x 4 waves x (2 x 1 KiB codes + 256 B: the scale dword of each of the 64
+// weight rows, which covers both units of a step).  NP = 3, AD = 1: 77 KiB
+// for 128-row tiles (two workgroups per CU); NP = 1, 32-row tiles: 32 KiB
+// (AD = 1) or 34 KiB (AD = 2), four workgroups per CU.
 constexpr int kPlRow = 64;
 template <int BM>
 constexpr int kPlPlane = BM * kPlRow;  // 8 KiB for 128 rows
@@ -42,8 +43,8 @@ constexpr int kPlScale = BM / 32 * 256;
 constexpr int kBWavePl = 2 * 1024 + 256;
 constexpr int kBSlotPl = 4 * kBWavePl;
 constexpr int kBSlotsPl = 3;
-template <int BM, int NP>
-constexpr int kPlLds = 2 * kPlSlot<BM, NP> + 2 * kPlScale<BM> + kBSlotsPl * kBSlotPl;
+template <int BM, int NP, int AD>
+constexpr int kPlLds = (AD + 1) * (kPlSlot<BM, NP> + kPlScale<BM>) + kBSlotsPl * kBSlotPl;
 
 // Position swizzle of a 64-byte plane row: for every 8, 16 or 32 lanes that
 // read one chunk each of rows n = lane % 32 (the same chunk index) the 16-byte
@@ -65,31 +66,36 @@ __device__ __forceinline__ int pl_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3;
 // Copies (wave w, when the tile has rows in block w: CPA): the plane codes
 // (16 rows of 64 bytes per copy, plane p at p * pst bytes from `prowp[blk]`,
 // row 32w + 16 blk + lane / 4) and the scale dwords (row 32w + lane % 32,
-// unit 2s + lane / 32), one step ahead; the wave's weights (two code halves
+// unit 2s + lane / 32), AD steps ahead; the wave's weights (two code halves
 // and one copy of the 64 rows' scale dwords) two steps ahead.  Per step:
 // wait until this wave's copies for the step have landed, one barrier, then
 // the MFMAs with the next copies issued between them.  Copies past the last
 // step are clamped to it (never used); with an odd number of units the last
 // step's second unit is zeroed when read (codes and weights zero, scales 1).
-template <int BM, int NP, bool SBYTE, int NB, bool CPA, typename Pre, typename Epilogue>
+template <int BM, int NP, int AD, bool SBYTE, int NB, bool CPA, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], int64_t pst, const uint8_t* srow,
                                              int nU, const uint8_t* __restrict__ btile, uint8_t* smem, Pre&& pre,
                                              Epilogue&& epilogue) {
   static_assert(NP >= 1 && NP <= 3 && (!SBYTE || NP == 1), "planes and their scales");
+  static_assert(AD == 1 || AD == 2, "A copied one or two steps ahead");
+  constexpr int AS = AD + 1;  // A ring slots
   constexpr int NBA = NB > 0 ? NB : 1;
   constexpr int NA = CPA ? 2 * NP + 1 : 0;  // copies of A per step: NP planes x 2 row halves, 1 scale
   constexpr int NW = NB > 0 ? 3 : 0;        // copies of weights per step
   constexpr int NCOPY = NA + NW;
   constexpr int NGROUP = NP * NB;                            // MFMA groups of a step (a plane of a block)
   constexpr int NPRE = NCOPY > NGROUP ? NCOPY - NGROUP : 0;  // copies issued before them
+  // copies of later steps in flight when step s starts: step s - 1's copies
+  // of the weights, and of A when A is two steps ahead
+  constexpr int INFLIGHT = NW + (AD == 2 ? NA : 0);
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int nsteps = (nU + 1) / 2;
   const int full = nU / 2;
   uint8_t* const aring = smem;
-  uint8_t* const asc = smem + 2 * kPlSlot<BM, NP>;
-  uint8_t* const bring = asc + 2 * kPlScale<BM> + wave * kBWavePl;
+  uint8_t* const asc = smem + AS * kPlSlot<BM, NP>;
+  uint8_t* const bring = asc + AS * kPlScale<BM> + wave * kBWavePl;
 
   f32x16_t acc[NBA][2];
 #pragma unroll
@@ -103,12 +109,12 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
     const int c = (lane & 3) ^ pl_swz(16 * blk + (lane >> 2));  // lane l writes position l % 4 of row l / 4
     const int u = min(2 * sc + (c >> 1), nU - 1);
     dma16(prowp[blk] + p * pst + u * 32 + (c & 1) * 16,
-          lds_addr(aring + (s & 1) * kPlSlot<BM, NP> + p * kPlPlane<BM> + (32 * wave + 16 * blk) * kPlRow));
+          lds_addr(aring + (s % AS) * kPlSlot<BM, NP> + p * kPlPlane<BM> + (32 * wave + 16 * blk) * kPlRow));
   };
   auto copy_as = [&](int s) {
     const int sc = min(s, nsteps - 1);
     const int u = min(2 * sc + h, nU - 1);
-    dma4(srow + (SBYTE ? (u & ~3) : 4 * u), lds_addr(asc + (s & 1) * kPlScale<BM> + wave * 256));
+    dma4(srow + (SBYTE ? (u & ~3) : 4 * u), lds_addr(asc + (s % AS) * kPlScale<BM> + wave * 256));
   };
   auto b_unit = [&](int s) { return min(2 * s + h, nU - 1); };
   auto copy_b = [&](int s, int j) {
@@ -122,28 +128,28 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
          lds_addr(bring + (s % kBSlotsPl) * kBSlotPl + 2048));
   };
   // Copies of a step, always issued in this order (vm_wait counts on it):
-  // with CPA, the planes' row halves and the scale dwords for step s + 1;
+  // with CPA, the planes' row halves and the scale dwords for step s + AD;
   // then (waves with a weight tile) the 2 code halves and the scale dwords
   // for step s + 2.
   auto copy = [&](int s, int ci) {
     if (CPA && ci < 2 * NP)
-      copy_a(s + 1, ci >> 1, ci & 1);
+      copy_a(s + AD, ci >> 1, ci & 1);
     else if (CPA && ci == 2 * NP)
-      copy_as(s + 1);
+      copy_as(s + AD);
     else if (ci - NA < 2)
       copy_b(s + 2, ci - NA);
     else
       copy_bs(s + 2);
   };
   auto step = [&](int s, bool tail) {
-    vm_wait<NW>();    // this wave's copies for step s have landed (the weights of s + 1 may not)
+    vm_wait<INFLIGHT>();  // this wave's copies for step s have landed (those for s + 1 may not)
     __syncthreads();  // everyone's have; everyone is done with step s - 1
 #pragma unroll
     for (int ci = 0; ci < NPRE; ++ci) copy(s, ci);
     if constexpr (NB > 0) {
       const uint8_t* bs = bring + (s % kBSlotsPl) * kBSlotPl;
-      const uint8_t* ps = aring + (s & 1) * kPlSlot<BM, NP>;
-      const uint8_t* ss = asc + (s & 1) * kPlScale<BM>;
+      const uint8_t* ps = aring + (s % AS) * kPlSlot<BM, NP>;
+      const uint8_t* ss = asc + (s % AS) * kPlScale<BM>;
       const int c = b_unit(s);
       const bool z = tail && h;
       i32x8_t bop[2];
@@ -177,22 +183,29 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
     }
   };
 
-  if constexpr (CPA) {
+  // the first steps' copies in the order of a step's: A(0) (and A(1) when
+  // AD = 2) with the weights of steps 0 and 1
+  auto copies_a = [&](int s) {
+    if constexpr (CPA) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      copy_a(0, p, 0);
-      copy_a(0, p, 1);
+      for (int p = 0; p < NP; ++p) {
+        copy_a(s, p, 0);
+        copy_a(s, p, 1);
+      }
+      copy_as(s);
     }
-    copy_as(0);
-  }
-  if constexpr (NB > 0) {
-    copy_b(0, 0);
-    copy_b(0, 1);
-    copy_bs(0);
-    copy_b(1, 0);
-    copy_b(1, 1);
-    copy_bs(1);
-  }
+  };
+  auto copies_b = [&](int s) {
+    if constexpr (NB > 0) {
+      copy_b(s, 0);
+      copy_b(s, 1);
+      copy_bs(s);
+    }
+  };
+  copies_a(0);
+  copies_b(0);
+  if constexpr (AD == 2) copies_a(1);
+  copies_b(1);
   for (int s = 0; s < full; ++s) step(s, false);
   if (full < nsteps) step(full, true);
   pre();         // LDS the epilogue reads, written before the barrier
@@ -205,12 +218,12 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
 // (0 when the wave has no weight tile); the wave copies its A block when the
 // tile has rows in it.  Tiles of BM = 32 rows have one block, copied by wave
 // 0.  Each variant carries its own copy of the epilogue.
-template <int BM, int NP, bool SBYTE, typename Pre, typename Epilogue>
+template <int BM, int NP, int AD, bool SBYTE, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_rows_pl(int rows, const uint8_t* const (&prowp)[2], int64_t pst,
                                              const uint8_t* srow, int nU, const uint8_t* __restrict__ btile,
                                              bool bok, uint8_t* smem, Pre&& pre, Epilogue&& ep) {
   const bool cpa = 32 * (threadIdx.x >> 6) < rows;
-#define MOE_PL(NB, CPA) gemm_main_pl<BM, NP, SBYTE, NB, CPA>(prowp, pst, srow, nU, btile, smem, pre, ep)
+#define MOE_PL(NB, CPA) gemm_main_pl<BM, NP, AD, SBYTE, NB, CPA>(prowp, pst, srow, nU, btile, smem, pre, ep)
   if constexpr (BM == 32) {
     if (!bok) {
       if (cpa)

@@ -690,7 +690,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
              const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, const uint8_t* __restrict__ aq,
              const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kPlLds<BM, 3> : kGemmLds<BM, true>];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kPlLds<BM, 3, 1> : kGemmLds<BM, true>];
   __shared__ float wrow[BM];
   const GroupTile id = group_tile(fc2_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
@@ -737,7 +737,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
     for (int blk = 0; blk < 2; ++blk)
       prowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
     const uint8_t* srow = as + (int64_t)(gs + min(32 * wave + (lane & 31), rows - 1)) * ass;
-    gemm_rows_pl<BM, 3, false>(rows, prowp, plane, srow, L.nC2, btile, bok, smem, pre, epilogue);
+    gemm_rows_pl<BM, 3, 1, false>(rows, prowp, plane, srow, L.nC2, btile, bok, smem, pre, epilogue);
   } else {
     // two passes over K: the hi activation plane, then the lo plane; rows
     // 32 wave + 8 blk + lane / 8 of the tile
