@@ -5,8 +5,8 @@
 // activation row is the sum of NP planes; the loop multiplies each plane by
 // the same weights into the same accumulators, so the weights are copied
 // once per step and never decoded.
-//   NP = 3: the bf16-activation MXFP4 FC2 (hi = bf16(a) as two planes, and
-//           the residual a - hi);
+//   NP = 3: the bf16-activation MXFP4 FC2 (hi = bf16(a) as two E4M3 planes,
+//           and the residual a - hi as an E2M1 plane, LO4);
 //   NP = 1: the W4A8-MX GEMMs (x rows, or the activation rows, quantised
 //           once).
 //
@@ -14,7 +14,8 @@
 // 32-value units): lane c + 32h holds B column c's unit h (32 E2M1 values in
 // K order, 16 bytes) and that unit's scale; lane r + 32h holds A row r's
 // bytes 16h..16h+15 of unit 0 followed by the same bytes of unit 1, and the
-// scale of row r's unit h.
+// scale of row r's unit h.  An E2M1 A operand is laid out as B: lane r + 32h
+// holds row r's unit h (16 bytes, low nibble first).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,26 +31,30 @@ namespace moe {
 // ring of AD + 1 slots x BM / 32 waves x 256 bytes (lane n + 32h of wave w:
 // the scale dword of row 32w + n for unit 2s + h); a weight ring of 3 slots
 // x 4 waves x (2 x 1 KiB codes + 256 B: the scale dword of each of the 64
-// weight rows, which covers both units of a step).  NP = 3, AD = 1: 77 KiB
-// for 128-row tiles (two workgroups per CU); NP = 1, 32-row tiles: 32 KiB
-// (AD = 1) or 34 KiB (AD = 2), four workgroups per CU.
+// weight rows, which covers both units of a step).  NP = 3 with LO4, AD = 1:
+// 69 KiB for 128-row tiles (two workgroups per CU); NP = 1, 32-row tiles:
+// 32 KiB (AD = 1) or 34 KiB (AD = 2), four workgroups per CU.
 constexpr int kPlRow = 64;
 template <int BM>
 constexpr int kPlPlane = BM * kPlRow;  // 8 KiB for 128 rows
-template <int BM, int NP>
-constexpr int kPlSlot = NP * kPlPlane<BM>;
+template <int BM>
+constexpr int kPlPlane4 = BM * (kPlRow / 2);  // an E2M1 plane: 32 bytes per row and step
+template <int BM, int NP, bool LO4>
+constexpr int kPlSlot = (LO4 ? NP - 1 : NP) * kPlPlane<BM> + (LO4 ? kPlPlane4<BM> : 0);
 template <int BM>
 constexpr int kPlScale = BM / 32 * 256;
 constexpr int kBWavePl = 2 * 1024 + 256;
 constexpr int kBSlotPl = 4 * kBWavePl;
 constexpr int kBSlotsPl = 3;
-template <int BM, int NP, int AD>
-constexpr int kPlLds = (AD + 1) * (kPlSlot<BM, NP> + kPlScale<BM>) + kBSlotsPl * kBSlotPl;
+template <int BM, int NP, int AD, bool LO4>
+constexpr int kPlLds = (AD + 1) * (kPlSlot<BM, NP, LO4> + kPlScale<BM>) + kBSlotsPl * kBSlotPl;
 
 // Position swizzle of a 64-byte plane row: for every 8, 16 or 32 lanes that
 // read one chunk each of rows n = lane % 32 (the same chunk index) the 16-byte
 // units land in distinct LDS banks.
 __device__ __forceinline__ int pl_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// The same for a 32-byte E2M1 plane row (two chunks).
+__device__ __forceinline__ int pl_swz4(int r) { return ((r >> 2) ^ (r >> 3) ^ (r >> 4)) & 1; }
 
 // Main loop for one BM-row x 256-column output tile, followed by
 // `epilogue(acc)`: one pass over the nU units of K in steps of two.  Wave w
@@ -65,22 +70,25 @@ __device__ __forceinline__ int pl_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3;
 //
 // Copies (wave w, when the tile has rows in block w: CPA): the plane codes
 // (16 rows of 64 bytes per copy, plane p at p * pst bytes from `prowp[blk]`,
-// row 32w + 16 blk + lane / 4) and the scale dwords (row 32w + lane % 32,
+// row 32w + 16 blk + lane / 4; with LO4 the last plane 32 rows of 32 bytes
+// from `lrow4`, row 32w + lane / 2) and the scale dwords (row 32w + lane % 32,
 // unit 2s + lane / 32), AD steps ahead; the wave's weights (two code halves
 // and one copy of the 64 rows' scale dwords) two steps ahead.  Per step:
 // wait until this wave's copies for the step have landed, one barrier, then
 // the MFMAs with the next copies issued between them.  Copies past the last
 // step are clamped to it (never used); with an odd number of units the last
 // step's second unit is zeroed when read (codes and weights zero, scales 1).
-template <int BM, int NP, int AD, bool SBYTE, int NB, bool CPA, typename Pre, typename Epilogue>
-__device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], int64_t pst, const uint8_t* srow,
-                                             int nU, const uint8_t* __restrict__ btile, uint8_t* smem, Pre&& pre,
-                                             Epilogue&& epilogue) {
-  static_assert(NP >= 1 && NP <= 3 && (!SBYTE || NP == 1), "planes and their scales");
+template <int BM, int NP, int AD, bool SBYTE, bool LO4, int NB, bool CPA, typename Pre, typename Epilogue>
+__device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], int64_t pst, const uint8_t* lrow4,
+                                             const uint8_t* srow, int nU, const uint8_t* __restrict__ btile,
+                                             uint8_t* smem, Pre&& pre, Epilogue&& epilogue) {
+  static_assert(NP >= 1 && NP <= 3 && (!SBYTE || NP == 1) && (!LO4 || NP > 1), "planes and their scales");
+  constexpr int N8 = LO4 ? NP - 1 : NP;  // E4M3 planes
   static_assert(AD == 1 || AD == 2, "A copied one or two steps ahead");
   constexpr int AS = AD + 1;  // A ring slots
   constexpr int NBA = NB > 0 ? NB : 1;
-  constexpr int NA = CPA ? 2 * NP + 1 : 0;  // copies of A per step: NP planes x 2 row halves, 1 scale
+  constexpr int NA = CPA ? 2 * N8 + (LO4 ? 1 : 0) + 1 : 0;  // copies of A per step: 2 per E4M3 plane,
+                                                             // 1 for an E2M1 one, 1 for the scales
   constexpr int NW = NB > 0 ? 3 : 0;        // copies of weights per step
   constexpr int NCOPY = NA + NW;
   constexpr int NGROUP = NP * NB;                            // MFMA groups of a step (a plane of a block)
@@ -94,7 +102,7 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
   const int nsteps = (nU + 1) / 2;
   const int full = nU / 2;
   uint8_t* const aring = smem;
-  uint8_t* const asc = smem + AS * kPlSlot<BM, NP>;
+  uint8_t* const asc = smem + AS * kPlSlot<BM, NP, LO4>;
   uint8_t* const bring = asc + AS * kPlScale<BM> + wave * kBWavePl;
 
   f32x16_t acc[NBA][2];
@@ -109,7 +117,14 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
     const int c = (lane & 3) ^ pl_swz(16 * blk + (lane >> 2));  // lane l writes position l % 4 of row l / 4
     const int u = min(2 * sc + (c >> 1), nU - 1);
     dma16(prowp[blk] + p * pst + u * 32 + (c & 1) * 16,
-          lds_addr(aring + (s % AS) * kPlSlot<BM, NP> + p * kPlPlane<BM> + (32 * wave + 16 * blk) * kPlRow));
+          lds_addr(aring + (s % AS) * kPlSlot<BM, NP, LO4> + p * kPlPlane<BM> + (32 * wave + 16 * blk) * kPlRow));
+  };
+  auto copy_a4 = [&](int s) {  // the E2M1 plane: lane l writes position l % 2 of row l / 2
+    const int sc = min(s, nsteps - 1);
+    const int c = (lane & 1) ^ pl_swz4(lane >> 1);
+    const int u = min(2 * sc + c, nU - 1);
+    dma16(lrow4 + u * 16,
+          lds_addr(aring + (s % AS) * kPlSlot<BM, NP, LO4> + N8 * kPlPlane<BM> + 32 * wave * (kPlRow / 2)));
   };
   auto copy_as = [&](int s) {
     const int sc = min(s, nsteps - 1);
@@ -128,13 +143,15 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
          lds_addr(bring + (s % kBSlotsPl) * kBSlotPl + 2048));
   };
   // Copies of a step, always issued in this order (vm_wait counts on it):
-  // with CPA, the planes' row halves and the scale dwords for step s + AD;
-  // then (waves with a weight tile) the 2 code halves and the scale dwords
-  // for step s + 2.
+  // with CPA, the planes' rows and the scale dwords for step s + AD; then
+  // (waves with a weight tile) the 2 code halves and the scale dwords for
+  // step s + 2.
   auto copy = [&](int s, int ci) {
-    if (CPA && ci < 2 * NP)
+    if (CPA && ci < 2 * N8)
       copy_a(s + AD, ci >> 1, ci & 1);
-    else if (CPA && ci == 2 * NP)
+    else if (CPA && LO4 && ci == 2 * N8)
+      copy_a4(s + AD);
+    else if (CPA && ci == NA - 1)
       copy_as(s + AD);
     else if (ci - NA < 2)
       copy_b(s + 2, ci - NA);
@@ -148,7 +165,7 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
     for (int ci = 0; ci < NPRE; ++ci) copy(s, ci);
     if constexpr (NB > 0) {
       const uint8_t* bs = bring + (s % kBSlotsPl) * kBSlotPl;
-      const uint8_t* ps = aring + (s % AS) * kPlSlot<BM, NP>;
+      const uint8_t* ps = aring + (s % AS) * kPlSlot<BM, NP, LO4>;
       const uint8_t* ss = asc + (s % AS) * kPlScale<BM>;
       const int c = b_unit(s);
       const bool z = tail && h;
@@ -166,7 +183,7 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
       for (int i = 0; i < NB; ++i) {
         const uint32_t asw = *(const uint32_t*)(ss + i * 256 + lane * 4);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
+        for (int p = 0; p < N8; ++p) {
           const uint8_t* pr = ps + p * kPlPlane<BM> + (i * 32 + n) * kPlRow;
           const i32x4_t a0 = *(const i32x4_t*)(pr + ((h ^ psw) * 16));
           i32x4_t a1 = *(const i32x4_t*)(pr + (((2 + h) ^ psw) * 16));
@@ -176,6 +193,16 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[j], acc[i][j], 0, 4, 0, sa, 0, sb[j]);
+          if (ci < NCOPY) copy(s, ci++);
+        }
+        if constexpr (LO4) {  // E2M1 x E2M1 (cbsz 4): the lane's own unit, as B
+          const i32x4_t a = *(const i32x4_t*)(ps + N8 * kPlPlane<BM> + (i * 32 + n) * (kPlRow / 2) +
+                                              ((h ^ pl_swz4(n)) * 16));
+          const i32x8_t aop = z ? i32x8_t{} : i32x8_t{a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+          const int sa = z ? 127 : (int)((asw >> (8 * N8)) & 0xFFu);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[j], acc[i][j], 4, 4, 0, sa, 0, sb[j]);
           if (ci < NCOPY) copy(s, ci++);
         }
       }
@@ -188,10 +215,11 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
   auto copies_a = [&](int s) {
     if constexpr (CPA) {
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
+      for (int p = 0; p < N8; ++p) {
         copy_a(s, p, 0);
         copy_a(s, p, 1);
       }
+      if constexpr (LO4) copy_a4(s);
       copy_as(s);
     }
   };
@@ -218,12 +246,14 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
 // (0 when the wave has no weight tile); the wave copies its A block when the
 // tile has rows in it.  Tiles of BM = 32 rows have one block, copied by wave
 // 0.  Each variant carries its own copy of the epilogue.
-template <int BM, int NP, int AD, bool SBYTE, typename Pre, typename Epilogue>
+template <int BM, int NP, int AD, bool SBYTE, bool LO4, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_rows_pl(int rows, const uint8_t* const (&prowp)[2], int64_t pst,
-                                             const uint8_t* srow, int nU, const uint8_t* __restrict__ btile,
-                                             bool bok, uint8_t* smem, Pre&& pre, Epilogue&& ep) {
+                                             const uint8_t* lrow4, const uint8_t* srow, int nU,
+                                             const uint8_t* __restrict__ btile, bool bok, uint8_t* smem, Pre&& pre,
+                                             Epilogue&& ep) {
   const bool cpa = 32 * (threadIdx.x >> 6) < rows;
-#define MOE_PL(NB, CPA) gemm_main_pl<BM, NP, AD, SBYTE, NB, CPA>(prowp, pst, srow, nU, btile, smem, pre, ep)
+#define MOE_PL(NB, CPA) \
+  gemm_main_pl<BM, NP, AD, SBYTE, LO4, NB, CPA>(prowp, pst, lrow4, srow, nU, btile, smem, pre, ep)
   if constexpr (BM == 32) {
     if (!bok) {
       if (cpa)

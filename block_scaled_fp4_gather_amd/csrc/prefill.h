@@ -30,8 +30,8 @@ struct PrefillWs {
   int64_t xq;          // u8 [M][H]  x codes per token
   int64_t xs;          // u8 [M][a8_scale_stride(H)]  x scales
   int64_t aq;          // u8 [R][I]  SiLU(gate)*up codes per grouped row; MXFP4 with bf16
-                       // activations: u8 [3][R][I] (plane p at p * pst bytes), planes 0 and 1
-                       // hold hi (its MXFP8 rounding, then the remainder), plane 2 lo
+                       // activations: u8 [2][R][I] E4M3 (plane p at p * pst bytes) holding hi
+                       // (its MXFP8 rounding, then the remainder), then u8 [R][I / 2] E2M1 lo
   int64_t as;          // u8 [R][a8_scale_stride(I)]  their scales; MXFP4 with bf16 activations:
                        // u32 [R][I / 32], byte p the scale of plane p for those 32 columns
   int64_t pst;         // bytes from one MXFP8 plane to the next (MXFP4 with bf16 activations)
@@ -67,7 +67,7 @@ inline PrefillWs prefill_ws(const Layout& L, int64_t routes, int64_t tokens, boo
   } else if (L.fmt == kMXFP4) {
     w.pst = align_up(routes * L.I, 256);
     w.aq = o;
-    w.as = w.aq + 3 * w.pst;
+    w.as = w.aq + 2 * w.pst + align_up(routes * L.I / 2, 256);
     o = w.as + align_up(routes * (L.I / 32) * 4, 256);
   } else {
     w.aq = w.as = w.act + align_up(2 * routes * L.I, 256);

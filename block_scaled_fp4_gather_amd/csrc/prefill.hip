@@ -16,12 +16,12 @@
 //              E4M3 block scale has at most 6 significant bits), v_mfma_f32_32x32x16_bf16 with
 //              fp32 accumulation, SiLU(gate)*up epilogue -> the activation as
 //              hi = bf16(a) plus the residual lo = a - hi: NVFP4 as two bf16
-//              planes; MXFP4 as three MXFP8 planes (hi rounded to MXFP8, what
-//              that leaves of hi, and lo);
+//              planes; MXFP4 as three planes (hi rounded to MXFP8, what that
+//              leaves of hi, and lo as MXFP4);
 //   fc2_gemm   over the activation rows and W2: NVFP4 as fc1_gemm, in two
 //              passes over K, one per bf16 plane; MXFP4 in one pass on
-//              v_mfma_scale_f32_32x32x64_f8f6f4, three per block and step,
-//              with the weights as stored; times the NVFP4 global and the
+//              v_mfma_scale_f32_32x32x64_f8f6f4, one pair per plane, block
+//              and step, with the weights as stored; times the NVFP4 global and the
 //              route's router weight -> fp32 rows;
 //   combine    per token, the fp32 sum of its valid routes' rows in route
 //              order, rounded once to bf16.
@@ -544,6 +544,39 @@ __device__ __forceinline__ uint32_t mx_block16(float (&v)[16], uint32_t (&w)[4],
   return sb;
 }
 
+// E2M1 code of v, |v| <= 6, rounded to nearest even (magnitudes 0, 0.5, 1,
+// 1.5, 2, 3, 4, 6 are codes 0..7; the sign is bit 3).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// An E2M1 block of 32 values held 16 per lane by lanes 2r and 2r + 1 (as
+// mx_block16): returns the scale byte and sets this lane's 16 nibbles (w,
+// eight to a dword, low nibble first).  The shared exponent is
+// floor(log2(max |v|)) - 2 (2 = exponent of E2M1's largest power of two),
+// raised by one where the largest value would exceed 6, so nothing is
+// clamped; a non-finite block gets scale byte 255.
+__device__ __forceinline__ uint32_t e2m1_block16(const float (&v)[16], uint32_t (&w)[2]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) m = max(m, __float_as_uint(v[q]) & 0x7FFFFFFFu);
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  w[0] = w[1] = 0;
+  if (m >= 0x7F800000u) return 255u;
+  const int ef = (int)(m >> 23);
+  uint32_t sb = (uint32_t)(ef > 2 ? ef - 2 : 0);
+  if (__uint_as_float(m) * mx_inv_scale(sb) > 6.0f) ++sb;
+  const float inv = mx_inv_scale(sb);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[q] |= e2m1_code(v[8 * q + e] * inv) << (4 * e);
+  return sb;
+}
+
 // Occupancy of the grouped GEMMs (waves per SIMD): tiles of 32 rows need a
 // quarter of the A ring and a quarter of the accumulators, so three
 // workgroups share a CU, and four for MXFP4 FC1 (39 KiB of LDS, 120 VGPRs;
@@ -585,10 +618,12 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFc1Wa
   const int n = 32 * b + (lane & 31);
   // a = f(gate, up); a non-gated activation (relu2) writes both halves as
   // outputs, at columns n and Ip + n.  NVFP4: hi = bf16(a) and lo =
-  // bf16(a - hi), two bf16 planes.  MXFP4: three MXFP8 planes (codes `aq`,
-  // plane p at p * `plane` bytes; one scale dword per row and 32 columns at
-  // `as`, `ass` bytes per row, byte p for plane p): plane 0 is hi = bf16(a)
-  // rounded to MXFP8, plane 1 what that leaves of hi, plane 2 lo = a - hi.
+  // bf16(a - hi), two bf16 planes.  MXFP4: three planes (codes `aq`, plane p
+  // at p * `plane` bytes; one scale dword per row and 32 columns at `as`,
+  // `ass` bytes per row, byte p for plane p): plane 0 is hi = bf16(a)
+  // rounded to MXFP8, plane 1 what that leaves of hi (E4M3 codes, a row of I
+  // bytes), plane 2 lo = a - hi as MXFP4 (E2M1 nibbles, a row of I / 2
+  // bytes).
   // Per 32-row block the values of a go to this wave's part of the (now idle)
   // A ring as 32 rows x 32 columns (row stride 144 B); lane l then takes row
   // l / 2, columns 16 (l % 2) .. + 15, whose block of 32 is its own 16 values
@@ -635,9 +670,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFc1Wa
           const uint32_t s1 = mx_block16(v, w, false);
           if (row < rows) *(uint4*)(dst + plane) = make_uint4(w[0], w[1], w[2], w[3]);
           take(true);
-          const uint32_t s2 = mx_block16(v, w, false);
+          uint32_t w4[2];
+          const uint32_t s2 = e2m1_block16(v, w4);
           if (row < rows) {
-            *(uint4*)(dst + 2 * plane) = make_uint4(w[0], w[1], w[2], w[3]);
+            *(uint2*)(aq + 2 * plane + ((int64_t)(gs + row) * L.I + c0 + 16 * half) / 2) = make_uint2(w4[0], w4[1]);
             if (half == 0) *(uint32_t*)(as + (int64_t)(gs + row) * ass + c0 / 8) = s0 | (s1 << 8) | (s2 << 16);
           }
           __builtin_amdgcn_wave_barrier();  // the next block's staging stores come after these reads
@@ -690,7 +726,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
              const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, const uint8_t* __restrict__ aq,
              const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kPlLds<BM, 3, 1> : kGemmLds<BM, true>];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kPlLds<BM, 3, 1, true> : kGemmLds<BM, true>];
   __shared__ float wrow[BM];
   const GroupTile id = group_tile(fc2_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
@@ -729,15 +765,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
   };
   const uint8_t* btile = prep + fc2_tile_offset(L, e, bok ? hb : 0);
   if constexpr (FMT == kMXFP4) {
-    // one pass over the three MXFP8 planes: codes of rows 32 wave + 16 blk +
-    // lane / 4, the scale dwords of row 32 wave + lane % 32 (grouped rows
-    // past the tile repeat its last row)
+    // one pass over the three planes: E4M3 codes of rows 32 wave + 16 blk +
+    // lane / 4, E2M1 codes of row 32 wave + lane / 2, the scale dwords of row
+    // 32 wave + lane % 32 (grouped rows past the tile repeat its last row)
     const uint8_t* prowp[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
       prowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
+    const uint8_t* lrow4 = aq + 2 * plane + (int64_t)(gs + min(32 * wave + (lane >> 1), rows - 1)) * (L.I / 2);
     const uint8_t* srow = as + (int64_t)(gs + min(32 * wave + (lane & 31), rows - 1)) * ass;
-    gemm_rows_pl<BM, 3, 1, false>(rows, prowp, plane, srow, L.nC2, btile, bok, smem, pre, epilogue);
+    gemm_rows_pl<BM, 3, 1, false, true>(rows, prowp, plane, lrow4, srow, L.nC2, btile, bok, smem, pre, epilogue);
   } else {
     // two passes over K: the hi activation plane, then the lo plane; rows
     // 32 wave + 8 blk + lane / 8 of the tile

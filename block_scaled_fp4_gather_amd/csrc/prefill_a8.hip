@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kA8Wav
                 const int* __restrict__ grp_start, const int* __restrict__ tile_start,
                 const int* __restrict__ tile_expert, const int* __restrict__ perm, uint8_t* __restrict__ aq,
                 uint8_t* __restrict__ as, int ass) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[BM == 32 ? kPlLds<32, 1, 1> : kGemmLds8];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[BM == 32 ? kPlLds<32, 1, 1, false> : kGemmLds8];
   const GroupTile id = group_tile(fc1_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
   const int e = id.e;
@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kA8Wav
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
       prowp[blk] = xq + (int64_t)(perm[gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)] / k) * L.H;
-    gemm_rows_pl<BM, 1, 1, true>(rows, prowp, 0, srow, L.nC1, btile, bok, smem, [] {}, epilogue);
+    gemm_rows_pl<BM, 1, 1, true, false>(rows, prowp, 0, nullptr, srow, L.nC1, btile, bok, smem, [] {}, epilogue);
   } else {
     // x rows this lane copies: rows 32 wave + 8 blk + lane / 8 of the tile
     const uint8_t* rowp[4];
@@ -305,7 +305,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kA8Wav
                 const int* __restrict__ counts, const int* __restrict__ grp_start,
                 const int* __restrict__ tile_start, const int* __restrict__ tile_expert,
                 const uint8_t* __restrict__ aq, const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[BM == 32 ? kPlLds<32, 1, 2> : kGemmLds8];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[BM == 32 ? kPlLds<32, 1, 2, false> : kGemmLds8];
   __shared__ float wrow[BM];
   const GroupTile id = group_tile(fc2_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
@@ -351,7 +351,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kA8Wav
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
       prowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
-    gemm_rows_pl<BM, 1, 2, true>(rows, prowp, 0, srow, L.nC2, btile, bok, smem, pre, epilogue);
+    gemm_rows_pl<BM, 1, 2, true, false>(rows, prowp, 0, nullptr, srow, L.nC2, btile, bok, smem, pre, epilogue);
   } else {
     // act rows this lane copies: rows 32 wave + 8 blk + lane / 8 of the tile;
     // the router weights go to LDS before the main loop, whose barriers
