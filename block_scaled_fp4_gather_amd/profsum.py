@@ -35,8 +35,9 @@ KERNELS = ("fc1_kernel", "fc2_kernel", "fc1_gemm_a8", "fc2_gemm_a8", "mxfp8_quan
 # HIP sources each kernel is built from: a summary stays valid while their
 # code (comments and blank space aside) is unchanged.
 _DECODE_SRC = ("decode_path.hip", "decode_path.h", "decode.h", "act.h", "layout.h")
-_GROUPED_SRC = ("prefill.hip", "prefill.h", "gemm_util.h", "decode.h", "act.h", "layout.h")
-_A8_SRC = ("prefill_a8.hip", "prefill.h", "gemm_util.h", "mxfp8.h", "act.h", "layout.h")
+_GROUPED_SRC = ("prefill.hip", "prefill.h", "gemm_util.h", "gemm_planes.h", "mxfp8.h", "decode.h", "act.h",
+                "layout.h")
+_A8_SRC = ("prefill_a8.hip", "prefill.h", "gemm_util.h", "gemm_planes.h", "mxfp8.h", "act.h", "layout.h")
 SOURCES = {"fc1_kernel": _DECODE_SRC, "fc2_kernel": _DECODE_SRC, "fc1_gemm": _GROUPED_SRC,
            "fc2_gemm": _GROUPED_SRC, "route_one": _GROUPED_SRC, "route_count": _GROUPED_SRC,
            "route_place": _GROUPED_SRC, "route_zero": _GROUPED_SRC, "combine": _GROUPED_SRC,
