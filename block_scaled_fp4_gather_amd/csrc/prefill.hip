@@ -283,6 +283,10 @@ constexpr int kASlots = 3;
 constexpr int kADist = kASlots - 1;  // steps ahead that A is copied (the weights: kBSlots - 1)
 template <int BM, bool PASS2>
 constexpr int kGemmLds = kASlots * kAPlane<BM> + kBSlots * kBSlot<PASS2>;
+// With both activation planes in every step (AP = 2, one pass; 32-row
+// tiles): 51 KiB, three workgroups per CU.
+template <int BM>
+constexpr int kGemmLds2 = kASlots * 2 * kAPlane<BM> + kBSlots * kBSlot<false>;
 
 // Grouped GEMM main loop for one 128-row x 256-column output tile, followed
 // by `epilogue(acc)`.  K runs over nU units of 32 values in steps of two; unit
@@ -313,24 +317,31 @@ constexpr int kGemmLds = kASlots * kAPlane<BM> + kBSlots * kBSlot<PASS2>;
 // ahead, tiles with few rows waited for it every step.  Copies past the last step are clamped to it (never used); with an
 // odd number of units the last step's second half (A and B both) is zeroed
 // when read.
-template <int FMT, int BM, int NB, bool CPA, bool PASS2, typename Pre, typename Epilogue>
+//
+// AP = 2 (NVFP4 FC2 of 32-row tiles) takes both activation planes in one
+// pass instead: a step copies and widens its weight unit once and multiplies
+// it by the hi plane's fragment and the lo plane's (`plane` elements apart),
+// both in the A ring's slot; PASS2 is then false.
+template <int FMT, int BM, int NB, bool CPA, bool PASS2, int AP, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int64_t plane, int nU,
                                           const uint8_t* __restrict__ btile, int nC, uint8_t* smem, Pre&& pre,
                                           Epilogue&& epilogue) {
+  static_assert(AP == 1 || (AP == 2 && !PASS2), "one or two planes per step, two only in one pass");
   constexpr int SPD = FMT == kMXFP4 ? 4 : 2;
   constexpr int NBA = NB > 0 ? NB : 1;
   // copies of later steps in flight when step s starts: those issued in the
   // steps s - kADist + 1 .. s - 1 (4 for A, 3 or 4 more for the weights)
   static_assert(kADist == kBSlots - 1, "A and the weights are copied the same number of steps ahead");
   constexpr int NW = NB > 0 ? (PASS2 ? 4 : 3) : 0;  // weight copies per step
-  constexpr int BCOPIES = (kADist - 1) * ((CPA ? 4 : 0) + NW);
+  constexpr int BCOPIES = (kADist - 1) * ((CPA ? 4 * AP : 0) + NW);
+  constexpr int ASLOT = AP * kAPlane<BM>;  // bytes of one A ring slot
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int n = lane & 31, h = lane >> 5;
   const int nsteps = (nU + 1) / 2;
   const int full = nU / 2;
   uint8_t* const aring = smem;
-  uint8_t* const bring = smem + kASlots * kAPlane<BM> + wave * kBWave<PASS2>;
+  uint8_t* const bring = smem + kASlots * ASLOT + wave * kBWave<PASS2>;
 
   f32x16_t acc[NBA][2];
 #pragma unroll
@@ -347,12 +358,12 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
     const int p = u >= nC ? 1 : 0;
     return (int64_t)p * plane * 2 + (u - p * nC) * 64;
   };
-  // copy of A rows block `blk` of step s into its ring slot
-  auto copy_a = [&](int s, int blk) {
+  // copy of A rows block `blk` of plane p (AP = 2) of step s into its ring slot
+  auto copy_a = [&](int s, int blk, int p) {
     const int sc = s < nsteps ? s : nsteps - 1;
     const int c = cp_lo ^ (blk & 1);
-    const uint8_t* g = (const uint8_t*)rowp[blk] + a_unit(2 * sc + (c >> 2)) + (c & 3) * 16;
-    dma16(g, lds_addr(aring + (s % kASlots) * kAPlane<BM> + (32 * wave + 8 * blk) * kARow));
+    const uint8_t* g = (const uint8_t*)rowp[blk] + p * plane * 2 + a_unit(2 * sc + (c >> 2)) + (c & 3) * 16;
+    dma16(g, lds_addr(aring + (s % kASlots) * ASLOT + p * kAPlane<BM> + (32 * wave + 8 * blk) * kARow));
   };
   // chunk of this lane's weight unit in step s (clamped; within its pass)
   auto b_chunk = [&](int s) {
@@ -376,16 +387,17 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
          lds_addr(bring + (s % kBSlots) * kBSlot<PASS2> + 2048));
   };
   // Copies of a step, always issued in this order (vm_wait counts on it):
-  // copies 0..3 are A blocks for step s + 2 (none without CPA), copies 4 and
-  // 5 the weight halves for the same step, copy 6 (one pass) their scales.
-  constexpr int NCOPY = NB > 0 ? (PASS2 ? 6 : 7) : 4;
+  // copies 0..4AP-1 are A blocks for step s + 2 (none without CPA), then the
+  // weight halves for the same step and (one pass) their scales.
+  constexpr int NCA = 4 * AP;
+  constexpr int NCOPY = NB > 0 ? NCA + (PASS2 ? 2 : 3) : NCA;
   constexpr int NGROUP = 4 * NB;                             // MFMA groups of a step
   constexpr int NPRE = NCOPY > NGROUP ? NCOPY - NGROUP : 0;  // copies issued before them
   auto copy = [&](int s, int ci) {
-    if (ci < 4) {
-      if constexpr (CPA) copy_a(s + kADist, ci);
-    } else if (ci < 6) {
-      copy_b(s + kADist, ci - 4);
+    if (ci < NCA) {
+      if constexpr (CPA) copy_a(s + kADist, ci & 3, ci >> 2);
+    } else if (ci < NCA + 2) {
+      copy_b(s + kADist, ci - NCA);
     } else {
       copy_bs(s + kADist);
     }
@@ -403,16 +415,20 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
     }
   };
   auto mfmas = [&](int s, bool tail, const bf16x8_t (&bf)[4][2]) {
-    const uint8_t* slot = aring + (s % kASlots) * kAPlane<BM>;
+    const uint8_t* slot = aring + (s % kASlots) * ASLOT;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        bf16x8_t af = lds_frag((const __bf16*)(slot + (i * 32 + n) * kARow + (((4 * h + q) ^ swz) * 16)));
-        if (tail && h) af = bf16x8_t{};
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[q][j], acc[i][j], 0, 0, 0);
+        for (int p = 0; p < AP; ++p) {
+          bf16x8_t af = lds_frag(
+              (const __bf16*)(slot + p * kAPlane<BM> + (i * 32 + n) * kARow + (((4 * h + q) ^ swz) * 16)));
+          if (tail && h) af = bf16x8_t{};
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf[q][j], acc[i][j], 0, 0, 0);
+        }
         // one of this step's copies after each of the first MFMA groups
         const int ci = NPRE + q * NB + i;
         if (ci < NCOPY) copy(s, ci);
@@ -436,7 +452,9 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
   for (int s = 0; s < kADist; ++s) {
     if constexpr (CPA) {
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) copy_a(s, blk);
+      for (int p = 0; p < AP; ++p)
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) copy_a(s, blk, p);
     }
     if constexpr (NB > 0) {
       copy_b(s, 0);
@@ -457,7 +475,7 @@ __device__ __forceinline__ void gemm_main(const uint16_t* const (&rowp)[4], int6
 // tile has rows in it.  Tiles of BM = 32 rows have one block, copied by wave
 // 0.  Each variant carries its own copy of the epilogue, called with the
 // NB x 2 accumulator blocks.
-template <int FMT, int BM, bool PASS2, typename Pre, typename Epilogue>
+template <int FMT, int BM, bool PASS2, int AP, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp)[4], int64_t plane, int nU,
                                           const uint8_t* __restrict__ btile, bool bok, int nC,
                                           uint8_t* smem, Pre&& pre, Epilogue&& ep) {
@@ -465,37 +483,37 @@ __device__ __forceinline__ void gemm_rows(int rows, const uint16_t* const (&rowp
   if constexpr (BM == 32) {
     if (!bok) {
       if (cpa)
-        gemm_main<FMT, BM, 0, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+        gemm_main<FMT, BM, 0, true, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
       else
-        gemm_main<FMT, BM, 0, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+        gemm_main<FMT, BM, 0, false, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
     } else {
       if (cpa)
-        gemm_main<FMT, BM, 1, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+        gemm_main<FMT, BM, 1, true, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
       else
-        gemm_main<FMT, BM, 1, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+        gemm_main<FMT, BM, 1, false, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
     }
   } else if (!bok) {
     if (cpa)
-      gemm_main<FMT, BM, 0, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+      gemm_main<FMT, BM, 0, true, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
     else
-      gemm_main<FMT, BM, 0, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+      gemm_main<FMT, BM, 0, false, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
   } else if (rows > 96) {
-    gemm_main<FMT, BM, 4, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+    gemm_main<FMT, BM, 4, true, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
   } else if (rows > 64) {
     if (cpa)
-      gemm_main<FMT, BM, 3, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+      gemm_main<FMT, BM, 3, true, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
     else
-      gemm_main<FMT, BM, 3, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+      gemm_main<FMT, BM, 3, false, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
   } else if (rows > 32) {
     if (cpa)
-      gemm_main<FMT, BM, 2, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+      gemm_main<FMT, BM, 2, true, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
     else
-      gemm_main<FMT, BM, 2, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+      gemm_main<FMT, BM, 2, false, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
   } else {
     if (cpa)
-      gemm_main<FMT, BM, 1, true, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+      gemm_main<FMT, BM, 1, true, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
     else
-      gemm_main<FMT, BM, 1, false, PASS2>(rowp, plane, nU, btile, nC, smem, pre, ep);
+      gemm_main<FMT, BM, 1, false, PASS2, AP>(rowp, plane, nU, btile, nC, smem, pre, ep);
   }
 }
 
@@ -714,7 +732,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kFc1Wa
       }
     });
   };
-  gemm_rows<FMT, BM, false>(rows, rowp, 0, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, L.nC1, smem,
+  gemm_rows<FMT, BM, false, 1>(rows, rowp, 0, L.nC1, prep + fc1_tile_offset(L, e, bok ? b : 0), bok, L.nC1, smem,
                             [] {}, epilogue);
 }
 
@@ -726,7 +744,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
              const int* __restrict__ perm,
              const uint16_t* __restrict__ act, int64_t plane, const uint8_t* __restrict__ aq,
              const uint8_t* __restrict__ as, int ass, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[FMT == kMXFP4 ? kPlLds<BM, 3, 1, true> : kGemmLds<BM, true>];
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t smem[FMT == kMXFP4 ? kPlLds<BM, 3, 1, true> : BM == 32 ? kGemmLds2<BM> : kGemmLds<BM, true>];
   __shared__ float wrow[BM];
   const GroupTile id = group_tile(fc2_blocks(L), tile_start, tile_expert, L.E);
   if (!id.ok) return;
@@ -776,13 +795,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kGemmW
     const uint8_t* srow = as + (int64_t)(gs + min(32 * wave + (lane & 31), rows - 1)) * ass;
     gemm_rows_pl<BM, 3, 1, false, true>(rows, prowp, plane, lrow4, srow, L.nC2, btile, bok, smem, pre, epilogue);
   } else {
-    // two passes over K: the hi activation plane, then the lo plane; rows
-    // 32 wave + 8 blk + lane / 8 of the tile
+    // rows 32 wave + 8 blk + lane / 8 of the tile; 32-row tiles take the hi
+    // and lo activation planes in one pass (each weight unit copied and
+    // widened once), larger ones in two passes over K, hi then lo
     const uint16_t* rowp[4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk)
       rowp[blk] = act + (int64_t)(gs + min(32 * wave + 8 * blk + (lane >> 3), rows - 1)) * L.I;
-    gemm_rows<FMT, BM, true>(rows, rowp, plane, 2 * L.nC2, btile, bok, L.nC2, smem, pre, epilogue);
+    if constexpr (BM == 32)
+      gemm_rows<FMT, BM, false, 2>(rows, rowp, plane, L.nC2, btile, bok, L.nC2, smem, pre, epilogue);
+    else
+      gemm_rows<FMT, BM, true, 1>(rows, rowp, plane, 2 * L.nC2, btile, bok, L.nC2, smem, pre, epilogue);
   }
 }
 
