@@ -16,9 +16,11 @@ constexpr int kRouteMaxExperts = 8192;   // experts the grouping's LDS histogram
 struct PrefillWs {
   int64_t counts;      // int32 [E]   valid routes per expert
   int64_t grp_start;   // int32 [E]   first grouped row of each expert
-  int64_t tile_start;  // int32 [E+1] first m-tile of each expert; [E] = total tiles
+  int64_t tile_start;  // int32 [E+1] first FC1 m-tile of each expert; [E] = total tiles
   int64_t fill;        // int32 [E]   grouped rows handed out per expert (routing)
-  int64_t tile_expert; // int32 [R/32 + E] expert of each m-tile
+  int64_t tile_expert; // int32 [R/32 + E] expert of each FC1 m-tile
+  int64_t tile_start2; // int32 [E+1] the same for FC2's m-tiles
+  int64_t tile_expert2;// int32 [R/32 + E]
   int64_t perm;        // int32 [R]   grouped row -> route index t*k + j
   int64_t rpos;        // int32 [R]   route index -> grouped row (valid routes)
   int64_t gw;          // fp32 [R]   router weight of each grouped row
@@ -52,7 +54,9 @@ inline PrefillWs prefill_ws(const Layout& L, int64_t routes, int64_t tokens, boo
   w.tile_start = w.grp_start + align_up(4 * (int64_t)L.E, 256);
   w.fill = w.tile_start + align_up(4 * ((int64_t)L.E + 1), 256);
   w.tile_expert = w.fill + align_up(4 * (int64_t)L.E, 256);
-  w.perm = w.tile_expert + align_up(4 * ((routes + 31) / 32 + (int64_t)L.E), 256);
+  w.tile_start2 = w.tile_expert + align_up(4 * ((routes + 31) / 32 + (int64_t)L.E), 256);
+  w.tile_expert2 = w.tile_start2 + align_up(4 * ((int64_t)L.E + 1), 256);
+  w.perm = w.tile_expert2 + align_up(4 * ((routes + 31) / 32 + (int64_t)L.E), 256);
   w.rpos = w.perm + align_up(4 * routes, 256);
   w.gw = w.rpos + align_up(4 * routes, 256);
   int64_t o = w.gw + align_up(4 * routes, 256);
@@ -88,12 +92,20 @@ __host__ __device__ inline int fc1_blocks(const Layout& L) { return (L.nB1 + 3) 
 // FC2 column blocks: 4 prepared tiles (256 output columns) each.
 __host__ __device__ inline int fc2_blocks(const Layout& L) { return (L.nB2 + 3) / 4; }
 
-// Rows of the grouped GEMMs' m-tiles for `routes` routes: 128, or 32 when
-// the experts get few routes each, where most 128-row tiles would hold a few
-// rows and three or four smaller workgroups per CU keep more weight copies
-// in flight.
-inline int prefill_bm(const Layout& L, int64_t routes) {
-  return routes <= (int64_t)kSparseRoutesPerExpert * L.E ? 32 : kGemmBM;
+// Rows of the grouped GEMMs' m-tiles for `routes` routes, each GEMM its
+// own: 128, or 32 when the experts get few routes each, where most 128-row
+// tiles would hold a few rows and three or four smaller workgroups per CU
+// keep more weight copies in flight.  Measured on MI355X per GEMM, 32-row
+// tiles stay ahead for longer in two cases: MXFP4 FC1 with bf16 activations
+// (up to 64 routes per expert) and NVFP4 FC2, whose 32-row tiles take both
+// activation planes in one pass (up to 128; at 114 they were 20% faster).
+inline int prefill_bm1(const Layout& L, int64_t routes, bool a8) {
+  const int64_t lim = !a8 && L.fmt == kMXFP4 ? 4 * kSparseRoutesPerExpert : kSparseRoutesPerExpert;
+  return routes <= lim * L.E ? 32 : kGemmBM;
+}
+inline int prefill_bm2(const Layout& L, int64_t routes, bool a8) {
+  const int64_t lim = !a8 && L.fmt == kNVFP4 ? 8 * kSparseRoutesPerExpert : kSparseRoutesPerExpert;
+  return routes <= lim * L.E ? 32 : kGemmBM;
 }
 
 // Workgroups of the larger grouped GEMM grid for up to `routes` routes (a

@@ -48,8 +48,8 @@ __device__ __forceinline__ int route_expert(const IdT* __restrict__ ids, int r, 
 }
 
 // Routing: the valid routes grouped by expert.  Expert e's routes take the
-// grouped rows [grp_start[e], grp_start[e] + counts[e]) and its m-tiles
-// [tile_start[e], tile_start[e + 1]); perm maps a grouped row to its route,
+// grouped rows [grp_start[e], grp_start[e] + counts[e]) and, in each GEMM's
+// m-tile numbering, its m-tiles [tile_start[e], tile_start[e + 1]); perm maps a grouped row to its route,
 // rpos a route to its grouped row, and gw holds each grouped row's router
 // weight.  The order of an expert's routes within
 // its rows is whatever the atomics hand out: every grouped row is computed
@@ -60,65 +60,78 @@ __device__ __forceinline__ int route_expert(const IdT* __restrict__ ids, int r, 
 constexpr int kRouteBlock = 4096;  // routes per workgroup of the routing kernels
 
 // Exclusive prefix over the E counters cnt (in LDS, E <= kRouteMaxExperts)
-// by the 1024 threads of a workgroup: counts[e], grp_start[e],
-// tile_start[e] (m-tiles of bm rows; tile_start[E] the total) and the expert
-// of each m-tile, tile_expert[t], are
-// written to global memory when `out` is set, and cnt[e] becomes
-// grp_start[e].  Ends with a barrier.
-__device__ void route_prefix(int* cnt, int E, int bm, bool out, int* __restrict__ counts,
-                             int* __restrict__ grp_start, int* __restrict__ tile_start,
-                             int* __restrict__ tile_expert) {
-  __shared__ int wpart[2][16];
+// by the 1024 threads of a workgroup: counts[e], grp_start[e] and, for each
+// of the two GEMMs' m-tile sizes (FC1: bm1 rows, table ts1 / te1; FC2: bm2,
+// ts2 / te2), tile_start[e] (tile_start[E] the total) and the expert of each
+// m-tile, tile_expert[t], are written to global memory when `out` is set,
+// and cnt[e] becomes grp_start[e].  Ends with a barrier.
+__device__ void route_prefix(int* cnt, int E, int bm1, int bm2, bool out, int* __restrict__ counts,
+                             int* __restrict__ grp_start, int* __restrict__ ts1, int* __restrict__ te1,
+                             int* __restrict__ ts2, int* __restrict__ te2) {
+  __shared__ int wpart[3][16];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   constexpr int PER = kRouteMaxExperts / 1024;  // counters per thread
   const int e0 = t * PER;
-  int c[PER], rsum = 0, tsum = 0;
+  int c[PER], rsum = 0, tsum1 = 0, tsum2 = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     c[i] = e0 + i < E ? cnt[e0 + i] : 0;
     rsum += c[i];
-    tsum += (c[i] + bm - 1) / bm;
+    tsum1 += (c[i] + bm1 - 1) / bm1;
+    tsum2 += (c[i] + bm2 - 1) / bm2;
   }
   // inclusive scans of the per-thread sums over the wave, then over the waves
-  int ri = rsum, ti = tsum;
+  int ri = rsum, ti1 = tsum1, ti2 = tsum2;
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
-    const int rv = __shfl_up(ri, m), tv = __shfl_up(ti, m);
+    const int rv = __shfl_up(ri, m), tv1 = __shfl_up(ti1, m), tv2 = __shfl_up(ti2, m);
     if (lane >= m) {
       ri += rv;
-      ti += tv;
+      ti1 += tv1;
+      ti2 += tv2;
     }
   }
   if (lane == 63) {
     wpart[0][wave] = ri;
-    wpart[1][wave] = ti;
+    wpart[1][wave] = ti1;
+    wpart[2][wave] = ti2;
   }
   __syncthreads();
-  int rb = ri - rsum, tb = ti - tsum;  // exclusive within the wave
+  int rb = ri - rsum, tb1 = ti1 - tsum1, tb2 = ti2 - tsum2;  // exclusive within the wave
   for (int w = 0; w < wave; ++w) {
     rb += wpart[0][w];
-    tb += wpart[1][w];
+    tb1 += wpart[1][w];
+    tb2 += wpart[2][w];
   }
-  int ttot = 0;
-  for (int w = 0; w < 16; ++w) ttot += wpart[1][w];
+  int ttot1 = 0, ttot2 = 0;
+  for (int w = 0; w < 16; ++w) {
+    ttot1 += wpart[1][w];
+    ttot2 += wpart[2][w];
+  }
   __syncthreads();  // every thread has read cnt before it is overwritten
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int e = e0 + i;
+    const int nt1 = (c[i] + bm1 - 1) / bm1, nt2 = (c[i] + bm2 - 1) / bm2;
     if (e < E) {
       if (out) {
         counts[e] = c[i];
         grp_start[e] = rb;
-        tile_start[e] = tb;
-        const int nt = (c[i] + bm - 1) / bm;
-        for (int q = 0; q < nt; ++q) tile_expert[tb + q] = e;
+        ts1[e] = tb1;
+        ts2[e] = tb2;
+        for (int q = 0; q < nt1; ++q) te1[tb1 + q] = e;
+        for (int q = 0; q < nt2; ++q) te2[tb2 + q] = e;
       }
       cnt[e] = rb;
     }
     rb += c[i];
-    tb += (c[i] + bm - 1) / bm;
+    tb1 += nt1;
+    tb2 += nt2;
   }
-  if (out && t == 0) tile_start[E] = ttot;
+  if (out && t == 0) {
+    ts1[E] = ttot1;
+    ts2[E] = ttot2;
+  }
   __syncthreads();
 }
 
@@ -126,10 +139,10 @@ __device__ void route_prefix(int* cnt, int E, int bm, bool out, int* __restrict_
 // its prefix, then every route takes its grouped row from an LDS counter.
 template <typename IdT>
 __global__ void __launch_bounds__(1024)
-    route_one(const IdT* __restrict__ ids, const float* __restrict__ tw, int R, int E, int bm,
-              int* __restrict__ counts, int* __restrict__ grp_start, int* __restrict__ tile_start,
-              int* __restrict__ tile_expert, int* __restrict__ perm, int* __restrict__ rpos,
-              float* __restrict__ gw) {
+    route_one(const IdT* __restrict__ ids, const float* __restrict__ tw, int R, int E, int bm1, int bm2,
+              int* __restrict__ counts, int* __restrict__ grp_start, int* __restrict__ ts1,
+              int* __restrict__ te1, int* __restrict__ ts2, int* __restrict__ te2, int* __restrict__ perm,
+              int* __restrict__ rpos, float* __restrict__ gw) {
   __shared__ int cnt[kRouteMaxExperts];
   const int t = threadIdx.x;
   for (int q = t; q < E; q += 1024) cnt[q] = 0;
@@ -141,7 +154,7 @@ __global__ void __launch_bounds__(1024)
     if (ex[i] >= 0) atomicAdd(&cnt[ex[i]], 1);
   }
   __syncthreads();
-  route_prefix(cnt, E, bm, true, counts, grp_start, tile_start, tile_expert);
+  route_prefix(cnt, E, bm1, bm2, true, counts, grp_start, ts1, te1, ts2, te2);
 #pragma unroll
   for (int i = 0; i < kRouteBlock / 1024; ++i) {
     if (ex[i] < 0) continue;
@@ -186,10 +199,10 @@ __global__ void __launch_bounds__(1024)
 
 template <typename IdT>
 __global__ void __launch_bounds__(1024)
-    route_place(const IdT* __restrict__ ids, const float* __restrict__ tw, int R, int E, int bm,
-                int* __restrict__ counts, int* __restrict__ grp_start, int* __restrict__ tile_start,
-                int* __restrict__ tile_expert, int* __restrict__ fill, int* __restrict__ perm,
-                int* __restrict__ rpos, float* __restrict__ gw) {
+    route_place(const IdT* __restrict__ ids, const float* __restrict__ tw, int R, int E, int bm1, int bm2,
+                int* __restrict__ counts, int* __restrict__ grp_start, int* __restrict__ ts1,
+                int* __restrict__ te1, int* __restrict__ ts2, int* __restrict__ te2, int* __restrict__ fill,
+                int* __restrict__ perm, int* __restrict__ rpos, float* __restrict__ gw) {
   __shared__ int cnt[kRouteMaxExperts];  // counts, then grp_start, then the block's next row per expert
   __shared__ int mine[kRouteMaxExperts];  // the block's routes per expert
   const int t = threadIdx.x;
@@ -199,7 +212,7 @@ __global__ void __launch_bounds__(1024)
     mine[q] = 0;
   }
   __syncthreads();
-  route_prefix(cnt, E, bm, blockIdx.x == 0, counts, grp_start, tile_start, tile_expert);
+  route_prefix(cnt, E, bm1, bm2, blockIdx.x == 0, counts, grp_start, ts1, te1, ts2, te2);
   int ex[kRouteBlock / 1024];
 #pragma unroll
   for (int i = 0; i < kRouteBlock / 1024; ++i) {
@@ -865,11 +878,13 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   const int R = M * k;
   int* counts = (int*)(ws + W.counts);
   int* grp_start = (int*)(ws + W.grp_start);
-  int* tile_start = (int*)(ws + W.tile_start);
+  int* ts1 = (int*)(ws + W.tile_start);  // FC1's m-tiles
+  int* te1 = (int*)(ws + W.tile_expert);
+  int* ts2 = (int*)(ws + W.tile_start2);  // FC2's
+  int* te2 = (int*)(ws + W.tile_expert2);
   int* perm = (int*)(ws + W.perm);
   int* rpos = (int*)(ws + W.rpos);
   float* gw = (float*)(ws + W.gw);
-  int* tile_expert = (int*)(ws + W.tile_expert);
   uint16_t* act = (uint16_t*)(ws + W.act);
   // NVFP4: elements from the hi plane to the lo plane; MXFP4: bytes from one
   // MXFP8 plane (aq, scale dwords as) to the next
@@ -878,50 +893,51 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   uint8_t* as = ws + W.as;
   const int ass = 4 * L.nC2;  // bytes of a row's scale dwords
   float* y = (float*)(ws + W.y);
-  // m-tiles of bm rows: at most one partial tile per expert beyond R / bm full ones
-  const int bm = prefill_bm(L, R);
-  const unsigned mt = (unsigned)((R + bm - 1) / bm + L.E);
+  // m-tiles of bm1 (FC1) and bm2 (FC2) rows: at most one partial tile per
+  // expert beyond R / bm full ones
+  const int bm1 = prefill_bm1(L, R, a8), bm2 = prefill_bm2(L, R, a8);
+  const int64_t mt1 = (R + bm1 - 1) / bm1 + L.E, mt2 = (R + bm2 - 1) / bm2 + L.E;
   if (phases & 5) {
     if (R <= kRouteBlock) {
-      hipLaunchKernelGGL((route_one<IdT>), dim3(1), dim3(1024), 0, st, ids, tw, R, L.E, bm, counts, grp_start,
-                         tile_start, tile_expert, perm, rpos, gw);
+      hipLaunchKernelGGL((route_one<IdT>), dim3(1), dim3(1024), 0, st, ids, tw, R, L.E, bm1, bm2, counts,
+                         grp_start, ts1, te1, ts2, te2, perm, rpos, gw);
     } else {
       int* fill = (int*)(ws + W.fill);
       const unsigned nb = (unsigned)((R + kRouteBlock - 1) / kRouteBlock);
       hipLaunchKernelGGL(route_zero, dim3((L.E + 255) / 256), dim3(256), 0, st, L.E, counts, fill);
       hipLaunchKernelGGL((route_count<IdT>), dim3(nb), dim3(1024), 0, st, ids, R, L.E, counts);
-      hipLaunchKernelGGL((route_place<IdT>), dim3(nb), dim3(1024), 0, st, ids, tw, R, L.E, bm, counts, grp_start,
-                         tile_start, tile_expert, fill, perm, rpos, gw);
+      hipLaunchKernelGGL((route_place<IdT>), dim3(nb), dim3(1024), 0, st, ids, tw, R, L.E, bm1, bm2, counts,
+                         grp_start, ts1, te1, ts2, te2, fill, perm, rpos, gw);
     }
   }
-  const unsigned grid1 = grid8((int64_t)mt * fc1_blocks(L)), grid2 = grid8((int64_t)mt * fc2_blocks(L));
+  const unsigned grid1 = grid8(mt1 * fc1_blocks(L)), grid2 = grid8(mt2 * fc2_blocks(L));
   if ((phases & 1) && a8) {
-    const hipError_t err = launch_fc1_a8(L, prep, x, M, k, ws, W, bm, grid1, st);
+    const hipError_t err = launch_fc1_a8(L, prep, x, M, k, ws, W, bm1, grid1, st);
     if (err != hipSuccess) return err;
   } else if (phases & 1) {
-    if (bm == 32)
-      hipLaunchKernelGGL((fc1_gemm<FMT, 32>), dim3(grid1), dim3(256), 0, st, prep, L, x, k,
-                         (const int*)counts, (const int*)grp_start, (const int*)tile_start, (const int*)tile_expert,
-                         (const int*)perm, act, plane, aq, as, ass);
+#define MOE_FC1(BM)                                                                                           \
+  hipLaunchKernelGGL((fc1_gemm<FMT, BM>), dim3(grid1), dim3(256), 0, st, prep, L, x, k, (const int*)counts,    \
+                     (const int*)grp_start, (const int*)ts1, (const int*)te1, (const int*)perm, act, plane, aq, \
+                     as, ass)
+    if (bm1 == 32)
+      MOE_FC1(32);
     else
-      hipLaunchKernelGGL((fc1_gemm<FMT, kGemmBM>), dim3(grid1), dim3(256), 0, st, prep, L, x, k,
-                         (const int*)counts, (const int*)grp_start, (const int*)tile_start, (const int*)tile_expert,
-                         (const int*)perm, act, plane, aq, as, ass);
+      MOE_FC1(kGemmBM);
+#undef MOE_FC1
   }
   if ((phases & 2) && a8) {
-    const hipError_t err = launch_fc2_a8(L, prep, ws, W, bm, grid2, st);
+    const hipError_t err = launch_fc2_a8(L, prep, ws, W, bm2, grid2, st);
     if (err != hipSuccess) return err;
   } else if (phases & 2) {
-    if (bm == 32)
-      hipLaunchKernelGGL((fc2_gemm<FMT, 32>), dim3(grid2), dim3(256), 0, st, prep, L, (const float*)gw,
-                         (const int*)counts, (const int*)grp_start, (const int*)tile_start, (const int*)tile_expert,
-                         (const int*)perm, (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as,
-                         ass, y);
+#define MOE_FC2(BM)                                                                                                \
+  hipLaunchKernelGGL((fc2_gemm<FMT, BM>), dim3(grid2), dim3(256), 0, st, prep, L, (const float*)gw,                 \
+                     (const int*)counts, (const int*)grp_start, (const int*)ts2, (const int*)te2, (const int*)perm, \
+                     (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as, ass, y)
+    if (bm2 == 32)
+      MOE_FC2(32);
     else
-      hipLaunchKernelGGL((fc2_gemm<FMT, kGemmBM>), dim3(grid2), dim3(256), 0, st, prep, L, (const float*)gw,
-                         (const int*)counts, (const int*)grp_start, (const int*)tile_start, (const int*)tile_expert,
-                         (const int*)perm, (const uint16_t*)act, plane, (const uint8_t*)aq, (const uint8_t*)as,
-                         ass, y);
+      MOE_FC2(kGemmBM);
+#undef MOE_FC2
   }
   if (phases & 10) {
     hipLaunchKernelGGL((combine<IdT>), dim3(M, (L.H + 1023) / 1024), dim3(256), 0, st, ids, k, L.E, L.H,

@@ -389,8 +389,8 @@ hipError_t launch_fc2_a8(const Layout& L, const uint8_t* prep, uint8_t* ws, cons
                          unsigned grid, hipStream_t st) {
 #define MOE_FC2A8(BM)                                                                                           \
   hipLaunchKernelGGL(fc2_gemm_a8<BM>, dim3(grid), dim3(256), 0, st, prep, L, (const float*)(ws + W.gw),        \
-                     (const int*)(ws + W.counts), (const int*)(ws + W.grp_start), (const int*)(ws + W.tile_start), \
-                     (const int*)(ws + W.tile_expert), (const uint8_t*)(ws + W.aq), (const uint8_t*)(ws + W.as), \
+                     (const int*)(ws + W.counts), (const int*)(ws + W.grp_start), (const int*)(ws + W.tile_start2), \
+                     (const int*)(ws + W.tile_expert2), (const uint8_t*)(ws + W.aq), (const uint8_t*)(ws + W.as), \
                      a8_scale_stride(L.I), (float*)(ws + W.y))
   if (bm == 32)
     MOE_FC2A8(32);

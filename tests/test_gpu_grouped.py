@@ -40,12 +40,15 @@ CASES = [
     # fmt, E, H, I, M, k, seed, hot-expert fraction
     ("mxfp4", 4, 64, 32, 1, 1, 1, 0.0),       # one route; FC1 and FC2 second tiles absent
     ("mxfp4", 6, 96, 64, 3, 3, 2, 0.0),       # odd K steps in FC1; FC2 tile half padding
+    # NVFP4 with 16 to 128 routes per expert: 128-row FC1 tiles, 32-row FC2 tiles (one pass)
     ("nvfp4", 5, 256, 96, 40, 4, 3, 0.0),     # I = 3 units: partial FC1 column block, odd FC2 K
     ("nvfp4", 8, 512, 128, 300, 2, 4, 0.5),   # 2 m-tiles for the hot expert
     ("mxfp4", 16, 1024, 256, 520, 4, 5, 0.9), # hot expert: 4 full m-tiles + a ragged one
     ("nvfp4", 12, 2560, 64, 200, 2, 6, 0.0),
     ("mxfp4", 3, 1536, 544, 100, 2, 7, 0.0),  # 17 FC1 tiles: last column block half empty
     ("mxfp4", 1, 64, 32, 130, 1, 8, 0.0),     # a single expert, 128 + 2 rows
+    # MXFP4 with 16 to 64 routes per expert: 32-row FC1 tiles, 128-row FC2 tiles
+    ("mxfp4", 8, 512, 128, 100, 4, 12, 0.5),  # hot expert: 7 FC1 tiles, 2 FC2 tiles
     # few routes per expert (at most 16 on average): 32-row m-tiles
     ("mxfp4", 64, 512, 128, 100, 4, 9, 0.9),  # hot expert: three 32-row tiles and a ragged one
     ("nvfp4", 40, 512, 96, 120, 4, 10, 0.6),  # I = 3 units: odd FC2 K; hot expert over several tiles
