@@ -20,10 +20,10 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Chunks of decode_max_tokens(k) tokens a call with bf16 activations takes
 // on the decode path by default: up to kDecodeAnyChunks whatever the
-// routing, up to kDecodeMaxChunks when the routes number at most E (few
-// routes per expert: the decode path reads an expert once per chunk, the
-// grouped path batches an expert's routes); other calls take the grouped
-// path.  Measured on MI355X: two chunks were faster than the grouped path on
+// routing, up to kDecodeMaxChunks when the chunks' route slots (chunks x
+// tokens per chunk x k) are fewer than E (few routes per expert: the decode
+// path reads an expert once per chunk, the grouped path batches an expert's
+// routes); other calls take the grouped path.  Measured on MI355X: two chunks were faster than the grouped path on
 // every layer from E8/H256 to E512/H2560; at 3-6 chunks E256-E512 layers
 // gained up to 1.0-1.5 E routes, while E128/H2048 at 1.5 E and E64/H1024 at
 // 3 E ran faster grouped.
@@ -110,14 +110,14 @@ moe_fp4_status make_plan(const moe_fp4_desc* desc, const Layout& L, int32_t M,
   const int k = desc->top_k;
   // The decode path takes any M in chunks of at most decode_max_tokens(k)
   // tokens.  By default with bf16 activations: up to kDecodeAnyChunks
-  // chunks, up to kDecodeMaxChunks when M k <= E (MXFP8 activations: one
+  // chunks, up to kDecodeMaxChunks when chunks mc k < E (MXFP8 activations: one
   // chunk, their grouped path quantises them); the grouped path beyond; the
   // decode path for any M when E is past what the grouped path's route
   // grouping holds.
   const bool decode_ok = k <= moe::kDecodeMaxSlots;
   const int mc = decode_ok ? moe::decode_max_tokens(k) : 1;
   const int64_t chunks = ((int64_t)(M < 1 ? 1 : M) + mc - 1) / mc;
-  const bool few_routes = (int64_t)M * k <= (int64_t)L.E;
+  const bool few_routes = chunks * mc * k < (int64_t)L.E;
   const int64_t auto_chunks = act_mxfp8(desc) ? 1 : (few_routes ? kDecodeMaxChunks : kDecodeAnyChunks);
   if (path == MOE_FP4_PATH_AUTO)
     path = decode_ok && (chunks <= auto_chunks || L.E > moe::kRouteMaxExperts) ? MOE_FP4_PATH_DECODE

@@ -129,10 +129,11 @@ hipError_t launch_prefill(const Layout& L, const uint8_t* prep, const uint16_t* 
                           const PrefillWs& W, int phases, bool a8, hipStream_t st);
 
 // The A8 GEMM launches (x quantisation + FC1, FC2) over a grid of `grid`
-// workgroups of m-tiles of `bm` rows (the same tile grids as the bf16 GEMMs).
+// workgroups of m-tiles of `bm` rows numbered by the tables ts / te (the
+// same tile grids as the bf16 GEMMs).
 hipError_t launch_fc1_a8(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k, uint8_t* ws,
-                         const PrefillWs& W, int bm, unsigned grid, hipStream_t st);
+                         const PrefillWs& W, int bm, const int* ts, const int* te, unsigned grid, hipStream_t st);
 hipError_t launch_fc2_a8(const Layout& L, const uint8_t* prep, uint8_t* ws, const PrefillWs& W, int bm,
-                         unsigned grid, hipStream_t st);
+                         const int* ts, const int* te, unsigned grid, hipStream_t st);
 
 }  // namespace moe

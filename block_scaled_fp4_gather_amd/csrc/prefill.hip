@@ -62,9 +62,10 @@ constexpr int kRouteBlock = 4096;  // routes per workgroup of the routing kernel
 // Exclusive prefix over the E counters cnt (in LDS, E <= kRouteMaxExperts)
 // by the 1024 threads of a workgroup: counts[e], grp_start[e] and, for each
 // of the two GEMMs' m-tile sizes (FC1: bm1 rows, table ts1 / te1; FC2: bm2,
-// ts2 / te2), tile_start[e] (tile_start[E] the total) and the expert of each
-// m-tile, tile_expert[t], are written to global memory when `out` is set,
-// and cnt[e] becomes grp_start[e].  Ends with a barrier.
+// ts2 / te2; a bm2 of 0 means FC2 shares FC1's table), tile_start[e]
+// (tile_start[E] the total) and the expert of each m-tile, tile_expert[t],
+// are written to global memory when `out` is set, and cnt[e] becomes
+// grp_start[e].  Ends with a barrier.
 __device__ void route_prefix(int* cnt, int E, int bm1, int bm2, bool out, int* __restrict__ counts,
                              int* __restrict__ grp_start, int* __restrict__ ts1, int* __restrict__ te1,
                              int* __restrict__ ts2, int* __restrict__ te2) {
@@ -72,6 +73,8 @@ __device__ void route_prefix(int* cnt, int E, int bm1, int bm2, bool out, int* _
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   constexpr int PER = kRouteMaxExperts / 1024;  // counters per thread
   const int e0 = t * PER;
+  const bool two = bm2 > 0;
+  if (!two) bm2 = bm1;
   int c[PER], rsum = 0, tsum1 = 0, tsum2 = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -118,9 +121,11 @@ __device__ void route_prefix(int* cnt, int E, int bm1, int bm2, bool out, int* _
         counts[e] = c[i];
         grp_start[e] = rb;
         ts1[e] = tb1;
-        ts2[e] = tb2;
         for (int q = 0; q < nt1; ++q) te1[tb1 + q] = e;
-        for (int q = 0; q < nt2; ++q) te2[tb2 + q] = e;
+        if (two) {
+          ts2[e] = tb2;
+          for (int q = 0; q < nt2; ++q) te2[tb2 + q] = e;
+        }
       }
       cnt[e] = rb;
     }
@@ -130,7 +135,7 @@ __device__ void route_prefix(int* cnt, int E, int bm1, int bm2, bool out, int* _
   }
   if (out && t == 0) {
     ts1[E] = ttot1;
-    ts2[E] = ttot2;
+    if (two) ts2[E] = ttot2;
   }
   __syncthreads();
 }
@@ -897,22 +902,28 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
   // expert beyond R / bm full ones
   const int bm1 = prefill_bm1(L, R, a8), bm2 = prefill_bm2(L, R, a8);
   const int64_t mt1 = (R + bm1 - 1) / bm1 + L.E, mt2 = (R + bm2 - 1) / bm2 + L.E;
+  // with one tile size FC2 reads FC1's table and the routing writes one
+  const int rbm2 = bm2 == bm1 ? 0 : bm2;
+  if (bm2 == bm1) {
+    ts2 = ts1;
+    te2 = te1;
+  }
   if (phases & 5) {
     if (R <= kRouteBlock) {
-      hipLaunchKernelGGL((route_one<IdT>), dim3(1), dim3(1024), 0, st, ids, tw, R, L.E, bm1, bm2, counts,
+      hipLaunchKernelGGL((route_one<IdT>), dim3(1), dim3(1024), 0, st, ids, tw, R, L.E, bm1, rbm2, counts,
                          grp_start, ts1, te1, ts2, te2, perm, rpos, gw);
     } else {
       int* fill = (int*)(ws + W.fill);
       const unsigned nb = (unsigned)((R + kRouteBlock - 1) / kRouteBlock);
       hipLaunchKernelGGL(route_zero, dim3((L.E + 255) / 256), dim3(256), 0, st, L.E, counts, fill);
       hipLaunchKernelGGL((route_count<IdT>), dim3(nb), dim3(1024), 0, st, ids, R, L.E, counts);
-      hipLaunchKernelGGL((route_place<IdT>), dim3(nb), dim3(1024), 0, st, ids, tw, R, L.E, bm1, bm2, counts,
+      hipLaunchKernelGGL((route_place<IdT>), dim3(nb), dim3(1024), 0, st, ids, tw, R, L.E, bm1, rbm2, counts,
                          grp_start, ts1, te1, ts2, te2, fill, perm, rpos, gw);
     }
   }
   const unsigned grid1 = grid8(mt1 * fc1_blocks(L)), grid2 = grid8(mt2 * fc2_blocks(L));
   if ((phases & 1) && a8) {
-    const hipError_t err = launch_fc1_a8(L, prep, x, M, k, ws, W, bm1, grid1, st);
+    const hipError_t err = launch_fc1_a8(L, prep, x, M, k, ws, W, bm1, ts1, te1, grid1, st);
     if (err != hipSuccess) return err;
   } else if (phases & 1) {
 #define MOE_FC1(BM)                                                                                           \
@@ -926,7 +937,7 @@ hipError_t launch_prefill_fmt(const Layout& L, const uint8_t* prep, const uint16
 #undef MOE_FC1
   }
   if ((phases & 2) && a8) {
-    const hipError_t err = launch_fc2_a8(L, prep, ws, W, bm2, grid2, st);
+    const hipError_t err = launch_fc2_a8(L, prep, ws, W, bm2, ts2, te2, grid2, st);
     if (err != hipSuccess) return err;
   } else if (phases & 2) {
 #define MOE_FC2(BM)                                                                                                \

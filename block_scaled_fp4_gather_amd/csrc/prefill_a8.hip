@@ -366,7 +366,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kA8Wav
 }
 
 hipError_t launch_fc1_a8(const Layout& L, const uint8_t* prep, const uint16_t* x, int M, int k, uint8_t* ws,
-                         const PrefillWs& W, int bm, unsigned grid, hipStream_t st) {
+                         const PrefillWs& W, int bm, const int* ts, const int* te, unsigned grid, hipStream_t st) {
   uint8_t* xq = ws + W.xq;
   uint8_t* xs = ws + W.xs;
   hipError_t err = launch_mxfp8_quantize(x, M, L.H, xq, xs, a8_scale_stride(L.H), st);
@@ -374,8 +374,7 @@ hipError_t launch_fc1_a8(const Layout& L, const uint8_t* prep, const uint16_t* x
 #define MOE_FC1A8(BM)                                                                                           \
   hipLaunchKernelGGL(fc1_gemm_a8<BM>, dim3(grid), dim3(256), 0, st, prep, L, (const uint8_t*)xq,               \
                      (const uint8_t*)xs, a8_scale_stride(L.H), k, (const int*)(ws + W.counts),                  \
-                     (const int*)(ws + W.grp_start), (const int*)(ws + W.tile_start),                           \
-                     (const int*)(ws + W.tile_expert), (const int*)(ws + W.perm), ws + W.aq, ws + W.as,          \
+                     (const int*)(ws + W.grp_start), ts, te, (const int*)(ws + W.perm), ws + W.aq, ws + W.as,   \
                      a8_scale_stride(L.I))
   if (bm == 32)
     MOE_FC1A8(32);
@@ -386,11 +385,11 @@ hipError_t launch_fc1_a8(const Layout& L, const uint8_t* prep, const uint16_t* x
 }
 
 hipError_t launch_fc2_a8(const Layout& L, const uint8_t* prep, uint8_t* ws, const PrefillWs& W, int bm,
-                         unsigned grid, hipStream_t st) {
+                         const int* ts, const int* te, unsigned grid, hipStream_t st) {
 #define MOE_FC2A8(BM)                                                                                           \
   hipLaunchKernelGGL(fc2_gemm_a8<BM>, dim3(grid), dim3(256), 0, st, prep, L, (const float*)(ws + W.gw),        \
-                     (const int*)(ws + W.counts), (const int*)(ws + W.grp_start), (const int*)(ws + W.tile_start2), \
-                     (const int*)(ws + W.tile_expert2), (const uint8_t*)(ws + W.aq), (const uint8_t*)(ws + W.as), \
+                     (const int*)(ws + W.counts), (const int*)(ws + W.grp_start), ts, te,                        \
+                     (const uint8_t*)(ws + W.aq), (const uint8_t*)(ws + W.as),                                   \
                      a8_scale_stride(L.I), (float*)(ws + W.y))
   if (bm == 32)
     MOE_FC2A8(32);

@@ -201,8 +201,9 @@ moe_fp4_status moe_fp4_workspace_bytes(const moe_fp4_desc* desc, int32_t M, size
  *           over chunks of up to C = min(16, 64 / k) tokens, each routed
  *           expert's weights read once per chunk (b12x PR #22, What);
  *           results are bit-reproducible.  Taken for M <= C; with bf16
- *           activations for M <= 2C, and for M <= 6C when M * k <= E (few
- *           routes per expert); and for every M when E > 8192.
+ *           activations for M <= 2C, and for M <= 6C when the chunks'
+ *           route slots ceil(M / C) * C * k are fewer than E (few routes
+ *           per expert); and for every M when E > 8192.
  *   grouped (any other M): routes grouped by expert in route order, FC1 and
  *           FC2 as grouped GEMMs on the matrix cores over bf16 operands (FP4
  *           dequantised exactly) with fp32 accumulation, per-route fp32 rows

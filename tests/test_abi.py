@@ -121,7 +121,7 @@ def test_tuning_hook_rejects_bad_shapes(L):
 def test_decode_path_past_one_launch_pair(L):
     # past M * k = 64 route slots or M = 16 the decode path runs in chunks
     # (chosen automatically with bf16 activations up to 2 chunks, and up to 6
-    # when the routes number at most E)
+    # when the chunks' route slots number fewer than E)
     wide = moe.Desc("nvfp4", 512, 2560, 320, 10, 64)     # 6 tokens per chunk
     t = moe.Tuning(0, 0, 0, moe.PATH_DECODE)
     assert _plan(wide, 7, t)[0] == moe.PATH_DECODE
@@ -137,8 +137,8 @@ def test_decode_path_past_one_launch_pair(L):
     assert _plan(small_e, 16)[0] == moe.PATH_DECODE     # two chunks
     assert _plan(small_e, 17)[0] == moe.PATH_GROUPED    # three, 136 routes > E
     big_e = moe.Desc("mxfp4", 256, 2048, 256, 8, 64)
-    assert _plan(big_e, 32)[0] == moe.PATH_DECODE       # four chunks, 256 routes <= E
-    assert _plan(big_e, 33)[0] == moe.PATH_GROUPED      # 264 routes > E
+    assert _plan(big_e, 24)[0] == moe.PATH_DECODE       # three chunks, 192 slots < E
+    assert _plan(big_e, 25)[0] == moe.PATH_GROUPED      # four, 256 slots
     # the grouped path's expert grouping holds at most 8192 experts; past it
     # the decode path takes every M
     wide_e = moe.Desc("mxfp4", 9000, 64, 32, 8, 64)

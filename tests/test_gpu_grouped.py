@@ -227,7 +227,7 @@ def test_band_edge_both_paths(fmt, k):
     the forced decode path (in chunks past one) and the forced grouped path
     all match the oracle."""
     edge = min(16, 64 // k)
-    for E, M in ((16, edge), (16, edge + 1), (16, 2 * edge + 1), (256, 4 * edge), (256, 6 * edge),
+    for E, M in ((16, edge), (16, edge + 1), (16, 2 * edge + 1), (256, 3 * edge), (256, 6 * edge),
                  (256, 6 * edge + 1)):
         rng = np.random.default_rng(40 + M + E)
         d, _, _ = random_case(rng, fmt, E, 256, 128, M, k)
@@ -235,8 +235,8 @@ def test_band_edge_both_paths(fmt, k):
         d["ids"][-1, -1] = E + 3
         acc, _ = oracle.forward_f32(fmt, d)
         layer = make_layer(fmt, d, k, M)
-        # up to 2 chunks: decode; up to 6 chunks with M k <= E: decode; else grouped
-        few = M * k <= E
+        # up to 2 chunks: decode; up to 6 chunks with fewer route slots than E: decode; else grouped
+        few = -(-M // edge) * edge * k < E
         want = moe.PATH_DECODE if M <= 2 * edge or (M <= 6 * edge and few) else moe.PATH_GROUPED
         assert moe.plan(layer.desc, M).path == want
         compare(run_layer(layer, d), acc, f"{fmt} E{E} k{k} M{M} auto")
