@@ -8,9 +8,9 @@
 // cast (b12x #311, commit on the prefill fused-sum epilogue).  Here:
 //   routing    groups the valid routes by expert (route_one, or route_zero,
 //              route_count and route_place for many routes), numbers the
-//              m-tiles of every expert (128 rows, or 32 when the experts get
-//              few routes each) and records each m-tile's expert and each
-//              grouped row's router weight;
+//              m-tiles of every expert for each GEMM (128 rows, or 32 when
+//              the experts get few routes each) and records each m-tile's
+//              expert and each grouped row's router weight;
 //   fc1_gemm   x rows gathered into LDS, FP4 weight units copied into LDS and
 //              widened to bf16 in registers (exact: E2M1 times a UE8M0 or
 //              E4M3 block scale has at most 6 significant bits), v_mfma_f32_32x32x16_bf16 with
@@ -18,8 +18,9 @@
 //              hi = bf16(a) plus the residual lo = a - hi: NVFP4 as two bf16
 //              planes; MXFP4 as three planes (hi rounded to MXFP8, what that
 //              leaves of hi, and lo as MXFP4);
-//   fc2_gemm   over the activation rows and W2: NVFP4 as fc1_gemm, in two
-//              passes over K, one per bf16 plane; MXFP4 in one pass on
+//   fc2_gemm   over the activation rows and W2: NVFP4 as fc1_gemm, both bf16
+//              planes on each widened weight unit (32-row m-tiles) or in two
+//              passes over K, one per plane (128-row); MXFP4 in one pass on
 //              v_mfma_scale_f32_32x32x64_f8f6f4, one pair per plane, block
 //              and step, with the weights as stored; times the NVFP4 global and the
 //              route's router weight -> fp32 rows;
