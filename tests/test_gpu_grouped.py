@@ -49,6 +49,9 @@ CASES = [
     ("mxfp4", 1, 64, 32, 130, 1, 8, 0.0),     # a single expert, 128 + 2 rows
     # MXFP4 with 16 to 64 routes per expert: 32-row FC1 tiles, 128-row FC2 tiles
     ("mxfp4", 8, 512, 128, 100, 4, 12, 0.5),  # hot expert: 7 FC1 tiles, 2 FC2 tiles
+    # past 4096 routes (routing in several workgroups) with a tile table per GEMM
+    ("mxfp4", 128, 256, 64, 1100, 4, 13, 0.0),  # 34 routes per expert
+    ("nvfp4", 64, 256, 64, 1200, 4, 14, 0.3),   # 75 per expert, a hot one
     # few routes per expert (at most 16 on average): 32-row m-tiles
     ("mxfp4", 64, 512, 128, 100, 4, 9, 0.9),  # hot expert: three 32-row tiles and a ragged one
     ("nvfp4", 40, 512, 96, 120, 4, 10, 0.6),  # I = 3 units: odd FC2 K; hot expert over several tiles
