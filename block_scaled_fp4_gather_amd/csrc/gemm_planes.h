@@ -73,12 +73,13 @@ __device__ __forceinline__ int pl_swz4(int r) { return ((r >> 2) ^ (r >> 3) ^ (r
 // row 32w + 16 blk + lane / 4; with LO4 the last plane 32 rows of 32 bytes
 // from `lrow4`, row 32w + lane / 2) and the scale dwords (row 32w + lane % 32,
 // unit 2s + lane / 32), AD steps ahead; the wave's weights (two code halves
-// and one copy of the 64 rows' scale dwords) two steps ahead.  Per step:
+// and one copy of the 64 rows' scale dwords) two steps ahead, with NT
+// non-temporally (weights read once).  Per step:
 // wait until this wave's copies for the step have landed, one barrier, then
 // the MFMAs with the next copies issued between them.  Copies past the last
 // step are clamped to it (never used); with an odd number of units the last
 // step's second unit is zeroed when read (codes and weights zero, scales 1).
-template <int BM, int NP, int AD, bool SBYTE, bool LO4, int NB, bool CPA, typename Pre, typename Epilogue>
+template <int BM, int NP, int AD, bool SBYTE, bool LO4, bool NT, int NB, bool CPA, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], int64_t pst, const uint8_t* lrow4,
                                              const uint8_t* srow, int nU, const uint8_t* __restrict__ btile,
                                              uint8_t* smem, Pre&& pre, Epilogue&& epilogue) {
@@ -134,8 +135,12 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
   auto b_unit = [&](int s) { return min(2 * s + h, nU - 1); };
   auto copy_b = [&](int s, int j) {
     const int cc = b_unit(min(s, nsteps - 1));
-    dma16(btile + (int64_t)cc * 1024 + (32 * j + n) * 16,
-          lds_addr(bring + (s % kBSlotsPl) * kBSlotPl + j * 1024));
+    const uint8_t* g = btile + (int64_t)cc * 1024 + (32 * j + n) * 16;
+    const uint32_t l = lds_addr(bring + (s % kBSlotsPl) * kBSlotPl + j * 1024);
+    if constexpr (NT)
+      dma16_nt(g, l);
+    else
+      dma16(g, l);
   };
   auto copy_bs = [&](int s) {
     const int cw = min(2 * min(s, nsteps - 1), nU - 1);
@@ -246,14 +251,14 @@ __device__ __forceinline__ void gemm_main_pl(const uint8_t* const (&prowp)[2], i
 // (0 when the wave has no weight tile); the wave copies its A block when the
 // tile has rows in it.  Tiles of BM = 32 rows have one block, copied by wave
 // 0.  Each variant carries its own copy of the epilogue.
-template <int BM, int NP, int AD, bool SBYTE, bool LO4, typename Pre, typename Epilogue>
+template <int BM, int NP, int AD, bool SBYTE, bool LO4, bool NT, typename Pre, typename Epilogue>
 __device__ __forceinline__ void gemm_rows_pl(int rows, const uint8_t* const (&prowp)[2], int64_t pst,
                                              const uint8_t* lrow4, const uint8_t* srow, int nU,
                                              const uint8_t* __restrict__ btile, bool bok, uint8_t* smem, Pre&& pre,
                                              Epilogue&& ep) {
   const bool cpa = 32 * (threadIdx.x >> 6) < rows;
 #define MOE_PL(NB, CPA) \
-  gemm_main_pl<BM, NP, AD, SBYTE, LO4, NB, CPA>(prowp, pst, lrow4, srow, nU, btile, smem, pre, ep)
+  gemm_main_pl<BM, NP, AD, SBYTE, LO4, NT, NB, CPA>(prowp, pst, lrow4, srow, nU, btile, smem, pre, ep)
   if constexpr (BM == 32) {
     if (!bok) {
       if (cpa)

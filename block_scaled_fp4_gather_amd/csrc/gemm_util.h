@@ -37,6 +37,13 @@ __device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
                : "=&s"(tmp) : "v"(g), "s"(lds));
 }
+// The same for data read once (weights): non-temporal, so that it does not
+// displace reused lines in the caches.
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds) {
+  uint32_t tmp;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
+               : "=&s"(tmp) : "v"(g), "s"(lds));
+}
 // Wait until at most N vector memory operations of this wave are in flight.
 template <int N>
 __device__ __forceinline__ void vm_wait() {

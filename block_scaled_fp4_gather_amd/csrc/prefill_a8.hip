@@ -288,7 +288,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kA8Wav
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
       prowp[blk] = xq + (int64_t)(perm[gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)] / k) * L.H;
-    gemm_rows_pl<BM, 1, 1, true, false>(rows, prowp, 0, nullptr, srow, L.nC1, btile, bok, smem, [] {}, epilogue);
+    gemm_rows_pl<BM, 1, 1, true, false, true>(rows, prowp, 0, nullptr, srow, L.nC1, btile, bok, smem, [] {}, epilogue);
   } else {
     // x rows this lane copies: rows 32 wave + 8 blk + lane / 8 of the tile
     const uint8_t* rowp[4];
@@ -351,7 +351,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kA8Wav
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
       prowp[blk] = aq + (int64_t)(gs + min(32 * wave + 16 * blk + (lane >> 2), rows - 1)) * L.I;
-    gemm_rows_pl<BM, 1, 2, true, false>(rows, prowp, 0, nullptr, srow, L.nC2, btile, bok, smem, pre, epilogue);
+    gemm_rows_pl<BM, 1, 2, true, false, true>(rows, prowp, 0, nullptr, srow, L.nC2, btile, bok, smem, pre, epilogue);
   } else {
     // act rows this lane copies: rows 32 wave + 8 blk + lane / 8 of the tile;
     // the router weights go to LDS before the main loop, whose barriers
