@@ -151,14 +151,20 @@ __global__ void __launch_bounds__(1024)
               int* __restrict__ rpos, float* __restrict__ gw) {
   __shared__ int cnt[kRouteMaxExperts];
   const int t = threadIdx.x;
-  for (int q = t; q < E; q += 1024) cnt[q] = 0;
-  __syncthreads();
+  // the ids and router weights are loaded first, while the counters clear
   int ex[kRouteBlock / 1024];
+  float wt[kRouteBlock / 1024];
 #pragma unroll
   for (int i = 0; i < kRouteBlock / 1024; ++i) {
-    ex[i] = route_expert(ids, t + 1024 * i, R, E);
-    if (ex[i] >= 0) atomicAdd(&cnt[ex[i]], 1);
+    const int r = t + 1024 * i;
+    ex[i] = route_expert(ids, r, R, E);
+    wt[i] = r < R ? tw[r] : 0.0f;
   }
+  for (int q = t; q < E; q += 1024) cnt[q] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kRouteBlock / 1024; ++i)
+    if (ex[i] >= 0) atomicAdd(&cnt[ex[i]], 1);
   __syncthreads();
   route_prefix(cnt, E, bm1, bm2, true, counts, grp_start, ts1, te1, ts2, te2);
 #pragma unroll
@@ -168,7 +174,7 @@ __global__ void __launch_bounds__(1024)
     const int p = atomicAdd(&cnt[ex[i]], 1);
     perm[p] = r;
     rpos[r] = p;
-    gw[p] = tw[r];
+    gw[p] = wt[i];
   }
 }
 
@@ -191,13 +197,14 @@ __global__ void __launch_bounds__(1024)
   __shared__ int cnt[kRouteMaxExperts];
   const int t = threadIdx.x;
   const int r0 = blockIdx.x * kRouteBlock;
+  int ex[kRouteBlock / 1024];  // loaded while the counters clear
+#pragma unroll
+  for (int i = 0; i < kRouteBlock / 1024; ++i) ex[i] = route_expert(ids, r0 + t + 1024 * i, R, E);
   for (int q = t; q < E; q += 1024) cnt[q] = 0;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kRouteBlock / 1024; ++i) {
-    const int e = route_expert(ids, r0 + t + 1024 * i, R, E);
-    if (e >= 0) atomicAdd(&cnt[e], 1);
-  }
+  for (int i = 0; i < kRouteBlock / 1024; ++i)
+    if (ex[i] >= 0) atomicAdd(&cnt[ex[i]], 1);
   __syncthreads();
   for (int q = t; q < E; q += 1024)
     if (cnt[q]) atomicAdd(&counts[q], cnt[q]);
@@ -213,18 +220,24 @@ __global__ void __launch_bounds__(1024)
   __shared__ int mine[kRouteMaxExperts];  // the block's routes per expert
   const int t = threadIdx.x;
   const int r0 = blockIdx.x * kRouteBlock;
+  // the block's ids and router weights, loaded while the prefix is taken
+  int ex[kRouteBlock / 1024];
+  float wt[kRouteBlock / 1024];
+#pragma unroll
+  for (int i = 0; i < kRouteBlock / 1024; ++i) {
+    const int r = r0 + t + 1024 * i;
+    ex[i] = route_expert(ids, r, R, E);
+    wt[i] = r < R ? tw[r] : 0.0f;
+  }
   for (int q = t; q < E; q += 1024) {
     cnt[q] = counts[q];
     mine[q] = 0;
   }
   __syncthreads();
   route_prefix(cnt, E, bm1, bm2, blockIdx.x == 0, counts, grp_start, ts1, te1, ts2, te2);
-  int ex[kRouteBlock / 1024];
 #pragma unroll
-  for (int i = 0; i < kRouteBlock / 1024; ++i) {
-    ex[i] = route_expert(ids, r0 + t + 1024 * i, R, E);
+  for (int i = 0; i < kRouteBlock / 1024; ++i)
     if (ex[i] >= 0) atomicAdd(&mine[ex[i]], 1);
-  }
   __syncthreads();
   for (int q = t; q < E; q += 1024)
     if (mine[q]) cnt[q] += atomicAdd(&fill[q], mine[q]);
@@ -236,7 +249,7 @@ __global__ void __launch_bounds__(1024)
     const int p = atomicAdd(&cnt[ex[i]], 1);
     perm[p] = r;
     rpos[r] = p;
-    gw[p] = tw[r];
+    gw[p] = wt[i];
   }
 }
 
