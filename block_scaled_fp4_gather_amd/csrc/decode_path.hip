@@ -274,10 +274,15 @@ __global__ void __launch_bounds__(1024)
   const int wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
   const int p = lane % KL, g = lane / KL;
-  const int blk = blockIdx.x % NB;
-  const int b = (blockIdx.x / NB) % L.nB1;
-  const int s = (blockIdx.x / NB) / L.nB1;
-  if (s >= M * k) return;  // a slot past the last chunk's tokens
+  // Workgroup id = ((tl / 8) NB + blk) 8 + tl % 8 for tile tl = s nB1 + b: the
+  // NB blocks of a tile, which share its scale blocks, have ids 8 apart, so
+  // round-robin dispatch over the 8 XCDs puts them on one XCD's L2.  The
+  // grid covers the tiles rounded up to a multiple of 8.
+  const int blk = (int)(blockIdx.x >> 3) % NB;
+  const int tl = (int)(blockIdx.x >> 3) / NB * 8 + (int)(blockIdx.x & 7);
+  const int b = tl % L.nB1;
+  const int s = tl / L.nB1;
+  if (s >= M * k) return;  // a slot past the last chunk's tokens, or a padding tile
   const int t0 = s / k;  // the slot's own token routes to the slot's expert
   const int ngroups = (L.nC1 + W * KL - 1) / (W * KL);
 
@@ -511,8 +516,8 @@ hipError_t launch_fc1(const Layout& L, const uint8_t* prep, const uint16_t* x, i
   const int waves = groups < kMaxWaves ? groups : kMaxWaves;
   const bool big = R == 32;
   const size_t lds = (size_t)fc1_lds_bytes(L, mc, R);
-  const dim3 grid((unsigned)((int64_t)slots * L.nB1 * (64 / R)), (unsigned)((M + mc - 1) / mc)),
-      block(64 * waves);
+  const int64_t tiles8 = ((int64_t)slots * L.nB1 + 7) / 8 * 8;  // see fc1_kernel's workgroup ids
+  const dim3 grid((unsigned)(tiles8 * (64 / R)), (unsigned)((M + mc - 1) / mc)), block(64 * waves);
   const bool early = KL == 4 && L.nC1 <= 128;
 #define MOE_FC1_E(RR, CC, EE)                                                                                   \
   hipLaunchKernelGGL((fc1_kernel<FMT, KL, RR, CC, EE, IdT>), grid, block, lds, st, prep, L, x, ids, M, k, mc, \
